@@ -1,0 +1,242 @@
+"""Benchmark of the NVFP4 W4A4 + RAC rollout hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of seeded synthetic
+input already resident in HBM:
+  MoE workloads:  moe_route -> nvfp4_quantize(X)+rac_select_residual(X) ->
+                  gate/up grouped GEMM (RAC fused, SiLU*mul epilogue, max|H|)
+                  -> nvfp4_quantize(H)+rac_select_residual(H) -> down grouped
+                  GEMM (RAC fused)
+  dense workloads: nvfp4_quantize(X)+rac_select_residual(X) -> W4A4 GEMM
+Weights are quantized once before timing (offline, as in rollout).
+
+Prints one JSON line.  `value` is the algorithmic GEMM TFLOP/s of the whole
+step (main + residual passes of every GEMM, residual counted over the active
+K-blocks only) divided by the step time; `roofline` covers the dominant
+kernel (the gate/up grouped GEMM, or the dense GEMM) timed with HIP events on
+the launch stream; `cpu_baseline` times the CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_F16_TFLOPS = 2516.6   # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--no-rac", action="store_true", help="naive W4A4 (RAC off)")
+    ap.add_argument("--cpu-baseline", type=int, default=1)
+    ap.add_argument("--cpu-sample-experts", type=int, default=48)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path runs on a single MI355X "
+              "(no sharding or collectives); rerun with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from nvfp4_w4a4_moe_quant_amd import _lib as L
+    from nvfp4_w4a4_moe_quant_amd import datagen as D
+    from nvfp4_w4a4_moe_quant_amd import pipeline as P
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = D.WORKLOADS[args.workload]
+
+    def to_dev(a, dtype):
+        if dtype == "bf16":
+            return torch.from_numpy(D.bf16_bits(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+
+    t_setup = time.time()
+    x_np = D.activations(w)
+    x = to_dev(x_np, w.x_dtype)
+    rac = not args.no_rac
+    nsx = w.n_select_x if rac else None
+    if w.kind == "moe":
+        lg_np = D.router_logits(w)
+        lg = torch.from_numpy(lg_np).to(dev)
+        wgu = P.quantize_weights(((e, to_dev(m, "bf16")) for e, m in D.expert_weights(w, "gate_up")),
+                                 w.E, 2 * w.I, w.H, dev)
+        wd = P.quantize_weights(((e, to_dev(m, "bf16")) for e, m in D.expert_weights(w, "down")),
+                                w.E, w.H, w.I, dev)
+        nsh = w.n_select_h if rac else None
+        rows = w.T * w.topk
+        amax_h = torch.zeros(1, dtype=torch.float32, device=dev)
+    else:
+        wq = P.quantize_weights([(0, to_dev(D.dense_weight(w), w.x_dtype))], 1, w.N, w.K, dev)
+        offs = torch.tensor([0, w.rows], dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    t_setup = time.time() - t_setup
+
+    NEV = 6 if w.kind == "moe" else 3
+
+    def step(ev):
+        if w.kind == "moe":
+            amax_h.zero_()  # SiLU*mul epilogue max-combines into it
+            ev[0].record()
+            rt = L.moe_route(lg, w.topk)
+            ev[1].record()
+            x_in = P.quantize_input(x, nsx)
+            ev[2].record()
+            h = P.gemm(x_in, wgu, rt.expert_offsets, rows, gather=rt.gather_rows,
+                       epilogue=L.NVFP4_EPI_SILU_MUL_BF16, out_amax=amax_h)
+            ev[3].record()
+            h_in = P.quantize_input(h, nsh, amax_in=amax_h)
+            ev[4].record()
+            y = P.gemm(h_in, wd, rt.expert_offsets, rows)
+            ev[5].record()
+            return x_in, h_in, y, rt
+        ev[0].record()
+        x_in = P.quantize_input(x, nsx)
+        ev[1].record()
+        y = P.gemm(x_in, wq, offs, w.rows)
+        ev[2].record()
+        return x_in, None, y, None
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(NEV)]
+    for _ in range(args.warmup):
+        out = step(mk())
+    torch.cuda.synchronize()
+    evs = [mk() for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        out = step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    def seg(i):  # mean ms of segment i over the timed steps
+        return float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+
+    x_in, h_in, y, rt = out
+    bx = int(x_in.rac.kblock_active.sum().item()) if rac else 0
+    res = {}
+    if w.kind == "moe":
+        bh = int(h_in.rac.kblock_active.sum().item()) if rac else 0
+        N_gu, K_gu, N_d, K_d = 2 * w.I, w.H, w.H, w.I
+        f_gu = 2.0 * rows * N_gu * (K_gu + 16 * bx)
+        f_d = 2.0 * rows * N_d * (K_d + 16 * bh)
+        t_route, t_qx, t_gu, t_qh, t_d = (seg(i) for i in range(5))
+        flops = f_gu + f_d
+        dom = dict(name="w4a4_grouped_gemm_rac gate/up (SiLU*mul epilogue)", flops=f_gu, ms=t_gu)
+        qx_bytes = w.T * w.H * 2 + 2 * (w.T * w.H // 2 + w.T * w.H // 16) if rac else \
+            w.T * w.H * 2 + w.T * w.H // 2 + w.T * w.H // 16
+        qh_bytes = rows * w.I * 2 + (2 if rac else 1) * (rows * w.I // 2 + rows * w.I // 16)
+        res.update(
+            route_us=t_route * 1e3,
+            quant_x=dict(us=t_qx * 1e3, bytes=qx_bytes, gbs=qx_bytes / t_qx / 1e6,
+                         frac_hbm=qx_bytes / t_qx / 1e6 / PEAK_HBM_GBS),
+            gemm_gate_up=dict(us=t_gu * 1e3, tflops=f_gu / t_gu / 1e9,
+                              frac_mfma=f_gu / t_gu / 1e9 / PEAK_F16_TFLOPS,
+                              active_kblocks=bx, kblocks=K_gu // 16),
+            quant_h=dict(us=t_qh * 1e3, bytes=qh_bytes, gbs=qh_bytes / t_qh / 1e6,
+                         frac_hbm=qh_bytes / t_qh / 1e6 / PEAK_HBM_GBS),
+            gemm_down=dict(us=t_d * 1e3, tflops=f_d / t_d / 1e9,
+                           frac_mfma=f_d / t_d / 1e9 / PEAK_F16_TFLOPS,
+                           active_kblocks=bh, kblocks=K_d // 16))
+        cnt = np.diff(rt.expert_offsets.cpu().numpy())
+        res["rows_per_expert"] = dict(min=int(cnt.min()), median=float(np.median(cnt)),
+                                      max=int(cnt.max()), empty=int((cnt == 0).sum()))
+        cfg = dict(workload=w.name, tokens=w.T, experts=w.E, topk=w.topk, hidden=w.H,
+                   intermediate=w.I, gemm_rows=rows, rac=rac, n_select_x=nsx, n_select_h=nsh)
+    else:
+        f = 2.0 * w.rows * w.N * (w.K + 16 * bx)
+        t_q, t_g = seg(0), seg(1)
+        flops = f
+        dom = dict(name="w4a4_grouped_gemm_rac dense", flops=f, ms=t_g)
+        res.update(quant_x=dict(us=t_q * 1e3), gemm=dict(us=t_g * 1e3, tflops=f / t_g / 1e9))
+        cfg = dict(workload=w.name, rows=w.rows, K=w.K, N=w.N, rac=rac, n_select_x=nsx)
+
+    value = flops / (ms_step * 1e-3) / 1e12
+    ach = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
+    line = {
+        "metric": "NVFP4 W4A4+RAC MoE grouped GEMM TFLOP/s (whole step, algorithmic flops)",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded; bf16 activations, N(0,0.02) weights pre-quantized to NVFP4)",
+        "config": cfg,
+        "roofline": {"bound": "mfma", "kernel": dom["name"], "achieved": round(ach, 3),
+                     "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_F16_TFLOPS, 4), "traffic": None},
+        "breakdown": res,
+        "setup_s": round(t_setup, 1),
+    }
+    if args.cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, x_np, args.cpu_sample_experts, rac)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, x_np, n_experts, rac):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    quantize + RAC of X, then the gate/up grouped GEMM (main + residual) over
+    the routed rows of the first n_experts experts."""
+    from nvfp4_w4a4_moe_quant_amd import datagen as D
+    from oracle import oracle as O
+
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    if w.kind == "moe":
+        d = O.quantize_rac(x_np, w.n_select_x)
+        rt = O.route(D.router_logits(w), w.topk)
+        ex = list(range(min(n_experts, w.E)))
+        rows = np.concatenate([rt["gather"][rt["offsets"][e]:rt["offsets"][e + 1]] for e in ex])
+        offs = np.concatenate([[0], np.cumsum([rt["offsets"][e + 1] - rt["offsets"][e] for e in ex])])
+        wq = [O.quantize(m) for _, m in D.expert_weights(w, "gate_up", ex)]
+        wst = (np.stack([q[0] for q in wq]), np.stack([q[1] for q in wq]),
+               np.array([q[2] for q in wq], np.float32))
+        t1 = time.perf_counter()
+        O.grouped_gemm(2 * w.I, w.H, offs.astype(np.int32), rows.astype(np.int32),
+                       (d["codes"], d["scales"], d["s_t"]),
+                       (d["res_codes"], d["res_scales"], d["s_tr"]) if rac else None, wst)
+        t2 = time.perf_counter()
+        bx = int(d["active"].sum())
+        flops = 2.0 * len(rows) * 2 * w.I * (w.H + (16 * bx if rac else 0))
+        sample = (f"oracle quantize+RAC of X [{w.T}x{w.H}] and routing (not in the rate), then "
+                  f"the gate/up grouped GEMM over the {len(rows)} routed rows of experts "
+                  f"0..{len(ex) - 1} (main + residual, exact int64 sums)")
+    else:
+        d = O.quantize_rac(x_np, w.n_select_x)
+        c, s, t = O.quantize(D.dense_weight(w))
+        t1 = time.perf_counter()
+        O.grouped_gemm(w.N, w.K, np.array([0, w.rows], np.int32), None,
+                       (d["codes"], d["scales"], d["s_t"]),
+                       (d["res_codes"], d["res_scales"], d["s_tr"]) if rac else None,
+                       (c[None], s[None], np.array([t], np.float32)))
+        t2 = time.perf_counter()
+        bx = int(d["active"].sum())
+        flops = 2.0 * w.rows * w.N * (w.K + (16 * bx if rac else 0))
+        sample = f"oracle quantize+RAC and the full dense GEMM {w.rows}x{w.K}x{w.N}"
+    return {"value": round(flops / (t2 - t1) / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle", "sample": sample, "gemm_s": round(t2 - t1, 2),
+            "total_s": round(t2 - t0, 2)}
+
+
+if __name__ == "__main__":
+    main()

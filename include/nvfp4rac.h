@@ -1,0 +1,206 @@
+/*
+ * nvfp4rac -- NVFP4 W4A4 MoE GEMMs with Residual Activation Compensation,
+ * native on AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * What the calls compute (cited by page title and section):
+ *  - QUADS arXiv abstract (mlsanity paper page, "Abstract (arXiv)"): NVFP4
+ *    pairs fine-grained scaling with native W4A4 FP4 GEMMs; activations are
+ *    recomputed online and quantized on the coarse E2M1 grid; Residual
+ *    Activation Compensation (RAC) corrects high-error activation channels
+ *    while keeping the native W4A4 GEMMs.
+ *  - Blog post "Why 4-bit RL rollout collapses - and it isn't the weights",
+ *    section "The failure mode": E2M1 has eight magnitude levels per sign;
+ *    weights go through one shared quantize-dequantize path.
+ *  - Same post, section "Two fixes, on two different sides": RAC finds roughly
+ *    the top 50% of activation channels by quantization error and runs a
+ *    second, residual FP4 pass over just those channels, fused into the
+ *    existing kernels; the main W4A4 pass stays intact.
+ *
+ * Number formats (the pages say only "fine-grained scaling"; this library
+ * implements the standard NVFP4 layout):
+ *  - element: E2M1 code, 4 bits, sign in bit 3, magnitude index in bits 0-2
+ *    over {0, 0.5, 1, 1.5, 2, 3, 4, 6}; -0 is never produced.
+ *  - block scale: one OCP E4M3 byte (bias 7, max 448, never NaN, sign 0) per
+ *    16 consecutive elements along K, blocks starting at k = 0.
+ *  - tensor scale: FP32 s_t = RN32(amax / 2688), 2688 = 6 * 448.
+ *  - layout: codes[rows, K/2] bytes, element 2j in the low nibble of byte j;
+ *    scales[rows, K/16] bytes.  Weights are [N, K] (out x in), y = x W^T.
+ *  - rounding: round-to-nearest-even with saturation for both encodings.
+ *    rho_b = RN32(amax_b / (6 s_t)), s_b = E4M3(rho_b), S_b = RN32(s_b s_t),
+ *    r_b = RN32(1 / S_b), code = E2M1(RN32(x r_b)).
+ *
+ * Conventions for every call:
+ *  - Pointers are device pointers unless stated; the caller owns all memory.
+ *    Calls allocate nothing; scratch comes from the caller's workspace `ws`
+ *    of at least the size the matching *_workspace_size call returns.
+ *  - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL is
+ *    the default stream).  Arguments are validated on the host before
+ *    anything is enqueued; a failed check returns its status and enqueues no
+ *    work.  Launch failures return NVFP4_ERR_HIP.  Device faults surface at
+ *    the caller's next synchronization.
+ *  - Not checked on the device (preconditions): finite inputs; group offsets
+ *    non-decreasing with the last equal to total_rows; gather indices in
+ *    range; an `amax_in` not smaller than the true max|x|.
+ *  - Re-entrant on distinct buffers; results are bit-reproducible (integer
+ *    and max reductions only; no floating-point atomics).
+ */
+#ifndef NVFP4RAC_H
+#define NVFP4RAC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,      /* a required pointer is NULL */
+  NVFP4_ERR_SHAPE = 2,     /* a size is negative or violates a divisibility rule */
+  NVFP4_ERR_DTYPE = 3,     /* unknown dtype or epilogue enum */
+  NVFP4_ERR_ALIGN = 4,     /* a pointer or leading dimension is misaligned */
+  NVFP4_ERR_WORKSPACE = 5, /* workspace missing or too small */
+  NVFP4_ERR_HIP = 6        /* a kernel launch failed */
+} nvfp4_status_t;
+
+typedef enum { NVFP4_IN_F32 = 0, NVFP4_IN_BF16 = 1 } nvfp4_in_dtype_t;
+
+typedef enum {
+  NVFP4_EPI_F32 = 0,          /* out: float [total_rows, N] */
+  NVFP4_EPI_SILU_MUL_BF16 = 1 /* out: bf16 [total_rows, N/2], h = silu(gate) * up */
+} nvfp4_epilogue_t;
+
+/* Text for a status code (static storage). */
+const char* nvfp4_status_string(int status);
+
+/* ------------------------------------------------------------------------
+ * nvfp4_quantize -- online NVFP4 quantization of one tensor (abstract:
+ * activations recomputed online and quantized on the E2M1 grid; blog, "The
+ * failure mode": weights use the same shared path).
+ *
+ * x        [rows, K] row-major, row stride ldx elements, dtype F32 or BF16.
+ *          Requires K % 16 == 0, ldx % 16 == 0, ldx >= K, x 16-byte aligned.
+ * amax_in  nullable device float: the tensor amax to use instead of max|x|
+ *          (a producer that already knows it, e.g. the SiLU*mul epilogue).
+ * codes    out [rows, K/2];  scales out [rows, K/16];  tensor_scale out [1].
+ * channel_score, channel_max  nullable pair (both or neither).  When given,
+ *          the RAC per-channel error statistics are computed in the same pass
+ *          over x:  e = x - deq(q(x)) in FP32;  with Es the exponent of s_t
+ *          (s_t = f 2^Es, f in [0.5, 1)) and q = min(floor(|e| 2^(8-Es)),
+ *          2^17 - 1):  channel_score[k] = sum over rows of q^2 (int64, exact)
+ *          and channel_max[k] = max over rows of |e| (float).  They feed
+ *          rac_select_residual.  (Blog, "Two fixes": channels ranked by
+ *          quantization error; the metric is this library's reading: the
+ *          sum of squared errors, in fixed point so that it is exact.)
+ * rows == 0 is allowed (writes s_t = RN32(amax_in/2688) or 0, and zero stats).
+ * ------------------------------------------------------------------------ */
+size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t K);
+int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx,
+                   const float* amax_in, uint8_t* codes, uint8_t* scales,
+                   float* tensor_scale, int64_t* channel_score, float* channel_max,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * rac_select_residual -- RAC channel selection and residual re-quantization
+ * (blog, "Two fixes, on two different sides": roughly the top 50% of
+ * activation channels by quantization error get a second, residual FP4 pass).
+ *
+ * Inputs: the same x, codes, scales, tensor_scale that nvfp4_quantize used
+ * and wrote, and its channel_score / channel_max.
+ * n_select (0 <= n_select <= K; K/2 in the workloads): the channels with the
+ *          largest channel_score are selected, ties toward the lower channel
+ *          index.
+ * selected out [n_select] int32, ascending channel indices.
+ * kblock_active out [K/16]: 1 where the 16-block holds a selected channel.
+ * res_codes/res_scales out, same layout as codes/scales; res_tensor_scale out:
+ *          r = e on selected channels and 0 elsewhere, quantized as its own
+ *          NVFP4 tensor in the same 16-element blocks with
+ *          s_tr = RN32(max over selected k of channel_max[k] / 2688)
+ *          (= max|r| / 2688).
+ * Requires K <= 16384 and the layout rules of nvfp4_quantize.
+ * ------------------------------------------------------------------------ */
+size_t rac_select_residual_workspace_size(int64_t rows, int64_t K);
+int rac_select_residual(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx,
+                        const uint8_t* codes, const uint8_t* scales,
+                        const float* tensor_scale, const int64_t* channel_score,
+                        const float* channel_max, int64_t n_select,
+                        int32_t* selected, uint8_t* kblock_active,
+                        uint8_t* res_codes, uint8_t* res_scales,
+                        float* res_tensor_scale, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_route -- top-k routing of T tokens over E experts and the gather map
+ * for the grouped GEMM (the MoE layer of the rollout model; the pages give no
+ * routing details, so this is the plain reading).
+ *
+ * logits   [T, E] float.  Per token, the k experts with the largest logit,
+ *          ties toward the lower expert index, in (logit desc, index asc)
+ *          order -> topk_ids [T, k].
+ * topk_weights nullable [T, k]: softmax(logits) of the chosen experts (not
+ *          renormalized; FP32, not bit-defined).
+ * expert_offsets [E+1]: exclusive prefix sum of per-expert counts.
+ * gather_rows [T*k]: source token of each grouped row, expert-major, tokens
+ *          ascending within an expert.  row_of [T, k]: grouped row of
+ *          (token, slot).
+ * Requires 1 <= k <= min(E, 16), E <= 1024.
+ * ------------------------------------------------------------------------ */
+size_t moe_route_workspace_size(int64_t T, int64_t E, int64_t k);
+int moe_route(const float* logits, int64_t T, int64_t E, int64_t k,
+              int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+              int32_t* gather_rows, int32_t* row_of, void* ws, size_t ws_bytes,
+              void* stream);
+
+/* ------------------------------------------------------------------------
+ * w4a4_grouped_gemm_rac -- grouped (per-expert) W4A4 GEMM with the RAC
+ * residual pass fused into the same kernel (abstract: native W4A4 GEMMs;
+ * blog, "Two fixes": the residual pass over the selected channels is layered
+ * on top of the intact main pass).
+ *
+ * For grouped row j of group g (offsets[g] <= j < offsets[g+1]) and src =
+ * gather_rows[j] (or j when gather_rows is NULL):
+ *   y[j, n] = s_tw[g] * ( s_ta * sum_k A[src,k] W_g[n,k]
+ *                       + s_tr * sum_{k in active blocks} R[src,k] W_g[n,k] )
+ * with A, R, W the exact dequantized values g * s_b (FP32 accumulation).
+ * r_codes == NULL turns RAC off (naive W4A4).  kblock_active == NULL means
+ * every block is active; skipping an inactive block is exact because its
+ * residual is zero.
+ * Epilogue F32 writes y.  Epilogue SILU_MUL_BF16 treats W as the fused
+ * gate/up weight [N = 2I, K] with the gate in rows [0, I) and writes
+ * h[j, i] = bf16(silu(y[j, i]) * y[j, I + i]) to out [total_rows, I] and, if
+ * out_amax is given, max-combines max|h| into *out_amax (an atomic max on the
+ * float bits; the caller initializes *out_amax, normally to 0, so that the
+ * call launches the GEMM kernel alone).
+ * Requires K % 128 == 0, N % 128 == 0, all tensors 16-byte aligned.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int64_t num_groups;           /* G >= 1 */
+  int64_t N;                    /* output columns (2I for SILU_MUL) */
+  int64_t K;                    /* contraction length */
+  int64_t total_rows;           /* rows of the grouped output */
+  const int32_t* group_offsets; /* [G+1] */
+  const int32_t* gather_rows;   /* [total_rows] or NULL (identity) */
+  const uint8_t* a_codes;       /* [src_rows, K/2] */
+  const uint8_t* a_scales;      /* [src_rows, K/16] */
+  const float* a_tscale;        /* [1] */
+  const uint8_t* r_codes;       /* residual, or NULL for RAC off */
+  const uint8_t* r_scales;
+  const float* r_tscale;
+  const uint8_t* kblock_active; /* [K/16] or NULL */
+  const uint8_t* w_codes;       /* [G, N, K/2] */
+  const uint8_t* w_scales;      /* [G, N, K/16] */
+  const float* w_tscale;        /* [G] */
+  int64_t epilogue;             /* nvfp4_epilogue_t */
+  void* out;                    /* float [total_rows, N] or bf16 [total_rows, N/2] */
+  float* out_amax;              /* SILU_MUL only, nullable, caller-initialized */
+} w4a4_gemm_args_t;
+
+size_t w4a4_grouped_gemm_rac_workspace_size(const w4a4_gemm_args_t* args);
+int w4a4_grouped_gemm_rac(const w4a4_gemm_args_t* args, void* ws, size_t ws_bytes,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4RAC_H */

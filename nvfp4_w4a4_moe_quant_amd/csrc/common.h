@@ -1,0 +1,132 @@
+// Internal helpers shared by the HIP translation units of libnvfp4rac.
+// gfx950 only; compiled with -ffp-contract=off so that the quantizer's FP32
+// steps stay the single IEEE operations the format definition names.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nvfp4rac.h"
+
+#define NV_RETURN_IF(cond, code) \
+  do {                           \
+    if (cond) return (code);     \
+  } while (0)
+
+static inline int nv_launch_status() {
+  return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+static inline bool nv_aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+static inline size_t nv_round256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// ---------------------------------------------------------------- formats
+
+// E4M3 byte (0..0x7E) -> float value.  Exponent field 0 is subnormal b*2^-9.
+__device__ __forceinline__ float nv_e4m3_to_f32(uint32_t b) {
+  return (b < 8u) ? (float)b * 0.001953125f
+                  : __uint_as_float((((b >> 3) + 120u) << 23) | ((b & 7u) << 20));
+}
+
+// Nearest E4M3 to rho >= 0 (finite), ties to even, saturating at 448.
+// Normal range: round the FP32 mantissa to 3 bits with the carry running into
+// the exponent; below 2^-6 the grid is uniform with step 2^-9.
+__device__ __forceinline__ uint32_t nv_e4m3_encode(float rho) {
+  if (!(rho > 0.0f)) return 0u;
+  if (rho >= 448.0f) return 0x7Eu;
+  if (rho < 0.015625f) return (uint32_t)__builtin_rintf(rho * 512.0f);
+  const uint32_t u = __float_as_uint(rho);
+  const uint32_t c = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
+  return c > 0x7Eu ? 0x7Eu : c;
+}
+
+// Nearest E2M1 code to v, ties to the even magnitude index, saturating at 6;
+// the thresholds are the midpoints of {0, .5, 1, 1.5, 2, 3, 4, 6}, strict where
+// the lower neighbour has the even index.
+__device__ __forceinline__ uint32_t nv_e2m1_encode(float v) {
+  const float a = __builtin_fabsf(v);
+  const uint32_t idx = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) +
+                       (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
+                       (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                       (uint32_t)(a > 5.0f);
+  return (v < 0.0f && idx != 0u) ? (idx | 8u) : idx;
+}
+
+// E2M1 code -> signed float value.
+__device__ __forceinline__ float nv_e2m1_to_f32(uint32_t c) {
+  const uint32_t idx = c & 7u;
+  const float g = (idx < 2u) ? (float)idx * 0.5f
+                             : __uint_as_float((((idx >> 1) + 126u) << 23) | ((idx & 1u) << 22));
+  return (c & 8u) ? -g : g;
+}
+
+// Tensor scale s_t = RN32(amax / 2688) (double quotient rounded once).
+__device__ __forceinline__ float nv_tensor_scale(float amax) {
+  return (float)((double)amax / 2688.0);
+}
+
+// Block scale code from the block amax: rho = RN32(amax_b / (6 s_t)).
+__device__ __forceinline__ uint32_t nv_block_scale(float amax_b, float s_t) {
+  if (s_t == 0.0f) return 0u;
+  const float rho = (float)((double)amax_b / (6.0 * (double)s_t));
+  return nv_e4m3_encode(rho);
+}
+
+// Reciprocal of the effective block scale, correctly rounded (0 for S_b = 0).
+__device__ __forceinline__ float nv_block_recip(float Sb) {
+  return (Sb > 0.0f) ? (float)(1.0 / (double)Sb) : 0.0f;
+}
+
+// Score shift 8 - Es where s_t = f * 2^Es, f in [0.5, 1).
+__device__ __forceinline__ int nv_score_shift(float s_t) {
+  return (s_t == 0.0f) ? 8 : 8 - __builtin_amdgcn_frexp_expf(s_t);
+}
+
+// Fixed-point magnitude q = min(floor(|e| 2^shift), 2^17 - 1), as float.
+__device__ __forceinline__ float nv_score_q(float e, int shift) {
+  const float q = __builtin_floorf(__builtin_ldexpf(__builtin_fabsf(e), shift));
+  return __builtin_fminf(q, 131071.0f);
+}
+
+// bf16 bits -> float.
+__device__ __forceinline__ float nv_bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t nv_f32_to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Load 16 consecutive inputs starting at element offset `off` (16-byte aligned).
+__device__ __forceinline__ void nv_load16(const void* x, int bf16, int64_t off, float* v) {
+  if (bf16) {
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + off);
+    const uint4 a = p[0], b = p[1];
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 q = p[i];
+      v[4 * i] = q.x;
+      v[4 * i + 1] = q.y;
+      v[4 * i + 2] = q.z;
+      v[4 * i + 3] = q.w;
+    }
+  }
+}
+
+// Wave-wide max of a non-negative float (64 lanes).
+__device__ __forceinline__ float nv_wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}

@@ -189,3 +189,18 @@ def router_logits(w: Workload) -> np.ndarray:
         gum = rng(w, S_ROUTE).gumbel(size=(w.T, w.E))
         return (logp[None, :] + gum).astype(np.float32)
     return rng(w, S_ROUTE).standard_normal((w.T, w.E), dtype=np.float32)
+
+
+S_HIDDEN = 7
+
+
+def hidden_like(w: Workload, rows: int) -> np.ndarray:
+    """A seeded stand-in for the expert intermediate H [rows, I] (bf16 values):
+    the product of two N(0, 0.05^2) draws through silu, i.e. the distribution
+    silu(g) * u of a gate/up output, for testing the H-side quantizer and the
+    down projection on their own."""
+    g = rng(w, S_HIDDEN)
+    a = g.standard_normal((rows, w.I), dtype=np.float32) * np.float32(0.05)
+    b = g.standard_normal((rows, w.I), dtype=np.float32) * np.float32(0.05)
+    h = a / (np.float32(1.0) + np.exp(-a)) * b
+    return _round_dtype(h.astype(np.float32), "bf16")

@@ -1,0 +1,91 @@
+"""The rollout hot path as a sequence of C-ABI calls (no arithmetic here).
+
+Dense linear (one GEMM input):
+    nvfp4_quantize(X, stats) -> rac_select_residual -> w4a4_grouped_gemm_rac
+MoE FFN layer (QUADS rollout: online NVFP4 activations + RAC on every GEMM
+input, native W4A4 expert GEMMs; arXiv abstract on the mlsanity page and the
+blog post's section "Two fixes, on two different sides"):
+    moe_route(logits)
+    nvfp4_quantize(X, stats) -> rac_select_residual(X)
+    w4a4_grouped_gemm_rac(gate/up, gather = routed rows, epilogue SiLU*mul -> H
+                          bf16 and max|H|)
+    nvfp4_quantize(H, amax_in = max|H|, stats) -> rac_select_residual(H)
+    w4a4_grouped_gemm_rac(down) -> Y (FP32, rows in expert order)
+Weights are quantized once, per expert and projection, by the same
+nvfp4_quantize ("shared quantize-dequantize path" for weights: blog post,
+section "The failure mode").
+"""
+from __future__ import annotations
+
+from typing import Dict, Iterable, NamedTuple, Optional, Tuple
+
+import torch
+
+from . import _lib as L
+
+
+class QuantWeights(NamedTuple):
+    w: L.NVFP4          # codes [G, N, K/2], scales [G, N, K/16], tscale [G]
+    N: int
+    K: int
+
+
+def quantize_weights(mats: Iterable[Tuple[int, torch.Tensor]], G: int, N: int, K: int,
+                     device) -> QuantWeights:
+    """mats yields (group index, W_g [N, K] on any device); each W_g becomes one
+    NVFP4 tensor with its own tensor scale."""
+    codes = torch.empty((G, N, K // 2), dtype=torch.uint8, device=device)
+    scales = torch.empty((G, N, K // 16), dtype=torch.uint8, device=device)
+    ts = torch.empty(G, dtype=torch.float32, device=device)
+    for g, wg in mats:
+        wg = wg.to(device, non_blocking=True)
+        q = L.nvfp4_quantize(wg).q
+        codes[g].copy_(q.codes)
+        scales[g].copy_(q.scales)
+        ts[g:g + 1].copy_(q.tscale)
+    return QuantWeights(L.NVFP4(codes, scales, ts), N, K)
+
+
+class GemmInput(NamedTuple):
+    qo: L.QuantOut
+    rac: Optional[L.RacOut]
+
+
+def quantize_input(x: torch.Tensor, n_select: Optional[int],
+                   amax_in: Optional[torch.Tensor] = None) -> GemmInput:
+    """Online quantization of a GEMM input; n_select None turns RAC off."""
+    qo = L.nvfp4_quantize(x, amax_in=amax_in, stats=n_select is not None)
+    rac = L.rac_select_residual(x, qo, n_select) if n_select is not None else None
+    return GemmInput(qo, rac)
+
+
+def gemm(inp: GemmInput, wq: QuantWeights, offsets: torch.Tensor, total_rows: int, *,
+         gather: Optional[torch.Tensor] = None, epilogue: int = L.NVFP4_EPI_F32,
+         out_amax: Optional[torch.Tensor] = None) -> torch.Tensor:
+    return L.w4a4_grouped_gemm_rac(
+        inp.qo.q, wq.w, offsets, N=wq.N, K=wq.K, total_rows=total_rows, gather_rows=gather,
+        r=inp.rac.r if inp.rac else None,
+        kblock_active=inp.rac.kblock_active if inp.rac else None,
+        epilogue=epilogue, out_amax=out_amax)
+
+
+def dense_forward(x: torch.Tensor, wq: QuantWeights, n_select: Optional[int]) -> Dict:
+    rows = x.shape[0]
+    offsets = torch.tensor([0, rows], dtype=torch.int32, device=x.device)
+    inp = quantize_input(x, n_select)
+    y = gemm(inp, wq, offsets, rows)
+    return dict(x_in=inp, y=y, offsets=offsets)
+
+
+def moe_forward(x: torch.Tensor, logits: torch.Tensor, wgu: QuantWeights, wd: QuantWeights,
+                topk: int, n_sel_x: Optional[int], n_sel_h: Optional[int]) -> Dict:
+    T = x.shape[0]
+    rt = L.moe_route(logits, topk)
+    rows = T * topk
+    x_in = quantize_input(x, n_sel_x)
+    amax_h = torch.zeros(1, dtype=torch.float32, device=x.device)
+    h = gemm(x_in, wgu, rt.expert_offsets, rows, gather=rt.gather_rows,
+             epilogue=L.NVFP4_EPI_SILU_MUL_BF16, out_amax=amax_h)
+    h_in = quantize_input(h, n_sel_h, amax_in=amax_h)
+    y = gemm(h_in, wd, rt.expert_offsets, rows)
+    return dict(route=rt, x_in=x_in, h=h, amax_h=amax_h, h_in=h_in, y=y)

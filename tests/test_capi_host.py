@@ -1,0 +1,116 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/nvfp4rac.h declares, and rejects invalid arguments
+with the documented status before enqueuing any work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from nvfp4_w4a4_moe_quant_amd import _lib as L
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "nvfp4rac.h")
+OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, EHIP = range(7)
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) == set(L.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_missing_library_raises():
+    with pytest.raises(RuntimeError):
+        L.load("/nonexistent/libnvfp4rac.so")
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert lib.nvfp4_status_string(s)
+    assert b"unknown" in lib.nvfp4_status_string(99)
+
+
+FAKE = ctypes.c_void_p(0x100000)      # 16-byte aligned, never dereferenced
+FAKE_MIS = ctypes.c_void_p(0x100004)  # misaligned
+
+
+def _q(lib, x=FAKE, dtype=1, rows=4, K=32, ldx=32, codes=FAKE, scales=FAKE, ts=FAKE,
+       score=None, chmax=None, ws=FAKE, wsb=1 << 20, amax=None):
+    return lib.nvfp4_quantize(x, dtype, rows, K, ldx, amax, codes, scales, ts, score, chmax,
+                              ws, wsb, None)
+
+
+def test_quantize_validation(lib):
+    assert _q(lib, x=None) == ENULL
+    assert _q(lib, codes=None) == ENULL
+    assert _q(lib, score=FAKE) == ENULL            # score without chmax
+    assert _q(lib, dtype=7) == EDTYPE
+    assert _q(lib, K=24, ldx=32) == ESHAPE          # K % 16
+    assert _q(lib, rows=-1) == ESHAPE
+    assert _q(lib, ldx=16) == ESHAPE                # ldx < K
+    assert _q(lib, ldx=40, K=32) == EALIGN          # ldx % 16
+    assert _q(lib, x=FAKE_MIS) == EALIGN
+    assert _q(lib, ws=None) == EWS
+    assert _q(lib, wsb=16) == EWS
+
+
+def test_rac_validation(lib):
+    def call(**kw):
+        a = dict(x=FAKE, dtype=1, rows=4, K=32, ldx=32, codes=FAKE, scales=FAKE, ts=FAKE,
+                 score=FAKE, chmax=FAKE, nsel=16, sel=FAKE, kact=FAKE, rc=FAKE, rs=FAKE,
+                 rts=FAKE, ws=FAKE, wsb=1 << 20)
+        a.update(kw)
+        return lib.rac_select_residual(a["x"], a["dtype"], a["rows"], a["K"], a["ldx"],
+                                       a["codes"], a["scales"], a["ts"], a["score"], a["chmax"],
+                                       a["nsel"], a["sel"], a["kact"], a["rc"], a["rs"],
+                                       a["rts"], a["ws"], a["wsb"], None)
+    assert call(score=None) == ENULL
+    assert call(nsel=33) == ESHAPE
+    assert call(nsel=-1) == ESHAPE
+    assert call(K=16 * 1024 * 2, ldx=16 * 1024 * 2) == ESHAPE
+    assert call(sel=None) == ENULL
+    assert call(rc=FAKE_MIS) == EALIGN
+    assert call(ws=None) == EWS
+
+
+def test_route_validation(lib):
+    def call(T=8, E=16, k=2, ws=FAKE, wsb=1 << 20, ids=FAKE):
+        return lib.moe_route(FAKE, T, E, k, ids, None, FAKE, FAKE, FAKE, ws, wsb, None)
+    assert call(ids=None) == ENULL
+    assert call(k=0) == ESHAPE
+    assert call(k=17, E=32) == ESHAPE
+    assert call(E=2000) == ESHAPE
+    assert call(k=5, E=4) == ESHAPE
+    assert call(ws=None) == EWS
+
+
+def test_gemm_validation(lib):
+    def call(**kw):
+        a = L.GemmArgs(num_groups=2, N=256, K=256, total_rows=10, group_offsets=FAKE,
+                       a_codes=FAKE, a_scales=FAKE, a_tscale=FAKE, w_codes=FAKE,
+                       w_scales=FAKE, w_tscale=FAKE, epilogue=0, out=FAKE)
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return lib.w4a4_grouped_gemm_rac(ctypes.byref(a), None, 0, None)
+    assert lib.w4a4_grouped_gemm_rac(None, None, 0, None) == ENULL
+    assert call(out=None) == ENULL
+    assert call(r_codes=FAKE) == ENULL              # residual codes without scales
+    assert call(epilogue=5) == EDTYPE
+    assert call(K=200) == ESHAPE                    # K % 128
+    assert call(N=96) == ESHAPE                     # N % 128
+    assert call(num_groups=0) == ESHAPE
+    assert call(a_codes=FAKE_MIS) == EALIGN
+    assert call(kblock_active=ctypes.c_void_p(0x100004), r_codes=FAKE, r_scales=FAKE,
+                r_tscale=FAKE) == EALIGN

@@ -1,0 +1,314 @@
+"""GPU parity of the HIP library against the CPU oracle, called through the
+C ABI (via the ctypes binding).
+
+Bars: bit-exact codes, scales, tensor scales, channel statistics, selected
+channels, block activity, residual bytes and routing indices; FP32 GEMM
+outputs within relative Frobenius error 1e-5 (only the FP32 accumulation
+order differs from the oracle's exact sums); SiLU*mul output within one bf16
+ulp (its exp() is not bit-defined across implementations).  The down
+projection of the MoE chain is checked on an H that comes from the oracle (or
+from the seeded generator), never from the GPU."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from nvfp4_w4a4_moe_quant_amd import _lib as L
+from nvfp4_w4a4_moe_quant_amd import datagen as D
+from nvfp4_w4a4_moe_quant_amd import pipeline as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+REL_F = 1e-5
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x, dtype):
+    x = np.ascontiguousarray(x, np.float32)
+    if dtype == "bf16":
+        return torch.from_numpy(D.bf16_bits(x).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(x).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def eq(a, b, what):
+    a, b = np.asarray(a), np.asarray(b)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    bad = np.flatnonzero(a.ravel() != b.ravel())
+    assert bad.size == 0, f"{what}: {bad.size} mismatches, first at {bad[:8]}: " \
+                          f"gpu {a.ravel()[bad[:8]]} oracle {b.ravel()[bad[:8]]}"
+
+
+def rel_frob(gpu, ref):
+    ref = np.asarray(ref, np.float64)
+    d = np.linalg.norm(np.asarray(gpu, np.float64) - ref)
+    n = np.linalg.norm(ref)
+    return d / n if n else d
+
+
+def bf16_ulp_ok(h_gpu_bits, h_ref_bits):
+    a = D.bf16_to_f32(np.asarray(h_gpu_bits, np.uint16)).astype(np.float64)
+    b = D.bf16_to_f32(np.asarray(h_ref_bits, np.uint16)).astype(np.float64)
+    ulp = np.maximum(np.abs(b), 2.0 ** -126) * 2.0 ** -7
+    return np.abs(a - b) <= ulp * 1.0001
+
+
+def check_quant_rac(orc, x, dtype, n_select, amax=None, ldx_pad=0):
+    """Quantize + RAC on the GPU and the oracle; everything bit-exact."""
+    rows, K = x.shape
+    if ldx_pad:
+        big = np.zeros((rows, K + ldx_pad), np.float32)
+        big[:, :K] = x
+        xd = to_dev(big, dtype)[:, :K]
+    else:
+        xd = to_dev(x, dtype)
+    am = None if amax is None else torch.tensor([amax], dtype=torch.float32, device=DEV)
+    qo = L.nvfp4_quantize(xd, amax_in=am, stats=True)
+    rac = L.rac_select_residual(xd, qo, n_select)
+    d = orc.quantize_rac(x, n_select, amax=amax)
+    eq(host(qo.q.tscale)[0], np.float32(d["s_t"]), "tensor scale")
+    eq(host(qo.q.scales), d["scales"], "block scales")
+    eq(host(qo.q.codes), d["codes"], "codes")
+    eq(host(qo.channel_score), d["score"], "channel score")
+    eq(host(qo.channel_max), d["chmax"], "channel max")
+    eq(host(rac.selected), d["selected"], "selected")
+    eq(host(rac.kblock_active), d["active"], "kblock_active")
+    eq(host(rac.r.tscale)[0], np.float32(d["s_tr"]), "residual tensor scale")
+    eq(host(rac.r.scales), d["res_scales"], "residual scales")
+    eq(host(rac.r.codes), d["res_codes"], "residual codes")
+    return qo, rac, d
+
+
+# ------------------------------------------------------------ quantizer
+@pytest.mark.parametrize("wid", [1, 2])
+def test_quant_rac_workloads_small(orc, wid):
+    w = D.WORKLOADS[wid]
+    say(f"quant+rac workload {wid} {w.name}")
+    check_quant_rac(orc, D.activations(w), w.x_dtype, w.n_select_x)
+
+
+@pytest.mark.parametrize("rows,K,dtype", [(1, 16, "bf16"), (3, 48, "f32"), (257, 272, "bf16"),
+                                          (1000, 768, "bf16"), (33, 4112, "f32"),
+                                          (5, 7168, "bf16"), (2, 16384, "bf16")])
+def test_quant_rac_shapes(orc, rows, K, dtype):
+    say(f"quant+rac shape {rows}x{K} {dtype}")
+    rng = np.random.default_rng(rows * 7 + K)
+    x = rng.standard_normal((rows, K)).astype(np.float32)
+    x[:, rng.integers(0, K, 3)] *= 40.0
+    if dtype == "bf16":
+        x = D.bf16_to_f32(D.bf16_bits(x))
+    check_quant_rac(orc, x, dtype, K // 2)
+
+
+def test_quant_rac_edge_values(orc):
+    say("quant+rac edge values")
+    rng = np.random.default_rng(77)
+    x = rng.standard_normal((40, 64)).astype(np.float32)
+    x[0] = 0.0                                 # all-zero row
+    x[1, :16] = 1e-30                          # tiny block -> subnormal/zero scale
+    x[2, 16:32] = np.float32(3e-6)             # subnormal block scale
+    x[3, 5] = 1e4                              # tensor amax dominated by one value
+    x[4] = 2.5                                 # exact E2M1 ties after scaling
+    check_quant_rac(orc, x, "f32", 32)
+    check_quant_rac(orc, x, "f32", 0)
+    check_quant_rac(orc, x, "f32", 64)
+
+
+def test_quant_rac_ties_and_zero(orc):
+    say("quant+rac all-zero and tied scores")
+    check_quant_rac(orc, np.zeros((7, 128), np.float32), "f32", 64)
+    x = np.tile(np.linspace(-3, 3, 32, dtype=np.float32), (9, 4))  # repeated channels
+    check_quant_rac(orc, x, "f32", 50)
+
+
+def test_quant_amax_in_and_stride(orc):
+    say("quant with amax_in and padded rows")
+    rng = np.random.default_rng(78)
+    x = D.bf16_to_f32(D.bf16_bits(rng.standard_normal((100, 256)).astype(np.float32)))
+    check_quant_rac(orc, x, "bf16", 128, amax=float(np.abs(x).max()) * 1.5)
+    check_quant_rac(orc, x, "bf16", 128, ldx_pad=32)
+
+
+def test_quant_empty_rows(orc):
+    say("quant rows=0")
+    xd = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    qo = L.nvfp4_quantize(xd, stats=True)
+    rac = L.rac_select_residual(xd, qo, 32)
+    assert host(qo.q.tscale)[0] == 0.0
+    assert not host(qo.channel_score).any()
+    eq(host(rac.selected), np.arange(32), "selected of empty input")
+
+
+# ------------------------------------------------------------- routing
+@pytest.mark.parametrize("T,E,k,routing", [(1, 4, 1, "normal"), (300, 8, 2, "zipf"),
+                                           (1000, 128, 8, "normal"), (777, 256, 8, "normal"),
+                                           (513, 64, 6, "zipf")])
+def test_route(orc, T, E, k, routing):
+    say(f"route T={T} E={E} k={k} {routing}")
+    w = D.small_moe(90 + T, T, E, k, 64, 32, routing=routing, n_empty=2 if routing == "zipf" else 0)
+    lg = D.router_logits(w)
+    rt = L.moe_route(torch.from_numpy(lg).to(DEV), k)
+    d = orc.route(lg, k)
+    eq(host(rt.topk_ids), d["topk_ids"], "topk ids")
+    eq(host(rt.expert_offsets), d["offsets"], "offsets")
+    eq(host(rt.gather_rows), d["gather"], "gather")
+    eq(host(rt.row_of), d["row_of"], "row_of")
+    np.testing.assert_allclose(host(rt.topk_weights), d["topk_weights"], rtol=2e-5, atol=1e-7)
+
+
+def test_route_ties(orc):
+    say("route with tied logits")
+    lg = np.zeros((70, 16), np.float32)
+    lg[::3, 5] = 1.0
+    rt = L.moe_route(torch.from_numpy(lg).to(DEV), 4)
+    d = orc.route(lg, 4)
+    eq(host(rt.topk_ids), d["topk_ids"], "topk ids")
+    eq(host(rt.gather_rows), d["gather"], "gather")
+
+
+# --------------------------------------------------------------- GEMM
+def quant_weights_checked(orc, mats, G, N, K, dtype, check=None):
+    """Quantize weights on the GPU; check the bytes of groups `check` against
+    the oracle.  Returns (QuantWeights, {g: oracle (codes, scales, s_t)})."""
+    mats = list(mats)
+    wq = P.quantize_weights(((g, to_dev(m, dtype)) for g, m in mats), G, N, K, DEV)
+    ref = {}
+    for g, m in mats:
+        if check is None or g in check:
+            c, s, t = orc.quantize(m)
+            ref[g] = (c, s, t)
+            eq(host(wq.w.codes[g]), c, f"weight codes g{g}")
+            eq(host(wq.w.scales[g]), s, f"weight scales g{g}")
+            eq(host(wq.w.tscale[g:g + 1])[0], np.float32(t), f"weight tscale g{g}")
+    return wq, ref
+
+
+def w_stack(ref, G):
+    return (np.stack([ref[g][0] for g in range(G)]), np.stack([ref[g][1] for g in range(G)]),
+            np.array([ref[g][2] for g in range(G)], np.float32))
+
+
+@pytest.mark.parametrize("wid,rac", [(1, True), (1, False)])
+def test_dense_workload1(orc, wid, rac):
+    w = D.WORKLOADS[wid]
+    say(f"dense gemm workload {wid} rac={rac}")
+    x, W = D.activations(w), D.dense_weight(w)
+    wq, ref = quant_weights_checked(orc, [(0, W)], 1, w.N, w.K, w.x_dtype)
+    out = P.dense_forward(to_dev(x, w.x_dtype), wq, w.n_select_x if rac else None)
+    d = orc.quantize_rac(x, w.n_select_x)
+    a = (d["codes"], d["scales"], d["s_t"])
+    r = (d["res_codes"], d["res_scales"], d["s_tr"]) if rac else None
+    y_ref = orc.grouped_gemm(w.N, w.K, np.array([0, w.rows], np.int32), None, a, r, w_stack(ref, 1))
+    y = host(out["y"])
+    err = rel_frob(y, y_ref)
+    say(f"  rel frob {err:.3e}")
+    assert err <= REL_F
+    np.testing.assert_allclose(y, y_ref, rtol=1e-4, atol=1e-5 * np.abs(y_ref).max())
+
+
+@pytest.mark.parametrize("rows,K,N", [(200, 384, 256), (1, 128, 128), (129, 256, 384)])
+def test_dense_ragged(orc, rows, K, N):
+    say(f"dense gemm ragged {rows}x{K}x{N}")
+    w = D.small_dense(50 + rows, rows, K, N)
+    x, W = D.activations(w), D.dense_weight(w)
+    wq, ref = quant_weights_checked(orc, [(0, W)], 1, N, K, "bf16")
+    out = P.dense_forward(to_dev(x, "bf16"), wq, K // 2)
+    d = orc.quantize_rac(x, K // 2)
+    y_ref = orc.grouped_gemm(N, K, np.array([0, rows], np.int32), None,
+                             (d["codes"], d["scales"], d["s_t"]),
+                             (d["res_codes"], d["res_scales"], d["s_tr"]), w_stack(ref, 1))
+    err = rel_frob(host(out["y"]), y_ref)
+    say(f"  rel frob {err:.3e}")
+    assert err <= REL_F
+
+
+def test_gemm_onehot_reads_dequantized_weights(orc):
+    """A = one-hot rows (value 1 at k = i): y[i, n] = s_ta * s_tw * W_deq[n, i]."""
+    say("gemm one-hot")
+    K, N = 128, 128
+    x = np.zeros((K, K), np.float32)
+    np.fill_diagonal(x, 2688.0)              # s_t = 1, s_b = 448, g = 6
+    rng = np.random.default_rng(5)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    wq, ref = quant_weights_checked(orc, [(0, W)], 1, N, K, "f32")
+    out = P.dense_forward(to_dev(x, "f32"), wq, None)
+    wdeq = orc.dequantize(ref[0][0], ref[0][1], ref[0][2])
+    y = host(out["y"])
+    np.testing.assert_allclose(y, 2688.0 * wdeq.T, rtol=1e-6)
+
+
+def _moe_case(orc, w, check_experts=None):
+    x, lg = D.activations(w), D.router_logits(w)
+    wgu, ref_gu = quant_weights_checked(orc, D.expert_weights(w, "gate_up"), w.E, 2 * w.I, w.H,
+                                        "bf16", check_experts)
+    wd, ref_d = quant_weights_checked(orc, D.expert_weights(w, "down"), w.E, w.H, w.I, "bf16",
+                                      check_experts)
+    return x, lg, wgu, ref_gu, wd, ref_d
+
+
+@pytest.mark.parametrize("T,E,k,H,I,routing", [(333, 6, 2, 256, 128, "zipf"),
+                                               (200, 16, 4, 384, 192, "normal")])
+def test_moe_chain_small(orc, T, E, k, H, I, routing):
+    say(f"moe chain T={T} E={E} k={k} H={H} I={I} {routing}")
+    w = D.small_moe(60 + T, T, E, k, H, I, routing=routing, n_empty=1 if routing == "zipf" else 0)
+    x, lg, wgu, ref_gu, wd, ref_d = _moe_case(orc, w)
+    out = P.moe_forward(to_dev(x, "bf16"), torch.from_numpy(lg).to(DEV), wgu, wd, k,
+                        w.n_select_x, w.n_select_h)
+    rt = orc.route(lg, k)
+    eq(host(out["route"].gather_rows), rt["gather"], "gather")
+    d = orc.quantize_rac(x, w.n_select_x)
+    eq(host(out["x_in"].qo.q.codes), d["codes"], "X codes")
+    eq(host(out["x_in"].rac.r.codes), d["res_codes"], "X residual codes")
+    rows = T * k
+    y_gu = orc.grouped_gemm(2 * I, H, rt["offsets"], rt["gather"],
+                            (d["codes"], d["scales"], d["s_t"]),
+                            (d["res_codes"], d["res_scales"], d["s_tr"]), w_stack(ref_gu, E))
+    h_ref, amax_ref = orc.silu_mul(y_gu, I)
+    h_gpu = host(out["h"].view(torch.int16)).view(np.uint16)
+    ok = bf16_ulp_ok(h_gpu, h_ref)
+    say(f"  H within 1 bf16 ulp: {ok.mean():.6f}, exact: {(h_gpu == h_ref).mean():.6f}")
+    assert ok.all()
+    amax_gpu = host(out["amax_h"])[0]
+    assert abs(amax_gpu - amax_ref) <= amax_ref * 2.0 ** -7
+    # down projection on the oracle's H (same bytes into both sides)
+    h_ref_f = D.bf16_to_f32(h_ref)
+    dh = orc.quantize_rac(h_ref_f, w.n_select_h)
+    h_in = P.quantize_input(to_dev(h_ref_f, "bf16"), w.n_select_h)
+    eq(host(h_in.qo.q.codes), dh["codes"], "H codes")
+    eq(host(h_in.rac.selected), dh["selected"], "H selected")
+    eq(host(h_in.rac.r.codes), dh["res_codes"], "H residual codes")
+    y_gpu = P.gemm(h_in, wd, out["route"].expert_offsets, rows)
+    y_ref = orc.grouped_gemm(H, I, rt["offsets"], None, (dh["codes"], dh["scales"], dh["s_t"]),
+                             (dh["res_codes"], dh["res_scales"], dh["s_tr"]), w_stack(ref_d, E))
+    err = rel_frob(host(y_gpu), y_ref)
+    say(f"  down rel frob {err:.3e}")
+    assert err <= REL_F
+    # whole GPU chain against the oracle chain (loose: H differs by <= 1 ulp)
+    err_chain = rel_frob(host(out["y"]), y_ref)
+    say(f"  chained layer rel frob {err_chain:.3e}")
+    assert err_chain <= 1e-2
+
+
+def test_moe_naive_mode_matches_main_sum(orc):
+    """RAC off on the GPU equals the oracle's naive W4A4 output (the main pass
+    alone)."""
+    say("moe naive mode")
+    w = D.small_moe(71, 150, 5, 2, 256, 128)
+    x, lg, wgu, ref_gu, wd, ref_d = _moe_case(orc, w)
+    rt = L.moe_route(torch.from_numpy(lg).to(DEV), 2)
+    x_in = P.quantize_input(to_dev(x, "bf16"), None)
+    y = P.gemm(x_in, wgu, rt.expert_offsets, 300, gather=rt.gather_rows)
+    r = orc.route(lg, 2)
+    c, s, t = orc.quantize(x)
+    y_ref = orc.grouped_gemm(256, 256, r["offsets"], r["gather"], (c, s, t), None,
+                             w_stack(ref_gu, 5))
+    assert rel_frob(host(y), y_ref) <= REL_F
