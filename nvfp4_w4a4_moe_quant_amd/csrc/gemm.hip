@@ -377,16 +377,18 @@ size_t w4a4_grouped_gemm_rac_workspace_size(const w4a4_gemm_args_t*) { return 0;
 
 int w4a4_grouped_gemm_rac(const w4a4_gemm_args_t* a, void*, size_t, void* stream) {
   NV_RETURN_IF(!a, NVFP4_ERR_NULL);
-  NV_RETURN_IF(!a->group_offsets || !a->a_codes || !a->a_scales || !a->a_tscale ||
-                   !a->w_codes || !a->w_scales || !a->w_tscale || !a->out,
-               NVFP4_ERR_NULL);
-  NV_RETURN_IF(a->r_codes && (!a->r_scales || !a->r_tscale), NVFP4_ERR_NULL);
   NV_RETURN_IF(a->epilogue != NVFP4_EPI_F32 && a->epilogue != NVFP4_EPI_SILU_MUL_BF16,
                NVFP4_ERR_DTYPE);
   NV_RETURN_IF(a->num_groups < 1 || a->total_rows < 0 || a->N <= 0 || a->K <= 0 ||
                    a->K % KC || a->N % 128 || a->N > (1 << 24) || a->K > (1 << 24) ||
                    a->total_rows > 0x7fffffff || a->num_groups > (1 << 20),
                NVFP4_ERR_SHAPE);
+  NV_RETURN_IF(!a->group_offsets || !a->w_codes || !a->w_scales || !a->w_tscale ||
+                   !a->a_tscale,
+               NVFP4_ERR_NULL);
+  if (a->total_rows == 0) return NVFP4_OK;  // nothing to compute; row buffers may be empty
+  NV_RETURN_IF(!a->a_codes || !a->a_scales || !a->out, NVFP4_ERR_NULL);
+  NV_RETURN_IF(a->r_codes && (!a->r_scales || !a->r_tscale), NVFP4_ERR_NULL);
   NV_RETURN_IF(!nv_aligned16(a->a_codes) || !nv_aligned16(a->w_codes) ||
                    (a->r_codes && !nv_aligned16(a->r_codes)) ||
                    (reinterpret_cast<uintptr_t>(a->a_scales) & 3) ||
@@ -415,7 +417,6 @@ int w4a4_grouped_gemm_rac(const w4a4_gemm_args_t* a, void*, size_t, void* stream
   p.out = a->out;
   p.out_amax = a->epilogue == NVFP4_EPI_SILU_MUL_BF16 ? a->out_amax : nullptr;
   p.silu = a->epilogue == NVFP4_EPI_SILU_MUL_BF16;
-  if (p.total_rows == 0) return NVFP4_OK;
   return launch<128, 128, 2, 2>(p, s);
 }
 

@@ -356,8 +356,9 @@ int64_t blocks_for(int64_t work, int64_t per_block, int64_t cap) {
   return b < cap ? b : cap;
 }
 
+// Per-row buffers may be NULL when rows == 0 (empty tensors have no storage).
 int check_x(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx) {
-  NV_RETURN_IF(!x, NVFP4_ERR_NULL);
+  NV_RETURN_IF(!x && rows > 0, NVFP4_ERR_NULL);
   NV_RETURN_IF(dtype != NVFP4_IN_F32 && dtype != NVFP4_IN_BF16, NVFP4_ERR_DTYPE);
   NV_RETURN_IF(rows < 0 || K <= 0 || (K & 15) || ldx < K, NVFP4_ERR_SHAPE);
   NV_RETURN_IF((ldx & 15) || !nv_aligned16(x), NVFP4_ERR_ALIGN);
@@ -391,7 +392,7 @@ int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ld
                    void* stream) {
   int st = check_x(x, dtype, rows, K, ldx);
   if (st) return st;
-  NV_RETURN_IF(!codes || !scales || !tensor_scale, NVFP4_ERR_NULL);
+  NV_RETURN_IF(!tensor_scale || (rows > 0 && (!codes || !scales)), NVFP4_ERR_NULL);
   NV_RETURN_IF((channel_score == nullptr) != (channel_max == nullptr), NVFP4_ERR_NULL);
   NV_RETURN_IF(!nv_aligned16(codes), NVFP4_ERR_ALIGN);
   NV_RETURN_IF(channel_score && ((reinterpret_cast<uintptr_t>(channel_score) & 7) ||
@@ -446,9 +447,10 @@ int rac_select_residual(const void* x, int dtype, int64_t rows, int64_t K, int64
                         void* stream) {
   int st = check_x(x, dtype, rows, K, ldx);
   if (st) return st;
-  NV_RETURN_IF(!codes || !scales || !tensor_scale || !channel_score || !channel_max ||
-                   !kblock_active || !res_codes || !res_scales || !res_tensor_scale,
+  NV_RETURN_IF(!tensor_scale || !channel_score || !channel_max || !kblock_active ||
+                   !res_tensor_scale,
                NVFP4_ERR_NULL);
+  NV_RETURN_IF(rows > 0 && (!codes || !scales || !res_codes || !res_scales), NVFP4_ERR_NULL);
   NV_RETURN_IF(n_select < 0 || n_select > K || K > kSelPer * kSelThreads, NVFP4_ERR_SHAPE);
   NV_RETURN_IF(n_select > 0 && !selected, NVFP4_ERR_NULL);
   NV_RETURN_IF(!nv_aligned16(codes) || !nv_aligned16(res_codes) ||

@@ -106,6 +106,7 @@ def test_gemm_validation(lib):
         return lib.w4a4_grouped_gemm_rac(ctypes.byref(a), None, 0, None)
     assert lib.w4a4_grouped_gemm_rac(None, None, 0, None) == ENULL
     assert call(out=None) == ENULL
+    assert call(out=None, total_rows=0) == OK       # empty problem: nothing enqueued
     assert call(r_codes=FAKE) == ENULL              # residual codes without scales
     assert call(epilogue=5) == EDTYPE
     assert call(K=200) == ESHAPE                    # K % 128

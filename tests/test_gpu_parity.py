@@ -8,8 +8,6 @@ order differs from the oracle's exact sums); SiLU*mul output within one bf16
 ulp (its exp() is not bit-defined across implementations).  The down
 projection of the MoE chain is checked on an H that comes from the oracle (or
 from the seeded generator), never from the GPU."""
-import sys
-
 import numpy as np
 import pytest
 import torch
@@ -19,73 +17,8 @@ from nvfp4_w4a4_moe_quant_amd import datagen as D
 from nvfp4_w4a4_moe_quant_amd import pipeline as P
 
 pytestmark = pytest.mark.gpu
-DEV = "cuda:0"
-REL_F = 1e-5
-
-
-def say(msg):
-    print(f"[case] {msg}", flush=True)
-    sys.stdout.flush()
-
-
-def to_dev(x, dtype):
-    x = np.ascontiguousarray(x, np.float32)
-    if dtype == "bf16":
-        return torch.from_numpy(D.bf16_bits(x).view(np.int16)).to(DEV).view(torch.bfloat16)
-    return torch.from_numpy(x).to(DEV)
-
-
-def host(t):
-    torch.cuda.synchronize()
-    return t.cpu().numpy()
-
-
-def eq(a, b, what):
-    a, b = np.asarray(a), np.asarray(b)
-    assert a.shape == b.shape, (what, a.shape, b.shape)
-    bad = np.flatnonzero(a.ravel() != b.ravel())
-    assert bad.size == 0, f"{what}: {bad.size} mismatches, first at {bad[:8]}: " \
-                          f"gpu {a.ravel()[bad[:8]]} oracle {b.ravel()[bad[:8]]}"
-
-
-def rel_frob(gpu, ref):
-    ref = np.asarray(ref, np.float64)
-    d = np.linalg.norm(np.asarray(gpu, np.float64) - ref)
-    n = np.linalg.norm(ref)
-    return d / n if n else d
-
-
-def bf16_ulp_ok(h_gpu_bits, h_ref_bits):
-    a = D.bf16_to_f32(np.asarray(h_gpu_bits, np.uint16)).astype(np.float64)
-    b = D.bf16_to_f32(np.asarray(h_ref_bits, np.uint16)).astype(np.float64)
-    ulp = np.maximum(np.abs(b), 2.0 ** -126) * 2.0 ** -7
-    return np.abs(a - b) <= ulp * 1.0001
-
-
-def check_quant_rac(orc, x, dtype, n_select, amax=None, ldx_pad=0):
-    """Quantize + RAC on the GPU and the oracle; everything bit-exact."""
-    rows, K = x.shape
-    if ldx_pad:
-        big = np.zeros((rows, K + ldx_pad), np.float32)
-        big[:, :K] = x
-        xd = to_dev(big, dtype)[:, :K]
-    else:
-        xd = to_dev(x, dtype)
-    am = None if amax is None else torch.tensor([amax], dtype=torch.float32, device=DEV)
-    qo = L.nvfp4_quantize(xd, amax_in=am, stats=True)
-    rac = L.rac_select_residual(xd, qo, n_select)
-    d = orc.quantize_rac(x, n_select, amax=amax)
-    eq(host(qo.q.tscale)[0], np.float32(d["s_t"]), "tensor scale")
-    eq(host(qo.q.scales), d["scales"], "block scales")
-    eq(host(qo.q.codes), d["codes"], "codes")
-    eq(host(qo.channel_score), d["score"], "channel score")
-    eq(host(qo.channel_max), d["chmax"], "channel max")
-    eq(host(rac.selected), d["selected"], "selected")
-    eq(host(rac.kblock_active), d["active"], "kblock_active")
-    eq(host(rac.r.tscale)[0], np.float32(d["s_tr"]), "residual tensor scale")
-    eq(host(rac.r.scales), d["res_scales"], "residual scales")
-    eq(host(rac.r.codes), d["res_codes"], "residual codes")
-    return qo, rac, d
+from gpu_util import (DEV, REL_F, bf16_ulp_ok, check_quant_rac, eq, host, rel_frob, say,
+                      to_dev)
 
 
 # ------------------------------------------------------------ quantizer
@@ -256,7 +189,7 @@ def _moe_case(orc, w, check_experts=None):
 
 
 @pytest.mark.parametrize("T,E,k,H,I,routing", [(333, 6, 2, 256, 128, "zipf"),
-                                               (200, 16, 4, 384, 192, "normal")])
+                                               (200, 16, 4, 384, 256, "normal")])
 def test_moe_chain_small(orc, T, E, k, H, I, routing):
     say(f"moe chain T={T} E={E} k={k} H={H} I={I} {routing}")
     w = D.small_moe(60 + T, T, E, k, H, I, routing=routing, n_empty=1 if routing == "zipf" else 0)
