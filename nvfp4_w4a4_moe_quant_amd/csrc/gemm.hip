@@ -38,12 +38,14 @@ constexpr int kThreads = 256;
 constexpr int KC = 128;            // k per chunk
 constexpr int CODE_ROW = KC / 2;   // 64 code bytes per row per chunk
 constexpr int SCALE_ROW = KC / 16; // 8 scale bytes per row per chunk
+constexpr int kMaxKChunks = 256;   // K <= 32768
 
 __device__ __forceinline__ uint32_t swz(uint32_t i) { return ((i >> 1) ^ (i >> 3)) & 3u; }
 
-// 8 E2M1 codes (one dword) times one E4M3 scale -> 8 exact fp16 values.
-__device__ __forceinline__ half8 dequant8(uint32_t codes, _Float16 sb) {
-  const half2v s2 = {sb, sb};
+// 8 E2M1 codes (one dword) times one E4M3 scale (as an fp16 pair) -> 8 exact
+// fp16 values.  The hardware FP4 conversion only applies the exponent of its
+// scale operand, so it runs with scale 1 and the packed multiply applies s_b.
+__device__ __forceinline__ half8 dequant8(uint32_t codes, half2v s2) {
   half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0);
   half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1);
   half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2);
@@ -52,15 +54,25 @@ __device__ __forceinline__ half8 dequant8(uint32_t codes, _Float16 sb) {
   p1 *= s2;
   p2 *= s2;
   p3 *= s2;
-  half8 r;
-  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
+  return __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
+                                 __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4,
+                                 5, 6, 7);
 }
 
-__device__ __forceinline__ _Float16 scale_f16(uint32_t byte) {
-  return (_Float16)nv_e4m3_to_f32(byte);  // exact: E4M3 values are fp16 values
+// Four E4M3 scale bytes -> four exact fp16 values (OCP E4M3 conversion, scale 1).
+__device__ __forceinline__ void scales4(uint32_t w, half2v& s01, half2v& s23) {
+  s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
 }
+
+__device__ __forceinline__ half2v pick_scale(half2v s01, half2v s23, int blk) {
+  return blk == 0 ? __builtin_shufflevector(s01, s01, 0, 0)
+       : blk == 1 ? __builtin_shufflevector(s01, s01, 1, 1)
+       : blk == 2 ? __builtin_shufflevector(s23, s23, 0, 0)
+                  : __builtin_shufflevector(s23, s23, 1, 1);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 struct GemmParams {
   int G, N, K, total_rows;
@@ -75,23 +87,26 @@ struct GemmParams {
   const float* w_ts;
   void* out;
   float* out_amax;
-  int silu;
   int m_slots;  // m-tile slots in the grid
   int n_tiles;
 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool RAC, bool SILU, bool GATHER>
 __global__ __launch_bounds__(kThreads) void k_gemm(GemmParams p) {
   static_assert(WAVES_M * WAVES_N == 4, "4 waves");
   constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "tile");
-  constexpr int ROWS = 2 * BM + BN;  // A rows, R rows, W rows
-  constexpr int NP = (ROWS * 4 + kThreads - 1) / kThreads;  // 16B code pieces per thread
-  constexpr int NS = (ROWS * 2 + kThreads - 1) / kThreads;  // scale dwords per thread
+  static_assert(!SILU || FN % 2 == 0, "SiLU pairs gate/up fragments");
+  constexpr int AR = RAC ? 2 * BM : BM;  // A rows then R rows
+  constexpr int ROWS = AR + BN;          // then W rows
+  static_assert(ROWS % 128 == 0, "whole wave-loads of codes and scales");
+  constexpr int NPI = ROWS * 4 / kThreads;  // 16-byte code pieces per thread per chunk
+  constexpr int NSI = ROWS * 2 / kThreads;  // 4-byte scale words per thread per chunk
   constexpr int STAGE_CODES = ROWS * CODE_ROW;
   constexpr int STAGE = STAGE_CODES + ROWS * SCALE_ROW;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
+  __shared__ uint64_t kact_lds[kMaxKChunks];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -104,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmParams p) {
   const int L = xcd * per + (xcd < rem ? xcd : rem) + bid / 8;
   const int mt = L / p.n_tiles, nt = L % p.n_tiles;
 
-  // ---- find the group that owns m-tile `mt`
+  // ---- find the group that owns m-tile `mt` (a wave scan of per-group tiles)
   int grp = -1, local = 0;
   {
     int run = 0;
@@ -133,19 +148,18 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmParams p) {
   if (grp < 0) return;  // wave-uniform and identical in every wave
   const int row_beg = p.offsets[grp] + local * BM;
   const int row_end = p.offsets[grp + 1];
-  const bool rac = p.r_codes != nullptr;
   const int K2 = p.K >> 1, K16 = p.K >> 4;
   const int I = p.N >> 1;
 
-  // ---- per-thread load assignments (pointers advance by one chunk per step)
-  auto src_row = [&](int i) -> int64_t {
+  // ---- source rows of the LDS tile rows
+  auto src_row = [&](int i) -> int64_t {  // i in [0, BM)
     int m = row_beg + i;
     if (m >= row_end) m = row_end - 1;
-    return p.gather ? (int64_t)p.gather[m] : (int64_t)m;
+    return GATHER ? (int64_t)p.gather[m] : (int64_t)m;
   };
-  auto w_row = [&](int i) -> int64_t {
+  auto w_row = [&](int i) -> int64_t {  // i in [0, BN)
     int n;
-    if (p.silu) {
+    if constexpr (SILU) {
       const int wv = i / WTN, f = (i % WTN) / 32, rr = i % 32;
       n = ((f & 1) ? I : 0) + nt * (BN / 2) + wv * (WTN / 2) + (f >> 1) * 32 + rr;
     } else {
@@ -153,109 +167,115 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmParams p) {
     }
     return (int64_t)grp * p.N + n;
   };
-  const uint8_t* cptr[NP];
-  uint32_t cdst[NP];
-  const uint8_t* sptr[NS];
-  uint32_t sdst[NS];
-#pragma unroll
-  for (int j = 0; j < NP; ++j) {
-    const int q = tid + kThreads * j;
-    const int i = q >> 2, pc = q & 3;
-    cptr[j] = nullptr;
-    cdst[j] = 0;
-    if (i < ROWS) {
-      if (i < BM) cptr[j] = p.a_codes + src_row(i) * K2 + pc * 16;
-      else if (i < 2 * BM) cptr[j] = rac ? p.r_codes + src_row(i - BM) * K2 + pc * 16 : nullptr;
-      else cptr[j] = p.w_codes + w_row(i - 2 * BM) * K2 + pc * 16;
-      cdst[j] = i * CODE_ROW + ((pc ^ swz(i)) << 4);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    const int q = tid + kThreads * j;
-    const int i = q >> 1, d = q & 1;
-    sptr[j] = nullptr;
-    sdst[j] = 0;
-    if (i < ROWS) {
-      if (i < BM) sptr[j] = p.a_scales + src_row(i) * K16 + d * 4;
-      else if (i < 2 * BM) sptr[j] = rac ? p.r_scales + src_row(i - BM) * K16 + d * 4 : nullptr;
-      else sptr[j] = p.w_scales + w_row(i - 2 * BM) * K16 + d * 4;
-      sdst[j] = STAGE_CODES + i * SCALE_ROW + d * 4;
-    }
-  }
-
-  uint4 creg[NP];
-  uint32_t sreg[NS];
-  auto gload = [&](int chunk) {
-#pragma unroll
-    for (int j = 0; j < NP; ++j)
-      if (cptr[j]) creg[j] = *reinterpret_cast<const uint4*>(cptr[j] + (int64_t)chunk * CODE_ROW);
-#pragma unroll
-    for (int j = 0; j < NS; ++j)
-      if (sptr[j]) sreg[j] = *reinterpret_cast<const uint32_t*>(sptr[j] + (int64_t)chunk * SCALE_ROW);
+  auto code_row_ptr = [&](int i) -> const uint8_t* {
+    if (i < BM) return p.a_codes + src_row(i) * K2;
+    if (RAC && i < AR) return p.r_codes + src_row(i - BM) * K2;
+    return p.w_codes + w_row(i - AR) * K2;
   };
-  auto lstore = [&](int buf) {
-    uint8_t* base = lds + buf * STAGE;
-#pragma unroll
-    for (int j = 0; j < NP; ++j)
-      if (cptr[j]) *reinterpret_cast<uint4*>(base + cdst[j]) = creg[j];
-#pragma unroll
-    for (int j = 0; j < NS; ++j)
-      if (sptr[j]) *reinterpret_cast<uint32_t*>(base + sdst[j]) = sreg[j];
+  auto scale_row_ptr = [&](int i) -> const uint8_t* {
+    if (i < BM) return p.a_scales + src_row(i) * K16;
+    if (RAC && i < AR) return p.r_scales + src_row(i - BM) * K16;
+    return p.w_scales + w_row(i - AR) * K16;
   };
 
-  float16v accm[FM][FN], accr[FM][FN];
+  // Direct global->LDS loads: wave-instruction j writes 1 KiB of codes
+  // (16 rows x 64 B) or 256 B of scales (32 rows x 8 B) contiguously; lane l
+  // fetches the 16-byte piece that the swizzle places in its slot.
+  const uint8_t* gcode[NPI];
+  const uint8_t* gscale[NSI];
+#pragma unroll
+  for (int j = 0; j < NPI; ++j) {
+    const int slot = (j * 4 + wave) * 64 + lane;
+    const int row = slot >> 2;
+    const uint32_t piece = (uint32_t)(slot & 3) ^ swz((uint32_t)row);
+    gcode[j] = code_row_ptr(row) + piece * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < NSI; ++j) {
+    const int slot = (j * 4 + wave) * 64 + lane;
+    gscale[j] = scale_row_ptr(slot >> 1) + (slot & 1) * 4;
+  }
+  // The DMA is issued through inline asm: the compiler cannot tell that the
+  // next stage never aliases the stage being read and would otherwise wait for
+  // the DMA before every LDS read.  Completion is awaited explicitly (vmcnt)
+  // before the barrier that publishes a stage.
+  auto issue = [&](int chunk, int buf) {
+    const uint32_t st = (uint32_t)(uintptr_t)(lds_ptr_t)(lds + buf * STAGE);
+#pragma unroll
+    for (int j = 0; j < NPI; ++j) {
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(st + (j * 4 + wave) * 1024);
+      const uint8_t* g = gcode[j] + (int64_t)chunk * CODE_ROW;
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                   :: "s"(m0), "v"(g) : "memory", "m0");
+    }
+#pragma unroll
+    for (int j = 0; j < NSI; ++j) {
+      const uint32_t m0 =
+          __builtin_amdgcn_readfirstlane(st + STAGE_CODES + (j * 4 + wave) * 256);
+      const uint8_t* g = gscale[j] + (int64_t)chunk * SCALE_ROW;
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                   :: "s"(m0), "v"(g) : "memory", "m0");
+    }
+  };
+
+  float16v accm[FM][FN], accr[RAC ? FM : 1][RAC ? FN : 1];
 #pragma unroll
   for (int a = 0; a < FM; ++a)
 #pragma unroll
-    for (int b = 0; b < FN; ++b) {
+    for (int b = 0; b < FN; ++b)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        accm[a][b][e] = 0.0f;
-        accr[a][b][e] = 0.0f;
-      }
-    }
+      for (int e = 0; e < 16; ++e) accm[a][b][e] = 0.0f;
+  if constexpr (RAC) {
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+      for (int b = 0; b < FN; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) accr[a][b][e] = 0.0f;
+  }
 
-  // fragment rows in the LDS tile
-  const int arow0 = wm * WTM + lr;            // + fm*32
-  const int wrow0 = 2 * BM + wn * WTN + lr;   // + fn*32
+  const int arow0 = wm * WTM + lr;       // + a*32 (A), + BM (R)
+  const int wrow0 = AR + wn * WTN + lr;  // + b*32
 
   const int nchunks = p.K / KC;
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  // residual block activity, 8 blocks (one chunk) per 64-bit word
+  if constexpr (RAC) {
+    for (int c = tid; c < nchunks; c += kThreads)
+      kact_lds[c] = p.kact ? *reinterpret_cast<const uint64_t*>(p.kact + (int64_t)c * 8) : ~0ull;
+  }
 
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int buf = ch & 1;
-    if (ch + 1 < nchunks) gload(ch + 1);
-    const uint8_t* base = lds + buf * STAGE;
-
-    // residual activity of the 8 blocks of this chunk
+  auto compute = [&](int ch, const uint8_t* base) {
     uint64_t act = ~0ull;
-    if (rac && p.kact) act = *reinterpret_cast<const uint64_t*>(p.kact + (int64_t)ch * 8);
+    if constexpr (RAC) act = kact_lds[ch];
 
-    uint32_t sa[FM], sr[FM], sw[FN];
+    // scales of the lane's 4 blocks for every fragment row
+    half2v sa01[FM], sa23[FM], sr01[RAC ? FM : 1], sr23[RAC ? FM : 1], sw01[FN], sw23[FN];
 #pragma unroll
     for (int a = 0; a < FM; ++a) {
       const int i = arow0 + a * 32;
-      sa[a] = *reinterpret_cast<const uint32_t*>(base + STAGE_CODES + i * SCALE_ROW + lh * 4);
-      if (rac) sr[a] = *reinterpret_cast<const uint32_t*>(base + STAGE_CODES + (i + BM) * SCALE_ROW + lh * 4);
+      scales4(*reinterpret_cast<const uint32_t*>(base + STAGE_CODES + i * SCALE_ROW + lh * 4),
+              sa01[a], sa23[a]);
+      if constexpr (RAC)
+        scales4(*reinterpret_cast<const uint32_t*>(base + STAGE_CODES + (i + BM) * SCALE_ROW +
+                                                   lh * 4),
+                sr01[a], sr23[a]);
     }
 #pragma unroll
     for (int b = 0; b < FN; ++b) {
       const int i = wrow0 + b * 32;
-      sw[b] = *reinterpret_cast<const uint32_t*>(base + STAGE_CODES + i * SCALE_ROW + lh * 4);
+      scales4(*reinterpret_cast<const uint32_t*>(base + STAGE_CODES + i * SCALE_ROW + lh * 4),
+              sw01[b], sw23[b]);
     }
 
 #pragma unroll
     for (int hp = 0; hp < 2; ++hp) {
       const uint32_t pc = 2 * lh + hp;
-      uint4 ca[FM], cr[FM], cw[FN];
+      uint4 ca[FM], cr[RAC ? FM : 1], cw[FN];
 #pragma unroll
       for (int a = 0; a < FM; ++a) {
         const uint32_t i = arow0 + a * 32;
         ca[a] = *reinterpret_cast<const uint4*>(base + i * CODE_ROW + ((pc ^ swz(i)) << 4));
-        if (rac) {
+        if constexpr (RAC) {
           const uint32_t ir = i + BM;
           cr[a] = *reinterpret_cast<const uint4*>(base + ir * CODE_ROW + ((pc ^ swz(ir)) << 4));
         }
@@ -267,50 +287,67 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmParams p) {
       }
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
-        const int s = hp * 4 + s4;        // MFMA step in the chunk
-        const int sbyte = s >> 1;         // scale byte within the lane's dword
+        const int s = hp * 4 + s4;  // MFMA step in the chunk
+        const int blk = s >> 1;     // block among the lane's four
         half8 av[FM], wv[FN];
 #pragma unroll
         for (int b = 0; b < FN; ++b) {
           const uint32_t c = s4 == 0 ? cw[b].x : s4 == 1 ? cw[b].y : s4 == 2 ? cw[b].z : cw[b].w;
-          wv[b] = dequant8(c, scale_f16((sw[b] >> (8 * sbyte)) & 0xFFu));
+          wv[b] = dequant8(c, pick_scale(sw01[b], sw23[b], blk));
         }
 #pragma unroll
         for (int a = 0; a < FM; ++a) {
           const uint32_t c = s4 == 0 ? ca[a].x : s4 == 1 ? ca[a].y : s4 == 2 ? ca[a].z : ca[a].w;
-          av[a] = dequant8(c, scale_f16((sa[a] >> (8 * sbyte)) & 0xFFu));
+          av[a] = dequant8(c, pick_scale(sa01[a], sa23[a], blk));
         }
 #pragma unroll
         for (int a = 0; a < FM; ++a)
 #pragma unroll
           for (int b = 0; b < FN; ++b)
             accm[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[a], wv[b], accm[a][b], 0, 0, 0);
-        // blocks s/2 (lanes 0-31) and 4 + s/2 (lanes 32-63) of the chunk
-        const bool ract = rac && (((act >> (8 * sbyte)) & 0xFFull) | ((act >> (8 * (4 + sbyte))) & 0xFFull));
-        if (ract) {
-          half8 rv[FM];
+        if constexpr (RAC) {
+          // blocks blk (lanes 0-31) and 4 + blk (lanes 32-63) of the chunk
+          if (((act >> (8 * blk)) & 0xFFull) | ((act >> (8 * (4 + blk))) & 0xFFull)) {
+            half8 rv[FM];
 #pragma unroll
-          for (int a = 0; a < FM; ++a) {
-            const uint32_t c = s4 == 0 ? cr[a].x : s4 == 1 ? cr[a].y : s4 == 2 ? cr[a].z : cr[a].w;
-            rv[a] = dequant8(c, scale_f16((sr[a] >> (8 * sbyte)) & 0xFFu));
+            for (int a = 0; a < FM; ++a) {
+              const uint32_t c =
+                  s4 == 0 ? cr[a].x : s4 == 1 ? cr[a].y : s4 == 2 ? cr[a].z : cr[a].w;
+              rv[a] = dequant8(c, pick_scale(sr01[a], sr23[a], blk));
+            }
+#pragma unroll
+            for (int a = 0; a < FM; ++a)
+#pragma unroll
+              for (int b = 0; b < FN; ++b)
+                accr[a][b] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_f16(rv[a], wv[b], accr[a][b], 0, 0, 0);
           }
-#pragma unroll
-          for (int a = 0; a < FM; ++a)
-#pragma unroll
-            for (int b = 0; b < FN; ++b)
-              accr[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rv[a], wv[b], accr[a][b], 0, 0, 0);
         }
       }
     }
-    if (ch + 1 < nchunks) lstore(buf ^ 1);
+  };
+
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int buf = ch & 1;
+    if (ch + 1 < nchunks) issue(ch + 1, buf ^ 1);
+    compute(ch, lds + buf * STAGE);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
   // ---- epilogue
   const float s_ta = *p.a_ts;
-  const float s_tr = rac ? *p.r_ts : 0.0f;
+  const float s_tr = RAC ? *p.r_ts : 0.0f;
   const float s_tw = p.w_ts[grp];
-  if (!p.silu) {
+  auto yval = [&](int a, int b, int e) -> float {
+    float y = s_ta * accm[a][b][e];
+    if constexpr (RAC) y = y + s_tr * accr[a][b][e];
+    return s_tw * y;
+  };
+  if constexpr (!SILU) {
     float* out = reinterpret_cast<float*>(p.out);
 #pragma unroll
     for (int a = 0; a < FM; ++a)
@@ -320,11 +357,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmParams p) {
         for (int e = 0; e < 16; ++e) {
           const int m = row_beg + wm * WTM + a * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
           const int n = nt * BN + wn * WTN + b * 32 + lr;
-          if (m < row_end) {
-            float y = s_ta * accm[a][b][e];
-            if (rac) y = y + s_tr * accr[a][b][e];
-            out[(int64_t)m * p.N + n] = s_tw * y;
-          }
+          if (m < row_end) out[(int64_t)m * p.N + n] = yval(a, b, e);
         }
   } else {
     uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
@@ -338,13 +371,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmParams p) {
           const int m = row_beg + wm * WTM + a * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
           const int hc = nt * (BN / 2) + wn * (WTN / 2) + (b >> 1) * 32 + lr;
           if (m < row_end) {
-            float g = s_ta * accm[a][b][e], u = s_ta * accm[a][b + 1][e];
-            if (rac) {
-              g = g + s_tr * accr[a][b][e];
-              u = u + s_tr * accr[a][b + 1][e];
-            }
-            g *= s_tw;
-            u *= s_tw;
+            const float g = yval(a, b, e), u = yval(a, b + 1, e);
             const float hv = g / (1.0f + expf(-g)) * u;
             const uint32_t hb = nv_f32_to_bf16(hv);
             out[(int64_t)m * I + hc] = (uint16_t)hb;
@@ -359,14 +386,29 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmParams p) {
   }
 }
 
-template <int BM, int BN, int WM, int WN>
-int launch(GemmParams& p, hipStream_t s) {
+template <int BM, int BN, int WM, int WN, bool RAC, bool SILU, bool GATHER>
+int launch_t(GemmParams& p, hipStream_t s) {
   p.m_slots = (p.total_rows + BM - 1) / BM + p.G;
   p.n_tiles = p.N / BN;
   const int64_t nb = (int64_t)p.m_slots * p.n_tiles;
   if (nb > 0x7fffffff) return NVFP4_ERR_SHAPE;
-  hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN>), dim3((unsigned)nb), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, RAC, SILU, GATHER>), dim3((unsigned)nb),
+                     dim3(kThreads), 0, s, p);
   return nv_launch_status();
+}
+
+template <bool RAC, bool SILU, bool GATHER>
+int launch_cfg(GemmParams& p, hipStream_t s) {
+  return launch_t<128, 128, 2, 2, RAC, SILU, GATHER>(p, s);
+}
+
+int launch(GemmParams& p, bool rac, bool silu, bool gather, hipStream_t s) {
+  if (rac) {
+    if (silu) return gather ? launch_cfg<true, true, true>(p, s) : launch_cfg<true, true, false>(p, s);
+    return gather ? launch_cfg<true, false, true>(p, s) : launch_cfg<true, false, false>(p, s);
+  }
+  if (silu) return gather ? launch_cfg<false, true, true>(p, s) : launch_cfg<false, true, false>(p, s);
+  return gather ? launch_cfg<false, false, true>(p, s) : launch_cfg<false, false, false>(p, s);
 }
 
 }  // namespace
@@ -381,7 +423,8 @@ int w4a4_grouped_gemm_rac(const w4a4_gemm_args_t* a, void*, size_t, void* stream
                NVFP4_ERR_DTYPE);
   NV_RETURN_IF(a->num_groups < 1 || a->total_rows < 0 || a->N <= 0 || a->K <= 0 ||
                    a->K % KC || a->N % 128 || a->N > (1 << 24) || a->K > (1 << 24) ||
-                   a->total_rows > 0x7fffffff || a->num_groups > (1 << 20),
+                   a->total_rows > 0x7fffffff || a->num_groups > (1 << 20) ||
+                   a->K > KC * kMaxKChunks,
                NVFP4_ERR_SHAPE);
   NV_RETURN_IF(!a->group_offsets || !a->w_codes || !a->w_scales || !a->w_tscale ||
                    !a->a_tscale,
@@ -416,8 +459,8 @@ int w4a4_grouped_gemm_rac(const w4a4_gemm_args_t* a, void*, size_t, void* stream
   p.w_ts = a->w_tscale;
   p.out = a->out;
   p.out_amax = a->epilogue == NVFP4_EPI_SILU_MUL_BF16 ? a->out_amax : nullptr;
-  p.silu = a->epilogue == NVFP4_EPI_SILU_MUL_BF16;
-  return launch<128, 128, 2, 2>(p, s);
+  return launch(p, a->r_codes != nullptr, a->epilogue == NVFP4_EPI_SILU_MUL_BF16,
+                a->gather_rows != nullptr, s);
 }
 
 }  // extern "C"
