@@ -26,6 +26,8 @@
 //    rows) run on the same XCD and share its L2.
 //  * Double-buffered LDS; 16-byte code pieces are XOR-swizzled per row so that
 //    the fragment reads of 8 (or 16) consecutive rows hit distinct banks.
+#include <stdlib.h>
+
 #include "common.h"
 
 namespace {
@@ -91,8 +93,9 @@ struct GemmParams {
   int n_tiles;
 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool RAC, bool SILU, bool GATHER>
-__global__ __launch_bounds__(kThreads) void k_gemm(GemmParams p) {
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int MINW, bool RAC, bool SILU,
+          bool GATHER>
+__global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
   static_assert(WAVES_M * WAVES_N == 4, "4 waves");
   constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -105,7 +108,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmParams p) {
   constexpr int NSI = ROWS * 2 / kThreads;  // 4-byte scale words per thread per chunk
   constexpr int STAGE_CODES = ROWS * CODE_ROW;
   constexpr int STAGE = STAGE_CODES + ROWS * SCALE_ROW;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
+  static_assert(NSTAGE >= 2 && (NSTAGE - 2) * (NPI + NSI) <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * STAGE];
   __shared__ uint64_t kact_lds[kMaxKChunks];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -327,15 +331,29 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmParams p) {
     }
   };
 
-  issue(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int buf = ch & 1;
-    if (ch + 1 < nchunks) issue(ch + 1, buf ^ 1);
-    compute(ch, lds + buf * STAGE);
+  // NSTAGE-deep pipeline: chunk ch + NSTAGE - 1 is in flight while chunk ch
+  // is computed; before the barrier that ends iteration ch, chunk ch + 1 must
+  // have landed, i.e. at most the DMA of the later chunks may be outstanding.
+  constexpr int PER_CHUNK = NPI + NSI;
+#pragma unroll
+  for (int c = 0; c < NSTAGE - 1; ++c)
+    if (c < nchunks) issue(c, c);
+  if (nchunks > 1 && NSTAGE > 2)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NSTAGE - 2) * PER_CHUNK) : "memory");
+  else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int buf = 0;
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int nxt = ch + NSTAGE - 1;
+    if (nxt < nchunks) issue(nxt, nxt % NSTAGE);
+    compute(ch, lds + buf * STAGE);
+    if (nxt < nchunks && NSTAGE > 2)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NSTAGE - 2) * PER_CHUNK) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    buf = buf + 1 == NSTAGE ? 0 : buf + 1;
   }
 
   // ---- epilogue
@@ -386,20 +404,40 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmParams p) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool RAC, bool SILU, bool GATHER>
+template <int BM, int BN, int WM, int WN, int NS, int MINW, bool RAC, bool SILU, bool GATHER>
 int launch_t(GemmParams& p, hipStream_t s) {
-  p.m_slots = (p.total_rows + BM - 1) / BM + p.G;
-  p.n_tiles = p.N / BN;
-  const int64_t nb = (int64_t)p.m_slots * p.n_tiles;
-  if (nb > 0x7fffffff) return NVFP4_ERR_SHAPE;
-  hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, RAC, SILU, GATHER>), dim3((unsigned)nb),
-                     dim3(kThreads), 0, s, p);
-  return nv_launch_status();
+  constexpr int rows = (RAC ? 2 * BM : BM) + BN;
+  if constexpr (rows % 128 != 0) {
+    return launch_t<128, 128, 2, 2, 2, 1, RAC, SILU, GATHER>(p, s);
+  } else {
+    if (p.N % BN) return NVFP4_ERR_SHAPE;
+    p.m_slots = (p.total_rows + BM - 1) / BM + p.G;
+    p.n_tiles = p.N / BN;
+    const int64_t nb = (int64_t)p.m_slots * p.n_tiles;
+    if (nb > 0x7fffffff) return NVFP4_ERR_SHAPE;
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, NS, MINW, RAC, SILU, GATHER>), dim3((unsigned)nb),
+                       dim3(kThreads), 0, s, p);
+    return nv_launch_status();
+  }
 }
 
+// Tile configurations (rows x cols per workgroup, waves, LDS stages, min waves
+// per SIMD).  NVFP4RAC_GEMM_CFG selects one for tuning runs.
 template <bool RAC, bool SILU, bool GATHER>
 int launch_cfg(GemmParams& p, hipStream_t s) {
-  return launch_t<128, 128, 2, 2, RAC, SILU, GATHER>(p, s);
+  static const int cfg = [] {
+    const char* e = getenv("NVFP4RAC_GEMM_CFG");
+    return e ? atoi(e) : 0;
+  }();
+  switch (cfg) {
+    case 1: return launch_t<128, 128, 2, 2, 3, 1, RAC, SILU, GATHER>(p, s);
+    case 2: return launch_t<128, 128, 2, 2, 2, 1, RAC, SILU, GATHER>(p, s);
+    case 3: return launch_t<128, 128, 2, 2, 4, 1, RAC, SILU, GATHER>(p, s);
+    case 4: return launch_t<64, 256, 1, 4, 3, 1, RAC, SILU, GATHER>(p, s);
+    case 5: return launch_t<128, 256, 2, 2, 3, 1, RAC, SILU, GATHER>(p, s);
+    case 6: return launch_t<128, 128, 2, 2, 3, 2, RAC, SILU, GATHER>(p, s);
+    default: return launch_t<128, 128, 2, 2, 2, 2, RAC, SILU, GATHER>(p, s);
+  }
 }
 
 int launch(GemmParams& p, bool rac, bool silu, bool gather, hipStream_t s) {
