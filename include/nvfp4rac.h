@@ -164,8 +164,11 @@ int moe_route(const float* logits, int64_t T, int64_t E, int64_t k,
  *                       + s_tr * sum_{k in active blocks} R[src,k] W_g[n,k] )
  * with A, R, W the exact dequantized values g * s_b (FP32 accumulation).
  * r_codes == NULL turns RAC off (naive W4A4).  kblock_active == NULL means
- * every block is active; skipping an inactive block is exact because its
- * residual is zero.
+ * every block is active.  With NVFP4_GEMM_SKIP_INACTIVE_BLOCKS in `flags`, the
+ * residual MFMAs of each 32-k step run only if one of its two 16-blocks is
+ * active; without it the residual pass runs over every block.  Both are exact
+ * (an inactive block's residual codes are zero); the flag pays off when the
+ * selection leaves many blocks inactive, and costs a few percent otherwise.
  * Epilogue F32 writes y.  Epilogue SILU_MUL_BF16 treats W as the fused
  * gate/up weight [N = 2I, K] with the gate in rows [0, I) and writes
  * h[j, i] = bf16(silu(y[j, i]) * y[j, I + i]) to out [total_rows, I] and, if
@@ -194,7 +197,10 @@ typedef struct {
   int64_t epilogue;             /* nvfp4_epilogue_t */
   void* out;                    /* float [total_rows, N] or bf16 [total_rows, N/2] */
   float* out_amax;              /* SILU_MUL only, nullable, caller-initialized */
+  int64_t flags;                /* NVFP4_GEMM_* bits */
 } w4a4_gemm_args_t;
+
+#define NVFP4_GEMM_SKIP_INACTIVE_BLOCKS 1
 
 size_t w4a4_grouped_gemm_rac_workspace_size(const w4a4_gemm_args_t* args);
 int w4a4_grouped_gemm_rac(const w4a4_gemm_args_t* args, void* ws, size_t ws_bytes,

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4rac.so")
 
 NVFP4_IN_F32, NVFP4_IN_BF16 = 0, 1
 NVFP4_EPI_F32, NVFP4_EPI_SILU_MUL_BF16 = 0, 1
+NVFP4_GEMM_SKIP_INACTIVE_BLOCKS = 1
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -34,7 +35,7 @@ class GemmArgs(ctypes.Structure):
         ("r_codes", _P), ("r_scales", _P), ("r_tscale", _P),
         ("kblock_active", _P),
         ("w_codes", _P), ("w_scales", _P), ("w_tscale", _P),
-        ("epilogue", _I64), ("out", _P), ("out_amax", _P),
+        ("epilogue", _I64), ("out", _P), ("out_amax", _P), ("flags", _I64),
     ]
 
 
@@ -193,7 +194,8 @@ def w4a4_grouped_gemm_rac(a: NVFP4, w: NVFP4, group_offsets: torch.Tensor, *, N:
                           kblock_active: Optional[torch.Tensor] = None,
                           epilogue: int = NVFP4_EPI_F32,
                           out: Optional[torch.Tensor] = None,
-                          out_amax: Optional[torch.Tensor] = None) -> torch.Tensor:
+                          out_amax: Optional[torch.Tensor] = None,
+                          skip_inactive: bool = False) -> torch.Tensor:
     """w: codes [G, N, K/2], scales [G, N, K/16], tscale [G]."""
     dev = a.codes.device
     G = group_offsets.numel() - 1
@@ -209,7 +211,8 @@ def w4a4_grouped_gemm_rac(a: NVFP4, w: NVFP4, group_offsets: torch.Tensor, *, N:
         r_codes=_ptr(r.codes if r else None), r_scales=_ptr(r.scales if r else None),
         r_tscale=_ptr(r.tscale if r else None), kblock_active=_ptr(kblock_active),
         w_codes=_ptr(w.codes), w_scales=_ptr(w.scales), w_tscale=_ptr(w.tscale),
-        epilogue=epilogue, out=_ptr(out), out_amax=_ptr(out_amax))
+        epilogue=epilogue, out=_ptr(out), out_amax=_ptr(out_amax),
+        flags=NVFP4_GEMM_SKIP_INACTIVE_BLOCKS if skip_inactive else 0)
     L = lib()
     nbytes = L.w4a4_grouped_gemm_rac_workspace_size(ctypes.byref(args))
     ws = _ws(nbytes, dev) if nbytes else None

@@ -49,6 +49,13 @@ def quantize_weights(mats: Iterable[Tuple[int, torch.Tensor]], G: int, N: int, K
 class GemmInput(NamedTuple):
     qo: L.QuantOut
     rac: Optional[L.RacOut]
+    skip_inactive: bool = False
+
+
+# Below this selected fraction of channels, many 16-blocks are likely to hold
+# no selected channel, and the GEMM skips their residual MFMAs; above it the
+# branch-free residual pass is faster (an inactive block's residual is zero).
+SKIP_BELOW_FRACTION = 1.0 / 8
 
 
 def quantize_input(x: torch.Tensor, n_select: Optional[int],
@@ -56,7 +63,8 @@ def quantize_input(x: torch.Tensor, n_select: Optional[int],
     """Online quantization of a GEMM input; n_select None turns RAC off."""
     qo = L.nvfp4_quantize(x, amax_in=amax_in, stats=n_select is not None)
     rac = L.rac_select_residual(x, qo, n_select) if n_select is not None else None
-    return GemmInput(qo, rac)
+    skip = n_select is not None and n_select <= SKIP_BELOW_FRACTION * x.shape[1]
+    return GemmInput(qo, rac, skip)
 
 
 def gemm(inp: GemmInput, wq: QuantWeights, offsets: torch.Tensor, total_rows: int, *,
@@ -66,7 +74,7 @@ def gemm(inp: GemmInput, wq: QuantWeights, offsets: torch.Tensor, total_rows: in
         inp.qo.q, wq.w, offsets, N=wq.N, K=wq.K, total_rows=total_rows, gather_rows=gather,
         r=inp.rac.r if inp.rac else None,
         kblock_active=inp.rac.kblock_active if inp.rac else None,
-        epilogue=epilogue, out_amax=out_amax)
+        epilogue=epilogue, out_amax=out_amax, skip_inactive=inp.skip_inactive)
 
 
 def dense_forward(x: torch.Tensor, wq: QuantWeights, n_select: Optional[int]) -> Dict:

@@ -245,3 +245,38 @@ def test_moe_naive_mode_matches_main_sum(orc):
     y_ref = orc.grouped_gemm(256, 256, r["offsets"], r["gather"], (c, s, t), None,
                              w_stack(ref_gu, 5))
     assert rel_frob(host(y), y_ref) <= REL_F
+
+
+@pytest.mark.parametrize("n_select", [16, 40])
+def test_residual_skip_with_inactive_blocks(orc, n_select):
+    """A sparse selection leaves most 16-blocks inactive: the step-skipping
+    GEMM (NVFP4_GEMM_SKIP_INACTIVE_BLOCKS) and the branch-free residual pass
+    both match the oracle, and each other."""
+    say(f"residual skip, n_select={n_select}")
+    rows, K, N = 150, 512, 256
+    w = D.small_dense(81, rows, K, N, n_outliers=0)
+    x = D.activations(w)
+    x[:, 64:80] *= 30.0                      # errors concentrated in two blocks
+    x[:, 200:216] *= 25.0
+    x = D.bf16_to_f32(D.bf16_bits(x))
+    W = D.dense_weight(w)
+    wq, ref = quant_weights_checked(orc, [(0, W)], 1, N, K, "bf16")
+    xd = to_dev(x, "bf16")
+    inp = P.quantize_input(xd, n_select)
+    kact = host(inp.rac.kblock_active)
+    assert (kact == 0).sum() >= K // 16 - 4
+    offs = torch.tensor([0, rows], dtype=torch.int32, device=DEV)
+    y_skip = L.w4a4_grouped_gemm_rac(inp.qo.q, wq.w, offs, N=N, K=K, total_rows=rows,
+                                     r=inp.rac.r, kblock_active=inp.rac.kblock_active,
+                                     skip_inactive=True)
+    y_full = L.w4a4_grouped_gemm_rac(inp.qo.q, wq.w, offs, N=N, K=K, total_rows=rows,
+                                     r=inp.rac.r, kblock_active=inp.rac.kblock_active,
+                                     skip_inactive=False)
+    d = orc.quantize_rac(x, n_select)
+    eq(kact, d["active"], "kblock_active")
+    y_ref = orc.grouped_gemm(N, K, np.array([0, rows], np.int32), None,
+                             (d["codes"], d["scales"], d["s_t"]),
+                             (d["res_codes"], d["res_scales"], d["s_tr"]), w_stack(ref, 1))
+    ys, yf = host(y_skip), host(y_full)
+    assert rel_frob(ys, y_ref) <= REL_F and rel_frob(yf, y_ref) <= REL_F
+    np.testing.assert_array_equal(ys, yf)
