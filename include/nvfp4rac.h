@@ -4,19 +4,20 @@
  *
  * What the calls compute (cited by page title and section):
  *  - QUADS arXiv abstract (mlsanity paper page, "Abstract (arXiv)"): NVFP4
- *    pairs fine-grained scaling with native W4A4 FP4 GEMMs; activations are
- *    recomputed online and quantized on the coarse E2M1 grid; Residual
- *    Activation Compensation (RAC) corrects high-error activation channels
- *    while keeping the native W4A4 GEMMs.
+ *    pairs per-block scale factors with 4-bit E2M1 values and multiplies
+ *    4-bit weights by 4-bit activations; rollout activations are new at
+ *    every step and are quantized at run time; Residual Activation
+ *    Compensation (RAC) repairs the activation channels with the worst
+ *    quantization error and keeps the 4-bit GEMMs.
  *  - Blog post "Why 4-bit RL rollout collapses - and it isn't the weights",
- *    section "The failure mode": E2M1 has eight magnitude levels per sign;
- *    weights go through one shared quantize-dequantize path.
- *  - Same post, section "Two fixes, on two different sides": RAC finds roughly
- *    the top 50% of activation channels by quantization error and runs a
- *    second, residual FP4 pass over just those channels, fused into the
- *    existing kernels; the main W4A4 pass stays intact.
+ *    section "The failure mode": E2M1 can represent eight magnitudes for
+ *    each sign; every engine quantizes the synchronized weights the same way.
+ *  - Same post, section "Two fixes, on two different sides": about half of
+ *    the activation channels, those with the largest error, also go through
+ *    a second 4-bit GEMM on their quantized residual, in the same kernels;
+ *    the ordinary 4-bit pass is unchanged.
  *
- * Number formats (the pages say only "fine-grained scaling"; this library
+ * Number formats (the pages name no block size or scale encoding; this library
  * implements the standard NVFP4 layout):
  *  - element: E2M1 code, 4 bits, sign in bit 3, magnitude index in bits 0-2
  *    over {0, 0.5, 1, 1.5, 2, 3, 4, 6}; -0 is never produced.
@@ -75,9 +76,9 @@ typedef enum {
 const char* nvfp4_status_string(int status);
 
 /* ------------------------------------------------------------------------
- * nvfp4_quantize -- online NVFP4 quantization of one tensor (abstract:
- * activations recomputed online and quantized on the E2M1 grid; blog, "The
- * failure mode": weights use the same shared path).
+ * nvfp4_quantize -- run-time NVFP4 quantization of one tensor (abstract:
+ * activations are quantized at every step; blog, "The failure mode": the
+ * weights go through the same quantizer once per synchronization).
  *
  * x        [rows, K] row-major, row stride ldx elements, dtype F32 or BF16.
  *          Requires K % 16 == 0, ldx % 16 == 0, ldx >= K, x 16-byte aligned.
@@ -103,8 +104,9 @@ int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ld
 
 /* ------------------------------------------------------------------------
  * rac_select_residual -- RAC channel selection and residual re-quantization
- * (blog, "Two fixes, on two different sides": roughly the top 50% of
- * activation channels by quantization error get a second, residual FP4 pass).
+ * (blog, "Two fixes, on two different sides": the activation channels with
+ * the largest errors, about half of them, get a second 4-bit GEMM pass on
+ * their quantized residual).
  *
  * Inputs: the same x, codes, scales, tensor_scale that nvfp4_quantize used
  * and wrote, and its channel_score / channel_max.
@@ -154,9 +156,9 @@ int moe_route(const float* logits, int64_t T, int64_t E, int64_t k,
 
 /* ------------------------------------------------------------------------
  * w4a4_grouped_gemm_rac -- grouped (per-expert) W4A4 GEMM with the RAC
- * residual pass fused into the same kernel (abstract: native W4A4 GEMMs;
- * blog, "Two fixes": the residual pass over the selected channels is layered
- * on top of the intact main pass).
+ * residual pass fused into the same kernel (abstract: 4-bit by 4-bit GEMMs;
+ * blog, "Two fixes": the selected channels' residual pass adds to the
+ * unchanged main pass).
  *
  * For grouped row j of group g (offsets[g] <= j < offsets[g+1]) and src =
  * gather_rows[j] (or j when gather_rows is NULL):

@@ -1,9 +1,9 @@
 // Grouped W4A4 GEMM over experts with the RAC residual pass fused in.
 //
-// QUADS arXiv abstract (mlsanity page, "Abstract (arXiv)"): native W4A4 FP4
-// GEMMs on NVFP4 operands.  QUADS blog post, section "Two fixes, on two
-// different sides": a second, residual FP4 pass over the selected channels is
-// fused into the existing kernel and layered on top of the intact main pass.
+// QUADS arXiv abstract (mlsanity page, "Abstract (arXiv)"): 4-bit weights
+// times 4-bit activations on NVFP4 operands.  QUADS blog post, section "Two
+// fixes, on two different sides": the selected channels' residual gets its
+// own 4-bit pass inside the same kernel, added to the unchanged main pass.
 //
 // MI355X design:
 //  * Operands stay NVFP4 in HBM and LDS (4 bits per element plus one E4M3

@@ -1,10 +1,10 @@
 // Online NVFP4 quantizer and Residual Activation Compensation (RAC) kernels.
 //
-// QUADS arXiv abstract (mlsanity page, "Abstract (arXiv)"): activations are
-// recomputed online and quantized on the coarse E2M1 grid with fine-grained
-// scaling.  QUADS blog post ("Why 4-bit RL rollout collapses"), section "Two
+// QUADS arXiv abstract (mlsanity page, "Abstract (arXiv)"): rollout
+// activations are new at every step, so they are quantized to E2M1 with
+// per-block scales at run time.  QUADS blog post ("Why 4-bit RL rollout collapses"), section "Two
 // fixes, on two different sides": RAC ranks activation channels by
-// quantization error, keeps roughly the top half, and re-quantizes their
+// quantization error, keeps about the worse half, and re-quantizes their
 // residual for a second FP4 pass.
 //
 // Passes over x (row-major [rows, K], 16-element blocks along K):

@@ -3,7 +3,7 @@
 Dense linear (one GEMM input):
     nvfp4_quantize(X, stats) -> rac_select_residual -> w4a4_grouped_gemm_rac
 MoE FFN layer (QUADS rollout: online NVFP4 activations + RAC on every GEMM
-input, native W4A4 expert GEMMs; arXiv abstract on the mlsanity page and the
+input, 4-bit by 4-bit expert GEMMs; arXiv abstract on the mlsanity page and the
 blog post's section "Two fixes, on two different sides"):
     moe_route(logits)
     nvfp4_quantize(X, stats) -> rac_select_residual(X)
@@ -12,8 +12,8 @@ blog post's section "Two fixes, on two different sides"):
     nvfp4_quantize(H, amax_in = max|H|, stats) -> rac_select_residual(H)
     w4a4_grouped_gemm_rac(down) -> Y (FP32, rows in expert order)
 Weights are quantized once, per expert and projection, by the same
-nvfp4_quantize ("shared quantize-dequantize path" for weights: blog post,
-section "The failure mode").
+nvfp4_quantize (every engine quantizes the synchronized weights the same way:
+blog post, section "The failure mode").
 """
 from __future__ import annotations
 

@@ -10,17 +10,19 @@
  * Sources (cited by page title and section):
  *  [ABS]  QUADS arXiv abstract, as reproduced on the mlsanity paper page
  *         ("QUADS: Stabilizing NVFP4 Reinforcement Learning for MoE ...",
- *         section "Abstract (arXiv)"): NVFP4 = fine-grained scaling + native
- *         W4A4 FP4 GEMMs; activations are recomputed online and quantized on
- *         the coarse E2M1 grid; RAC corrects high-error activation channels
- *         while preserving the native W4A4 GEMMs.
+ *         section "Abstract (arXiv)"): NVFP4 pairs per-block scale factors
+ *         with 4-bit E2M1 values and multiplies 4-bit weights by 4-bit
+ *         activations; rollout activations are new at every step and are
+ *         quantized at run time; RAC repairs the activation channels whose
+ *         quantization error is worst and keeps the 4-bit GEMMs.
  *  [FAIL] Blog post "Why 4-bit RL rollout collapses - and it isn't the
- *         weights", section "The failure mode": E2M1 has 8 magnitude levels
- *         per sign; weights follow one identical quantize-dequantize path.
- *  [FIX]  Same blog post, section "Two fixes, on two different sides": RAC
- *         picks roughly the top 50% of activation channels by quantization
- *         error and runs a second, residual FP4 pass over just those
- *         channels; the main W4A4 pass stays intact.
+ *         weights", section "The failure mode": E2M1 can represent eight
+ *         magnitudes for each sign; every rollout engine quantizes the
+ *         synchronized weights the same way.
+ *  [FIX]  Same blog post, section "Two fixes, on two different sides": about
+ *         half of the activation channels, those with the largest error,
+ *         also go through a second 4-bit GEMM on their quantized residual,
+ *         in the same kernels; the ordinary 4-bit pass is unchanged.
  *
  * The pages fix neither the block size, the scale encodings, the rounding
  * mode, the error metric nor the tie-breaks.  This file implements the
@@ -226,7 +228,7 @@ int64_t or_score_term(float e, int shift) {
 }
 
 /* Per-channel quantization-error statistics over all rows of the call
- * [FIX: "activation channels with the largest quantization error"].
+ * [FIX: channels are ranked by their quantization error].
  * A channel is one K column of the GEMM input.  score[k] = sum over rows of
  * q^2 (exact int64: the sum of squared errors in fixed point);
  * chmax[k] = max over rows of |e|. */
@@ -295,8 +297,8 @@ void or_rac_select(const int64_t* score, const float* chmax, int64_t K,
 }
 
 /* Masked residual r = mask * e, re-quantized to NVFP4 in the same 16-element
- * blocks with its own tensor scale [FIX: "a second, residual FP4 pass over
- * just those channels"].  The residual tensor amax is max|r| computed here
+ * blocks with its own tensor scale [FIX: the selected channels' residual gets
+ * its own 4-bit pass].  The residual tensor amax is max|r| computed here
  * directly from r; it is also returned so tests can check it against the
  * selection's s_tr. */
 void or_rac_residual(const float* x, int64_t rows, int64_t K, int64_t ldx,
@@ -348,8 +350,8 @@ static int64_t group_of(const int32_t* offsets, int64_t G, int64_t j) {
  * output row j, src = gather[j] (or j).  Both sums are exact int64 sums of
  * the integer images (scaled by 2^-20); they are combined in long double and
  * rounded once to float.  Residual terms are dropped when r_codes is NULL
- * (naive W4A4).  [ABS: native W4A4 GEMMs; FIX: main pass intact, residual
- * pass layered on top.] */
+ * (naive W4A4).  [ABS: 4-bit by 4-bit GEMMs; FIX: the ordinary pass is
+ * unchanged and the residual pass adds to it.] */
 static void gemm_one(int64_t G, int64_t N, int64_t K, const int32_t* offsets,
                      const int32_t* gather, const uint8_t* a_codes,
                      const uint8_t* a_scales, float a_ts,

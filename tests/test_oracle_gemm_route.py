@@ -1,9 +1,9 @@
 """Pins of the oracle's grouped W4A4 GEMM (with and without the RAC residual
 pass), its MoE routing and the SiLU*mul step.
 
-GEMM: native W4A4 GEMMs on NVFP4 operands (QUADS arXiv abstract, mlsanity
-page "Abstract (arXiv)"); the residual pass is layered on top of an intact
-main pass (QUADS blog post, section "Two fixes, on two different sides").
+GEMM: 4-bit by 4-bit GEMMs on NVFP4 operands (QUADS arXiv abstract, mlsanity
+page "Abstract (arXiv)"); the residual pass adds to an unchanged main pass
+(QUADS blog post, section "Two fixes, on two different sides").
 Routing and SiLU*mul belong to the MoE FFN layer the workloads describe."""
 from fractions import Fraction as Fr
 
