@@ -108,8 +108,10 @@ int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ld
  * the largest errors, about half of them, get a second 4-bit GEMM pass on
  * their quantized residual).
  *
- * Inputs: the same x, codes, scales, tensor_scale that nvfp4_quantize used
- * and wrote, and its channel_score / channel_max.
+ * Inputs: the same x, scales, tensor_scale that nvfp4_quantize used and
+ * wrote, and its channel_score / channel_max.  codes is not read and may be
+ * NULL: the main codes are a function of x, scales and tensor_scale, and the
+ * residual pass recomputes them, which costs less than reading them back.
  * n_select (0 <= n_select <= K; K/2 in the workloads): the channels with the
  *          largest channel_score are selected, ties toward the lower channel
  *          index.
@@ -120,7 +122,8 @@ int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ld
  *          NVFP4 tensor in the same 16-element blocks with
  *          s_tr = RN32(max over selected k of channel_max[k] / 2688)
  *          (= max|r| / 2688).
- * Requires K <= 16384 and the layout rules of nvfp4_quantize.
+ * Requires K <= 16384 and the layout rules of nvfp4_quantize; ws 4-byte
+ * aligned.  The result is deterministic (integer ranks, max reductions).
  * ------------------------------------------------------------------------ */
 size_t rac_select_residual_workspace_size(int64_t rows, int64_t K);
 int rac_select_residual(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx,

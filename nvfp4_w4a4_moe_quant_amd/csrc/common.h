@@ -130,3 +130,34 @@ __device__ __forceinline__ float nv_wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
+
+// Clear the sign of E2M1 codes whose magnitude index is 0 (no -0), for the 8
+// codes of a word: bit 3 of a nibble survives only if its low 3 bits are not 0.
+__device__ __forceinline__ uint32_t nv_clear_neg_zero(uint32_t w) {
+  const uint32_t nz = ((w & 0x77777777u) + 0x77777777u) & 0x88888888u;
+  return w & (nz | 0x77777777u);
+}
+
+// 8 values times r -> 8 E2M1 codes (element 2j in the low nibble of byte j).
+// The gfx950 packed FP4 conversion rounds to nearest even and saturates at 6;
+// each product x*r is one FP32 multiply before it.
+__device__ __forceinline__ uint32_t nv_encode8(const float* v, float r) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0] * r, v[1] * r, 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2] * r, v[3] * r, 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4] * r, v[5] * r, 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6] * r, v[7] * r, 1.0f, 3);
+  return nv_clear_neg_zero(w);
+}
+
+typedef float nv_float2 __attribute__((ext_vector_type(2)));
+
+// 8 E2M1 codes -> 8 signed grid values (FP32, exact).
+__device__ __forceinline__ void nv_decode8(uint32_t w, float* g) {
+  const nv_float2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const nv_float2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const nv_float2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const nv_float2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  g[0] = a.x; g[1] = a.y; g[2] = b.x; g[3] = b.y;
+  g[4] = c.x; g[5] = c.y; g[6] = d.x; g[7] = d.y;
+}

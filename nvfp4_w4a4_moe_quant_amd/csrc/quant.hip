@@ -11,10 +11,13 @@
 //   k_amax      partial max|x| per workgroup (tensor amax), zeroes RAC stats
 //   k_quant     tensor scale, block scales, E2M1 codes; optionally the exact
 //               per-channel error statistics (score = sum q^2, max |e|)
-//   k_select    one workgroup: top-n channels by (score desc, index asc)
-//               via radix select, block-activity flags, residual tensor scale
-//   k_residual  r = mask * e re-quantized in the same blocks
+//   k_rank      rank of every channel by (score desc, index asc); the
+//               first n are selected; block masks and activity flags
+//   k_residual  r = mask * e re-quantized in the same blocks; also the
+//               residual tensor scale and the ascending selected indices
 // All reductions are max or integer sums, so results are order-independent.
+#include <stdlib.h>
+
 #include "common.h"
 
 namespace {
@@ -83,16 +86,53 @@ __device__ float workgroup_amax(const float* __restrict__ partials, int nparts,
 // handles column block (blockIdx.x * tpr + t % tpr) for rows
 // start + t / tpr, start + t / tpr + rpi, ...  With statistics, per-channel
 // partial sums are accumulated in registers (FP64, exact integers below 2^53),
-// combined in LDS, then added to the global int64 sums.
-template <bool kStats>
-__global__ __launch_bounds__(kThreads) void k_quant(
-    const void* __restrict__ x, int bf16, int64_t rows, int64_t K, int64_t ldx,
+// combined in LDS, then added to the global int64 sums.  That costs one
+// global atomic pair per channel and workgroup, and atomics on one address
+// are serialized, so the host keeps the row splits few and the workgroups
+// large (16 waves).
+constexpr int kQThreads = 1024;
+
+// Raw 16-element block as loaded (bf16: 8 dwords, fp32: 16 dwords); it is
+// widened to FP32 only when used, which keeps two rows in flight within the
+// register budget of a 1024-thread workgroup.
+template <bool kBf16>
+struct RawBlock {
+  uint32_t w[kBf16 ? 8 : 16];
+  __device__ __forceinline__ void load(const void* x, int64_t off) {
+    if constexpr (kBf16) {
+      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + off);
+      const uint4 a = p[0], b = p[1];
+      w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+      w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    } else {
+      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(x) + off);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 q = p[i];
+        w[4 * i] = q.x; w[4 * i + 1] = q.y; w[4 * i + 2] = q.z; w[4 * i + 3] = q.w;
+      }
+    }
+  }
+  __device__ __forceinline__ void widen(float* v) const {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if constexpr (kBf16)
+        v[i] = __uint_as_float((i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16));
+      else
+        v[i] = __uint_as_float(w[i]);
+    }
+  }
+};
+
+template <bool kStats, bool kBf16>
+__global__ __launch_bounds__(kQThreads) void k_quant(
+    const void* __restrict__ x, int64_t rows, int64_t K, int64_t ldx,
     const float* __restrict__ partials, int nparts, const float* __restrict__ amax_in,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ tscale_out,
     int64_t* __restrict__ score, uint32_t* __restrict__ chmax, int tpr, int rpi,
     int64_t rows_per_split) {
   extern __shared__ unsigned char dyn_lds[];
-  __shared__ float red[kThreads / 64];
+  __shared__ float red[kQThreads / 64];
   const float amax = workgroup_amax(partials, nparts, amax_in, red);
   const float s_t = nv_tensor_scale(amax);
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *tscale_out = s_t;
@@ -114,40 +154,54 @@ __global__ __launch_bounds__(kThreads) void k_quant(
     emax[i] = 0.0f;
   }
 
-  if (active) {
-    for (int64_t r = r0 + sub; r < r1; r += rpi) {
-      float v[16];
-      nv_load16(x, bf16, r * ldx + cb * 16, v);
-      float amax_b = 0.0f;
+  auto block = [&](const RawBlock<kBf16>& raw, int64_t r) {
+    float v[16];
+    raw.widen(v);
+    float amax_b = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) amax_b = __builtin_fmaxf(amax_b, __builtin_fabsf(v[i]));
-      const uint32_t sc = nv_block_scale(amax_b, s_t);
-      const float sb = nv_e4m3_to_f32(sc);
-      const float Sb = sb * s_t;
-      const float rb = nv_block_recip(Sb);
-      uint32_t packed[2] = {0u, 0u};
+    for (int i = 0; i < 16; ++i) amax_b = __builtin_fmaxf(amax_b, __builtin_fabsf(v[i]));
+    const uint32_t sc = nv_block_scale(amax_b, s_t);
+    const float sb = nv_e4m3_to_f32(sc);
+    const float rb = nv_block_recip(sb * s_t);
+    const uint32_t lo = nv_encode8(v, rb), hi = nv_encode8(v + 8, rb);
+    if constexpr (kStats) {
+      float g[16];
+      nv_decode8(lo, g);
+      nv_decode8(hi, g + 8);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const uint32_t c = nv_e2m1_encode(v[i] * rb);
-        packed[i >> 3] |= c << ((i & 7) * 4);
-        if constexpr (kStats) {
-          const float d = (nv_e2m1_to_f32(c) * sb) * s_t;
-          const float e = v[i] - d;
-          const float q = nv_score_q(e, shift);
-          acc[i] = __builtin_fma((double)q, (double)q, acc[i]);
-          emax[i] = __builtin_fmaxf(emax[i], __builtin_fabsf(e));
-        }
+        const float e = v[i] - (g[i] * sb) * s_t;
+        const float q = nv_score_q(e, shift);
+        acc[i] = __builtin_fma((double)q, (double)q, acc[i]);
+        emax[i] = __builtin_fmaxf(emax[i], __builtin_fabsf(e));
       }
-      *reinterpret_cast<uint2*>(codes + r * (K >> 1) + cb * 8) = make_uint2(packed[0], packed[1]);
-      scales[r * CB + cb] = (uint8_t)sc;
+    }
+    *reinterpret_cast<uint2*>(codes + r * (K >> 1) + cb * 8) = make_uint2(lo, hi);
+    scales[r * CB + cb] = (uint8_t)sc;
+  };
+
+  // bf16: two rows per iteration, both loads issued before either is used
+  // (fp32 blocks are twice as large, so one row there).
+  constexpr int kIn = kBf16 ? 2 : 1;
+  if (active) {
+    for (int64_t r = r0 + sub; r < r1; r += kIn * (int64_t)rpi) {
+      RawBlock<kBf16> b[kIn];
+#pragma unroll
+      for (int u = 0; u < kIn; ++u)
+        if (r + u * rpi < r1) b[u].load(x, (r + u * rpi) * ldx + cb * 16);
+#pragma unroll
+      for (int u = 0; u < kIn; ++u)
+        if (r + u * rpi < r1) block(b[u], r + u * rpi);
     }
   }
 
   if constexpr (kStats) {
-    // LDS: tpr*16 int64 sums, then tpr*16 uint32 maxima.
+    // LDS: int64 sums then uint32 maxima, both [16][tpr] (element-in-block
+    // major), so the lanes of a wave, which hold consecutive column blocks,
+    // hit consecutive words and the atomics are free of bank conflicts.
     unsigned long long* lsum = reinterpret_cast<unsigned long long*>(dyn_lds);
     uint32_t* lmax = reinterpret_cast<uint32_t*>(lsum + tpr * 16);
-    for (int i = threadIdx.x; i < tpr * 16; i += kThreads) {
+    for (int i = threadIdx.x; i < tpr * 16; i += kQThreads) {
       lsum[i] = 0ull;
       lmax[i] = 0u;
     }
@@ -155,26 +209,100 @@ __global__ __launch_bounds__(kThreads) void k_quant(
     if (active) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        if (acc[i] != 0.0) atomicAdd(&lsum[cbl * 16 + i], (unsigned long long)acc[i]);
-        if (emax[i] != 0.0f) atomicMax(&lmax[cbl * 16 + i], __float_as_uint(emax[i]));
+        if (acc[i] != 0.0) atomicAdd(&lsum[i * tpr + cbl], (unsigned long long)acc[i]);
+        if (emax[i] != 0.0f) atomicMax(&lmax[i * tpr + cbl], __float_as_uint(emax[i]));
       }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < tpr * 16; i += kThreads) {
-      const int64_t k = (int64_t)blockIdx.x * tpr * 16 + i;
+    // slot j holds channel (tile start) + 16 * (j % tpr) + j / tpr
+    for (int j = threadIdx.x; j < tpr * 16; j += kQThreads) {
+      const int64_t k = ((int64_t)blockIdx.x * tpr + j % tpr) * 16 + j / tpr;
       if (k < K) {
-        if (lsum[i]) atomicAdd(reinterpret_cast<unsigned long long*>(score) + k, lsum[i]);
-        if (lmax[i]) atomicMax(chmax + k, lmax[i]);
+        if (lsum[j]) atomicAdd(reinterpret_cast<unsigned long long*>(score) + k, lsum[j]);
+        if (lmax[j]) atomicMax(chmax + k, lmax[j]);
       }
     }
   }
 }
 
 // ---------------------------------------------------------------- select
+// Channel k is selected iff its rank in the order (score desc, index asc),
+//   rank_k = #{j : s_j > s_k} + #{j < k : s_j == s_k},
+// is below n_sel: exactly the first n_sel channels of that order.  The ranks
+// are counted directly, which needs no sort and no serial passes.
+// k_rank: workgroup b ranks channels 64b .. 64b+63 (one per lane); its 16
+// waves split the j range and walk their part of the scores with uniform
+// loads; the partial counts are summed in LDS.  Per workgroup it also writes
+// the selection bytes, the 16-channel block masks and activity flags of its
+// four blocks, and the max |e| over its selected channels.
+constexpr int kRankWaves = 16;
+constexpr int kRankTile = 4096;  // keys staged in LDS per pass (32 KiB)
 constexpr int kSelThreads = 1024;
-constexpr int kSelPer = 16;  // K <= 16384
+constexpr int kMaxSelectK = 16384;
 
-// Exclusive prefix sum over the workgroup; returns the total in *total.
+__global__ __launch_bounds__(64 * kRankWaves) void k_rank(
+    const int64_t* __restrict__ score_in, const uint32_t* __restrict__ chmax, int K, int n_sel,
+    uint16_t* __restrict__ mask16, uint8_t* __restrict__ kact, uint32_t* __restrict__ part_max) {
+  __shared__ uint64_t tile[kRankTile];
+  __shared__ uint32_t cnt[kRankWaves][64];
+  const uint64_t* score = reinterpret_cast<const uint64_t*>(score_in);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int k0 = blockIdx.x * 64;
+  const int k = k0 + lane;
+  const uint64_t sk = k < K ? score[k] : ~0ull;
+  const int d0 = k0, d1 = k0 + 64 < K ? k0 + 64 : K;  // this workgroup's own channels
+
+  uint32_t c = 0;
+  for (int t0 = 0; t0 < K; t0 += kRankTile) {
+    const int n = K - t0 < kRankTile ? K - t0 : kRankTile;
+    __syncthreads();  // the previous tile is consumed
+#pragma unroll 4
+    for (int i = threadIdx.x; i < n; i += 64 * kRankWaves) tile[i] = score[t0 + i];
+    __syncthreads();
+    // this wave's share of the tile, split where the tie rule changes
+    const int per = (n + kRankWaves - 1) / kRankWaves;
+    const int j0 = t0 + w * per;
+    const int j1 = j0 + per < t0 + n ? j0 + per : t0 + n;
+    {  // j below every channel of this workgroup: a tie ranks j first
+      const int e = j1 < d0 ? j1 : d0;
+#pragma unroll 8
+      for (int j = j0; j < e; ++j) c += tile[j - t0] >= sk ? 1u : 0u;
+    }
+    {
+      const int b = j0 > d0 ? j0 : d0, e = j1 < d1 ? j1 : d1;
+      for (int j = b; j < e; ++j) {
+        const uint64_t sj = tile[j - t0];
+        c += (sj > sk || (sj == sk && j < k)) ? 1u : 0u;
+      }
+    }
+    {  // j above every channel of this workgroup: a tie ranks j after
+      const int b = j0 > d1 ? j0 : d1;
+#pragma unroll 8
+      for (int j = b; j < j1; ++j) c += tile[j - t0] > sk ? 1u : 0u;
+    }
+  }
+  cnt[w][lane] = c;
+  __syncthreads();
+  if (w == 0) {
+    uint32_t rank = 0;
+#pragma unroll
+    for (int i = 0; i < kRankWaves; ++i) rank += cnt[i][lane];
+    const bool s = k < K && rank < (uint32_t)n_sel;
+    const uint64_t m = __ballot(s);
+    if (lane < 4 && k0 + 16 * lane < K) {
+      const uint32_t bits = (uint32_t)(m >> (16 * lane)) & 0xFFFFu;
+      mask16[blockIdx.x * 4 + lane] = (uint16_t)bits;
+      kact[blockIdx.x * 4 + lane] = bits ? 1 : 0;
+    }
+    const float a = nv_wave_max(s ? __uint_as_float(chmax[k]) : 0.0f);
+    if (lane == 0) part_max[blockIdx.x] = __float_as_uint(a);
+  }
+}
+
+// Exclusive prefix sum over a workgroup of kNT threads; returns the total
+// in *total.  wsum holds kNT / 64 entries.
+template <int kNT>
 __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   uint32_t inc = v;
@@ -186,7 +314,8 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* t
   if (lane == 63) wsum[w] = inc;
   __syncthreads();
   uint32_t before = 0, all = 0;
-  for (int i = 0; i < kSelThreads / 64; ++i) {
+#pragma unroll
+  for (int i = 0; i < kNT / 64; ++i) {
     const uint32_t s = wsum[i];
     if (i < w) before += s;
     all += s;
@@ -196,129 +325,57 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* t
   return before + inc - v;
 }
 
-__global__ __launch_bounds__(kSelThreads) void k_select(
-    const int64_t* __restrict__ score_in, const uint32_t* __restrict__ chmax, int K, int n_sel,
-    int32_t* __restrict__ selected, uint8_t* __restrict__ kact, uint16_t* __restrict__ mask16,
-    float* __restrict__ res_ts) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t found[2];
-  __shared__ uint32_t wsum[kSelThreads / 64];
-  __shared__ uint32_t wmax[kSelThreads / 64];
-  __shared__ uint8_t lmask[kSelPer * kSelThreads];
-  const int t = threadIdx.x;
-  const int per = (K + kSelThreads - 1) / kSelThreads;
-  const int base = t * per;
-
-  uint64_t v[kSelPer];
-#pragma unroll
-  for (int i = 0; i < kSelPer; ++i) {
-    const int k = base + i;
-    v[i] = (i < per && k < K) ? (uint64_t)score_in[k] : 0ull;
-  }
-  auto valid = [&](int i) { return i < per && base + i < K; };
-
-  // Radix select (8-bit digits, most significant first) of the n_sel-th
-  // largest score T; `remaining` ends as the number of channels equal to T
-  // that are taken (the lowest-index ones).
-  uint64_t prefix = 0, pmask = 0;
-  uint32_t remaining = (uint32_t)n_sel;
-  if (n_sel > 0) {
-    for (int shift = 56; shift >= 0; shift -= 8) {
-      if (t < 256) hist[t] = 0u;
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < kSelPer; ++i)
-        if (valid(i) && (v[i] & pmask) == prefix) atomicAdd(&hist[(v[i] >> shift) & 255u], 1u);
-      __syncthreads();
-      if (t < 64) {
-        // lane t owns digits 255-4t .. 252-4t (descending order)
-        uint32_t c[4], s = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          c[j] = hist[255 - (4 * t + j)];
-          s += c[j];
-        }
-        uint32_t inc = s;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t n = __shfl_up(inc, o, 64);
-          if (t >= o) inc += n;
-        }
-        uint32_t run = inc - s;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (run < remaining && remaining <= run + c[j]) {
-            found[0] = 255u - (uint32_t)(4 * t + j);
-            found[1] = run;
-          }
-          run += c[j];
-        }
-      }
-      __syncthreads();
-      prefix |= (uint64_t)found[0] << shift;
-      pmask |= (uint64_t)0xFF << shift;
-      remaining -= found[1];
-      __syncthreads();
-    }
-  }
-  const uint64_t T = prefix;
-
-  // rank among channels equal to T (ascending index)
-  uint32_t eq = 0;
-#pragma unroll
-  for (int i = 0; i < kSelPer; ++i) eq += (n_sel > 0 && valid(i) && v[i] == T) ? 1u : 0u;
-  uint32_t tot;
-  uint32_t eq_before = block_exclusive_scan(eq, wsum, &tot);
-
-  uint32_t nsel_local = 0;
-  float amax_r = 0.0f;
-  uint8_t m[kSelPer];
-#pragma unroll
-  for (int i = 0; i < kSelPer; ++i) {
-    bool s = false;
-    if (n_sel > 0 && valid(i)) {
-      if (v[i] > T) s = true;
-      else if (v[i] == T) { s = eq_before < remaining; ++eq_before; }
-    }
-    m[i] = s ? 1 : 0;
-    if (s) {
-      ++nsel_local;
-      amax_r = __builtin_fmaxf(amax_r, __uint_as_float(chmax[base + i]));
-    }
-    if (valid(i)) lmask[base + i] = m[i];
-  }
-  uint32_t pos = block_exclusive_scan(nsel_local, wsum, &tot);
-#pragma unroll
-  for (int i = 0; i < kSelPer; ++i)
-    if (m[i]) selected[pos++] = base + i;
-
-  amax_r = nv_wave_max(amax_r);
-  if ((t & 63) == 0) wmax[t >> 6] = __float_as_uint(amax_r);
-  __syncthreads();  // also publishes lmask
-  if (t == 0) {
-    float a = 0.0f;
-    for (int w = 0; w < kSelThreads / 64; ++w) a = __builtin_fmaxf(a, __uint_as_float(wmax[w]));
-    *res_ts = nv_tensor_scale(a);
-  }
-  for (int b = t; b < (K >> 4); b += kSelThreads) {
-    uint32_t bits = 0;
-    for (int j = 0; j < 16; ++j) bits |= (uint32_t)lmask[b * 16 + j] << j;
-    mask16[b] = (uint16_t)bits;
-    kact[b] = bits ? 1 : 0;
-  }
-}
-
 // -------------------------------------------------------------- residual
+// r = mask * e in every block with a selected channel, e = x - deq(q(x)).
+// The main codes are recomputed from x, the block scale and the tensor scale
+// (the same operations as k_quant, so the same codes) rather than read back:
+// that saves a quarter of this pass's reads.  Every workgroup first reduces
+// k_rank's per-workgroup maxima to the residual tensor scale; workgroup 0
+// also writes it and lists the selected channels in ascending order (a prefix
+// sum of the block masks' popcounts).
 __global__ __launch_bounds__(kThreads) void k_residual(
     const void* __restrict__ x, int bf16, int64_t rows, int64_t K, int64_t ldx,
-    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-    const float* __restrict__ tscale, const uint16_t* __restrict__ mask16,
-    const float* __restrict__ res_ts, uint8_t* __restrict__ res_codes,
+    const uint8_t* __restrict__ scales, const float* __restrict__ tscale,
+    const uint16_t* __restrict__ mask16, const uint32_t* __restrict__ part_max, int nparts,
+    int32_t* __restrict__ selected,
+    float* __restrict__ res_ts, uint8_t* __restrict__ res_codes,
     uint8_t* __restrict__ res_scales) {
+  __shared__ uint32_t wred[kThreads / 64];
+  float a = 0.0f;
+  for (int i = threadIdx.x; i < nparts; i += kThreads)
+    a = __builtin_fmaxf(a, __uint_as_float(part_max[i]));
+  a = nv_wave_max(a);
+  if ((threadIdx.x & 63) == 0) wred[threadIdx.x >> 6] = __float_as_uint(a);
+  __syncthreads();
+  float m_all = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) m_all = __builtin_fmaxf(m_all, __uint_as_float(wred[w]));
+  const float s_tr = nv_tensor_scale(m_all);
+  if (blockIdx.x == 0) {
+    __syncthreads();  // wred is reused by the scan
+    if (threadIdx.x == 0) *res_ts = s_tr;
+    // thread t lists the selected channels of blocks [t*pb, t*pb + pb)
+    constexpr int kPb = (kMaxSelectK / 16 + kThreads - 1) / kThreads;
+    const int nb = (int)(K >> 4);
+    const int pb = (nb + kThreads - 1) / kThreads;
+    const int b0 = threadIdx.x * pb;
+    uint32_t bits[kPb];
+    uint32_t n = 0;
+#pragma unroll
+    for (int i = 0; i < kPb; ++i) {
+      bits[i] = (i < pb && b0 + i < nb) ? (uint32_t)mask16[b0 + i] : 0u;
+      n += __builtin_popcount(bits[i]);
+    }
+    uint32_t tot;
+    uint32_t pos = block_exclusive_scan<kThreads>(n, wred, &tot);
+#pragma unroll
+    for (int i = 0; i < kPb; ++i)
+      for (uint32_t m = bits[i]; m; m &= m - 1) selected[pos++] = (b0 + i) * 16 + __builtin_ctz(m);
+  }
+
   const int64_t CB = K >> 4;
   const int64_t nblk = rows * CB;
   const float s_t = *tscale;
-  const float s_tr = *res_ts;
   for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk;
        b += (int64_t)gridDim.x * kThreads) {
     const int64_t r = b / CB, cb = b - r * CB;
@@ -328,22 +385,23 @@ __global__ __launch_bounds__(kThreads) void k_residual(
     if (m) {
       float v[16];
       nv_load16(x, bf16, r * ldx + cb * 16, v);
-      const uint2 cw = *reinterpret_cast<const uint2*>(codes + r * (K >> 1) + cb * 8);
       const float sb = nv_e4m3_to_f32(scales[r * CB + cb]);
-      float e[16];
+      const float rm = nv_block_recip(sb * s_t);
+      float g[16], e[16];
+      nv_decode8(nv_encode8(v, rm), g);
+      nv_decode8(nv_encode8(v + 8, rm), g + 8);
       float amax_b = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const uint32_t c = ((i < 8 ? cw.x : cw.y) >> ((i & 7) * 4)) & 15u;
-        const float d = (nv_e2m1_to_f32(c) * sb) * s_t;
+        const float d = (g[i] * sb) * s_t;
         e[i] = ((m >> i) & 1u) ? v[i] - d : 0.0f;
         amax_b = __builtin_fmaxf(amax_b, __builtin_fabsf(e[i]));
       }
       sc = nv_block_scale(amax_b, s_tr);
       const float Sb = nv_e4m3_to_f32(sc) * s_tr;
       const float rb = nv_block_recip(Sb);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) packed[i >> 3] |= nv_e2m1_encode(e[i] * rb) << ((i & 7) * 4);
+      packed[0] = nv_encode8(e, rb);
+      packed[1] = nv_encode8(e + 8, rb);
     }
     *reinterpret_cast<uint2*>(res_codes + r * (K >> 1) + cb * 8) = make_uint2(packed[0], packed[1]);
     res_scales[r * CB + cb] = (uint8_t)sc;
@@ -415,29 +473,62 @@ int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ld
     hipLaunchKernelGGL(k_zero_stats, dim3((unsigned)blocks_for(K, 256, 1024)), dim3(256), 0, s,
                        K, channel_score, chm);
   }
-  // column tiles of at most 256 column blocks, rows_per_iter sub-rows
-  const int64_t ntile = (CB + kThreads - 1) / kThreads;
+  // Column tiles of at most tile_max column blocks (16: 256 channels, 512 B
+  // of bf16 per row), rpi rows in flight per pass.  Narrow tiles keep the
+  // global atomics per workgroup few.
+  static const int tile_max = [] {
+    const char* e = getenv("NVFP4RAC_QUANT_TPR");
+    return e ? atoi(e) : 16;
+  }();
+  const int64_t ntile = (CB + tile_max - 1) / tile_max;
   const int tpr = (int)((CB + ntile - 1) / ntile);
-  const int rpi = kThreads / tpr;
-  int64_t splits = blocks_for(rows, (int64_t)rpi * 16, 65535);
-  const int64_t max_splits = 512 / ntile > 0 ? 512 / ntile : 1;
+  const int rpi = kQThreads / tpr;
+  // Row splits: with statistics every workgroup adds one atomic per channel
+  // to the global sums, so the splits stay few (about one workgroup per CU
+  // over all column tiles) and each thread takes at least two rows.
+  static const int wg_target = [] {
+    const char* e = getenv("NVFP4RAC_QUANT_WGS");
+    return e ? atoi(e) : 256;
+  }();
+  static const int min_rows = [] {
+    const char* e = getenv("NVFP4RAC_QUANT_MINROWS");
+    return e ? atoi(e) : 2;
+  }();
+  int64_t splits = blocks_for(rows, (int64_t)rpi * min_rows, 65535);
+  const int64_t max_splits = stats ? (wg_target / ntile > 0 ? wg_target / ntile : 1) : 65535;
   if (splits > max_splits) splits = max_splits;
   const int64_t rows_per_split = rows > 0 ? (rows + splits - 1) / splits : 1;
   const size_t lds = stats ? (size_t)tpr * 16 * (sizeof(uint64_t) + sizeof(uint32_t)) : 0;
-  if (stats)
-    hipLaunchKernelGGL(k_quant<true>, dim3((unsigned)ntile, (unsigned)splits), dim3(kThreads), lds,
-                       s, x, bf16, rows, K, ldx, partials, nparts, amax_in, codes, scales,
-                       tensor_scale, channel_score, chm, tpr, rpi, rows_per_split);
-  else
-    hipLaunchKernelGGL(k_quant<false>, dim3((unsigned)ntile, (unsigned)splits), dim3(kThreads), 0,
-                       s, x, bf16, rows, K, ldx, partials, nparts, amax_in, codes, scales,
-                       tensor_scale, nullptr, nullptr, tpr, rpi, rows_per_split);
+  const dim3 grid((unsigned)ntile, (unsigned)splits);
+  int64_t* sc = stats ? channel_score : nullptr;
+  uint32_t* cm = stats ? chm : nullptr;
+#define NV_QUANT_LAUNCH(ST, BF)                                                                 \
+  hipLaunchKernelGGL((k_quant<ST, BF>), grid, dim3(kQThreads), ST ? lds : 0, s, x, rows, K, ldx, \
+                     partials, nparts, amax_in, codes, scales, tensor_scale, sc, cm, tpr, rpi,   \
+                     rows_per_split)
+  if (stats && bf16) NV_QUANT_LAUNCH(true, true);
+  else if (stats) NV_QUANT_LAUNCH(true, false);
+  else if (bf16) NV_QUANT_LAUNCH(false, true);
+  else NV_QUANT_LAUNCH(false, false);
+#undef NV_QUANT_LAUNCH
   return nv_launch_status();
 }
 
-size_t rac_select_residual_workspace_size(int64_t, int64_t K) {
-  return nv_round256(sizeof(uint16_t) * (size_t)(K > 0 ? K / 16 : 0));
+// Workspace of rac_select_residual: block masks [K/16] u16, then the
+// per-workgroup max |e| of the selected channels [ceil(K/64)] u32.
+struct RacWs {
+  size_t mask_off, max_off, total;
+};
+static RacWs rac_ws_layout(int64_t K) {
+  RacWs w;
+  const size_t k = (size_t)(K > 0 ? K : 0);
+  w.mask_off = 0;
+  w.max_off = nv_round256(sizeof(uint16_t) * (k / 16));
+  w.total = w.max_off + nv_round256(sizeof(uint32_t) * ((k + 63) / 64));
+  return w;
 }
+
+size_t rac_select_residual_workspace_size(int64_t, int64_t K) { return rac_ws_layout(K).total; }
 
 int rac_select_residual(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx,
                         const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
@@ -447,29 +538,35 @@ int rac_select_residual(const void* x, int dtype, int64_t rows, int64_t K, int64
                         void* stream) {
   int st = check_x(x, dtype, rows, K, ldx);
   if (st) return st;
+  (void)codes;  // recomputed from x, scales and tensor_scale
   NV_RETURN_IF(!tensor_scale || !channel_score || !channel_max || !kblock_active ||
                    !res_tensor_scale,
                NVFP4_ERR_NULL);
-  NV_RETURN_IF(rows > 0 && (!codes || !scales || !res_codes || !res_scales), NVFP4_ERR_NULL);
-  NV_RETURN_IF(n_select < 0 || n_select > K || K > kSelPer * kSelThreads, NVFP4_ERR_SHAPE);
+  NV_RETURN_IF(rows > 0 && (!scales || !res_codes || !res_scales), NVFP4_ERR_NULL);
+  NV_RETURN_IF(n_select < 0 || n_select > K || K > kMaxSelectK, NVFP4_ERR_SHAPE);
   NV_RETURN_IF(n_select > 0 && !selected, NVFP4_ERR_NULL);
-  NV_RETURN_IF(!nv_aligned16(codes) || !nv_aligned16(res_codes) ||
-                   (reinterpret_cast<uintptr_t>(channel_score) & 7),
+  NV_RETURN_IF(!nv_aligned16(res_codes) || (reinterpret_cast<uintptr_t>(channel_score) & 7) ||
+                   (reinterpret_cast<uintptr_t>(channel_max) & 3),
                NVFP4_ERR_ALIGN);
   NV_RETURN_IF(!ws || ws_bytes < rac_select_residual_workspace_size(rows, K) ||
-                   (reinterpret_cast<uintptr_t>(ws) & 1),
+                   (reinterpret_cast<uintptr_t>(ws) & 3),
                NVFP4_ERR_WORKSPACE);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  uint16_t* mask16 = reinterpret_cast<uint16_t*>(ws);
-  hipLaunchKernelGGL(k_select, dim3(1), dim3(kSelThreads), 0, s, channel_score,
+  const RacWs L = rac_ws_layout(K);
+  unsigned char* base = reinterpret_cast<unsigned char*>(ws);
+  uint16_t* mask16 = reinterpret_cast<uint16_t*>(base + L.mask_off);
+  uint32_t* part_max = reinterpret_cast<uint32_t*>(base + L.max_off);
+  const int nrank = (int)((K + 63) / 64);
+  hipLaunchKernelGGL(k_rank, dim3(nrank), dim3(64 * kRankWaves), 0, s, channel_score,
                      reinterpret_cast<const uint32_t*>(channel_max), (int)K, (int)n_select,
-                     selected, kblock_active, mask16, res_tensor_scale);
+                     mask16, kblock_active, part_max);
   st = nv_launch_status();
   if (st) return st;
+  // at least one workgroup: it also writes selected[] and the tensor scale
   const int64_t nblk = rows * (K / 16);
   hipLaunchKernelGGL(k_residual, dim3((unsigned)blocks_for(nblk, kThreads, 8192)), dim3(kThreads),
-                     0, s, x, dtype == NVFP4_IN_BF16, rows, K, ldx, codes, scales, tensor_scale,
-                     mask16, res_tensor_scale, res_codes, res_scales);
+                     0, s, x, dtype == NVFP4_IN_BF16, rows, K, ldx, scales, tensor_scale, mask16,
+                     part_max, nrank, selected, res_tensor_scale, res_codes, res_scales);
   return nv_launch_status();
 }
 

@@ -82,7 +82,9 @@ def test_rac_validation(lib):
     assert call(K=16 * 1024 * 2, ldx=16 * 1024 * 2) == ESHAPE
     assert call(sel=None) == ENULL
     assert call(rc=FAKE_MIS) == EALIGN
+    assert call(scales=None) == ENULL
     assert call(ws=None) == EWS
+    assert call(wsb=64) == EWS
 
 
 def test_route_validation(lib):

@@ -63,6 +63,42 @@ def test_quant_rac_ties_and_zero(orc):
     check_quant_rac(orc, x, "f32", 50)
 
 
+@pytest.mark.parametrize("K,n_sel,kind", [(2048, 1024, "ties"), (768, 384, "huge"),
+                                           (16384, 8192, "ties"), (4112, 1, "huge"),
+                                           (4096, 4095, "zeros"), (1024, 512, "equal")])
+def test_select_crafted_scores(orc, K, n_sel, kind):
+    """Selection on hand-made int64 scores (heavy ties, values near 2^63,
+    all-zero, all-equal) against the oracle's sort; the residual uses the
+    real per-channel max |e|, so its bytes are checked as well."""
+    say(f"select crafted {kind} K={K} n_sel={n_sel}")
+    rng = np.random.default_rng(K + n_sel)
+    x = D.bf16_to_f32(D.bf16_bits(rng.standard_normal((3, K)).astype(np.float32)))
+    xd = to_dev(x, "bf16")
+    qo = L.nvfp4_quantize(xd, stats=True)
+    if kind == "ties":
+        score = rng.integers(0, 5, K).astype(np.int64) << 40
+    elif kind == "huge":
+        score = (np.int64(2 ** 62) + rng.integers(0, 2 ** 61, K)).astype(np.int64)
+        score[rng.integers(0, K, K // 8)] = np.iinfo(np.int64).max
+        score[rng.integers(0, K, K // 8)] = 0
+    elif kind == "zeros":
+        score = np.zeros(K, np.int64)
+    else:
+        score = np.full(K, 123456789, np.int64)
+    chmax = host(qo.channel_max)
+    qo2 = L.QuantOut(qo.q, torch.from_numpy(score).to(DEV), qo.channel_max)
+    rac = L.rac_select_residual(xd, qo2, n_sel)
+    sel, mask, active, s_tr = orc.rac_select(score, chmax, n_sel)
+    eq(host(rac.selected), sel, "selected")
+    eq(host(rac.kblock_active), active, "kblock_active")
+    eq(host(rac.r.tscale)[0], np.float32(s_tr), "residual tensor scale")
+    rc, rs, s_tr_r, _ = orc.rac_residual(x, host(qo.q.codes), host(qo.q.scales),
+                                         float(host(qo.q.tscale)[0]), mask)
+    assert np.float32(s_tr_r) == np.float32(s_tr)
+    eq(host(rac.r.scales), rs, "residual scales")
+    eq(host(rac.r.codes), rc, "residual codes")
+
+
 def test_quant_amax_in_and_stride(orc):
     say("quant with amax_in and padded rows")
     rng = np.random.default_rng(78)
