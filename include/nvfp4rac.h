@@ -187,7 +187,7 @@ typedef struct {
   int64_t N;                    /* output columns (2I for SILU_MUL) */
   int64_t K;                    /* contraction length */
   int64_t total_rows;           /* rows of the grouped output */
-  const int32_t* group_offsets; /* [G+1] */
+  const int32_t* group_offsets; /* [G+1], ascending, [0] = 0, [G] = total_rows */
   const int32_t* gather_rows;   /* [total_rows] or NULL (identity) */
   const uint8_t* a_codes;       /* [src_rows, K/2] */
   const uint8_t* a_scales;      /* [src_rows, K/16] */

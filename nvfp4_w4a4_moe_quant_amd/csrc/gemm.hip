@@ -691,6 +691,143 @@ int launch_t(GemmParams& p, hipStream_t s) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode-shaped GEMM: one group and few rows (a 16 x 4096 x 4096 linear layer
+// is the model case).  There the 64 x 128 prefill tiles would make only N/128
+// workgroups, and those few CUs would have to stream all of W.  Here a
+// workgroup owns 16 output columns and one 16-row tile over the whole of K:
+// N/16 workgroups stream W exactly once, and every lane issues all of its
+// loads for a pass before the first use, so each workgroup pays about one
+// memory latency.  v_mfma_f32_16x16x32_f16 matches the 16-row shape.  The
+// four waves split K and add their accumulators through LDS in a fixed
+// order.  A and R (a few KiB per row) are read by every workgroup from L2.
+//
+// k layout: a 128-k group is split into four 32-k quarters, one per 16-lane
+// quarter of the wave; the quarter's 32 contiguous k (16 code bytes, two
+// scale blocks) feed four MFMA steps of 8 k each.  The same permutation of k
+// is applied to A, R and W, so the contraction is unchanged.
+typedef float float4v __attribute__((ext_vector_type(4)));
+constexpr int kGvGroups = 8;      // 128-k groups per wave per load pass
+constexpr int kGvMaxRows = 64;    // rows up to which the decode kernel is used
+
+// WAVES waves split K (K % (128 * WAVES) == 0).  The only device values the
+// loads wait for are the gather indices; the group spans rows [0, total_rows)
+// (offsets[0] == 0, offsets[1] == total_rows).
+template <int WAVES, bool RAC, bool GATHER>
+__global__ __launch_bounds__(64 * WAVES) void k_gemv16(GemmParams p) {
+  __shared__ float4v red[WAVES][2][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // K slice of this wave, rotated by the workgroup id so that the workgroups
+  // (which all read the same A and R rows) spread over different lines
+  const int w = (wave + (int)blockIdx.x) % WAVES;
+  const int c = lane & 15, q = lane >> 4;
+  const int K = p.K;
+  const int kw = K / WAVES;  // k per wave
+  const float s_ta = *p.a_ts;
+  const float s_tr = RAC ? *p.r_ts : 0.0f;
+  const float s_tw = p.w_ts[0];
+  const int m = (int)blockIdx.y * 16 + c;  // A row fed by this lane
+  const bool mv = m < p.total_rows;
+  const int64_t n = (int64_t)blockIdx.x * 16 + c;   // W row fed by this lane
+  const uint8_t* wc = p.w_codes + n * (K >> 1);
+  const uint8_t* wsc = p.w_scales + n * (K >> 4);
+
+  float4v accm = {0.0f, 0.0f, 0.0f, 0.0f}, accr = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int g0 = 0; g0 < kw; g0 += 128 * kGvGroups) {
+    const int ng = (kw - g0) / 128 < kGvGroups ? (kw - g0) / 128 : kGvGroups;
+    uint4 wv[kGvGroups], av[kGvGroups], rv[kGvGroups];
+    uint32_t wsv[kGvGroups], asv[kGvGroups], rsv[kGvGroups];
+#pragma unroll
+    for (int g = 0; g < kGvGroups; ++g) {
+      const int kb = w * kw + g0 + g * 128 + q * 32;
+      wv[g] = make_uint4(0u, 0u, 0u, 0u);
+      wsv[g] = 0u;
+      if (g < ng) {
+        wv[g] = *reinterpret_cast<const uint4*>(wc + (kb >> 1));
+        wsv[g] = *reinterpret_cast<const uint16_t*>(wsc + (kb >> 4));
+      }
+    }
+    const int64_t src = mv ? (GATHER ? (int64_t)p.gather[m] : (int64_t)m) : 0;
+    const uint8_t* ac = p.a_codes + src * (K >> 1);
+    const uint8_t* asc = p.a_scales + src * (K >> 4);
+    const uint8_t* rc = RAC ? p.r_codes + src * (K >> 1) : nullptr;
+    const uint8_t* rsc = RAC ? p.r_scales + src * (K >> 4) : nullptr;
+#pragma unroll
+    for (int g = 0; g < kGvGroups; ++g) {
+      const int kb = w * kw + g0 + g * 128 + q * 32;
+      av[g] = rv[g] = make_uint4(0u, 0u, 0u, 0u);
+      asv[g] = rsv[g] = 0u;
+      if (g < ng && mv) {
+        av[g] = *reinterpret_cast<const uint4*>(ac + (kb >> 1));
+        asv[g] = *reinterpret_cast<const uint16_t*>(asc + (kb >> 4));
+        if constexpr (RAC) {
+          rv[g] = *reinterpret_cast<const uint4*>(rc + (kb >> 1));
+          rsv[g] = *reinterpret_cast<const uint16_t*>(rsc + (kb >> 4));
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < kGvGroups; ++g) {
+      if (g >= ng) break;
+      const half2v sw = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wsv[g], 1.0f, false);
+      const half2v sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(asv[g], 1.0f, false);
+      half2v sr = sa;
+      if constexpr (RAC) sr = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rsv[g], 1.0f, false);
+      const uint32_t wword[4] = {wv[g].x, wv[g].y, wv[g].z, wv[g].w};
+      const uint32_t aword[4] = {av[g].x, av[g].y, av[g].z, av[g].w};
+      const uint32_t rword[4] = {rv[g].x, rv[g].y, rv[g].z, rv[g].w};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int hi = st >> 1;  // steps 0-1: first block, 2-3: second
+        const half2v s_w = hi ? __builtin_shufflevector(sw, sw, 1, 1)
+                              : __builtin_shufflevector(sw, sw, 0, 0);
+        const half2v s_a = hi ? __builtin_shufflevector(sa, sa, 1, 1)
+                              : __builtin_shufflevector(sa, sa, 0, 0);
+        const half8 bw = dequant8(wword[st], s_w);
+        const half8 ba = dequant8(aword[st], s_a);
+        accm = __builtin_amdgcn_mfma_f32_16x16x32_f16(ba, bw, accm, 0, 0, 0);
+        if constexpr (RAC) {
+          const half2v s_r = hi ? __builtin_shufflevector(sr, sr, 1, 1)
+                                : __builtin_shufflevector(sr, sr, 0, 0);
+          const half8 br = dequant8(rword[st], s_r);
+          accr = __builtin_amdgcn_mfma_f32_16x16x32_f16(br, bw, accr, 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  red[w][0][lane] = accm;
+  red[w][1][lane] = accr;
+  __syncthreads();
+  if (wave != 0) return;
+  float4v sm = red[0][0][lane], sr = red[0][1][lane];
+#pragma unroll
+  for (int i = 1; i < WAVES; ++i) {
+    sm += red[i][0][lane];
+    sr += red[i][1][lane];
+  }
+  float* out = reinterpret_cast<float*>(p.out);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (int)blockIdx.y * 16 + 4 * q + i;  // D row of element i
+    if (row < p.total_rows) {
+      float y = s_ta * sm[i];
+      if constexpr (RAC) y = y + s_tr * sr[i];
+      out[(int64_t)row * p.N + n] = s_tw * y;
+    }
+  }
+}
+
+template <bool RAC, bool GATHER>
+int launch_gemv(GemmParams& p, hipStream_t s) {
+  const dim3 grid((unsigned)(p.N / 16), (unsigned)((p.total_rows + 15) / 16));
+  if (p.K % 1024 == 0)
+    hipLaunchKernelGGL((k_gemv16<8, RAC, GATHER>), grid, dim3(512), 0, s, p);
+  else
+    hipLaunchKernelGGL((k_gemv16<4, RAC, GATHER>), grid, dim3(256), 0, s, p);
+  return nv_launch_status();
+}
+
 // Tile configurations (rows x cols per workgroup, waves, LDS stages, min waves
 // per SIMD, residual step skipping).  The default, 64 x 128 with 2 x 2 waves of
 // 32 x 64, fits 128 VGPRs and runs four waves per SIMD; MoE groups of ~256 rows
@@ -771,8 +908,13 @@ int w4a4_grouped_gemm_rac(const w4a4_gemm_args_t* a, void*, size_t, void* stream
   p.out = a->out;
   p.out_amax = a->epilogue == NVFP4_EPI_SILU_MUL_BF16 ? a->out_amax : nullptr;
   p.skip = (a->flags & NVFP4_GEMM_SKIP_INACTIVE_BLOCKS) && a->kblock_active ? 1 : 0;
-  return launch(p, a->r_codes != nullptr, a->epilogue == NVFP4_EPI_SILU_MUL_BF16,
-                a->gather_rows != nullptr, s);
+  const bool rac = a->r_codes != nullptr, gather = a->gather_rows != nullptr;
+  if (p.G == 1 && p.total_rows <= kGvMaxRows && p.K % 512 == 0 &&
+      a->epilogue == NVFP4_EPI_F32) {
+    if (rac) return gather ? launch_gemv<true, true>(p, s) : launch_gemv<true, false>(p, s);
+    return gather ? launch_gemv<false, true>(p, s) : launch_gemv<false, false>(p, s);
+  }
+  return launch(p, rac, a->epilogue == NVFP4_EPI_SILU_MUL_BF16, gather, s);
 }
 
 }  // extern "C"

@@ -271,6 +271,7 @@ __global__ __launch_bounds__(64 * kRankWaves) void k_rank(
     }
     {
       const int b = j0 > d0 ? j0 : d0, e = j1 < d1 ? j1 : d1;
+#pragma unroll 8
       for (int j = b; j < e; ++j) {
         const uint64_t sj = tile[j - t0];
         c += (sj > sk || (sj == sk && j < k)) ? 1u : 0u;

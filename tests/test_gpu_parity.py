@@ -200,6 +200,47 @@ def test_dense_ragged(orc, rows, K, N):
     assert err <= REL_F
 
 
+def _nv(orc_triple):
+    """Oracle NVFP4 (codes, scales, s_t) -> device NVFP4."""
+    c, sc, t = orc_triple
+    return L.NVFP4(torch.from_numpy(np.ascontiguousarray(c)).to(DEV),
+                   torch.from_numpy(np.ascontiguousarray(sc)).to(DEV),
+                   torch.tensor([t], dtype=torch.float32, device=DEV))
+
+
+@pytest.mark.parametrize("rows,K,N,rac,gather", [
+    (16, 4096, 256, True, False), (1, 512, 128, True, False), (5, 1536, 128, False, False),
+    (33, 1024, 256, True, True), (64, 2048, 384, True, False), (17, 512, 128, False, True),
+    (65, 512, 128, True, False)])
+def test_decode_shaped_gemm(orc, rows, K, N, rac, gather):
+    """One group with few rows (the decode kernel below 65 rows when K % 512
+    == 0; 65 rows takes the prefill kernel), with and without RAC and a row
+    gather, against the oracle GEMM on oracle-quantized operands."""
+    say(f"decode gemm {rows}x{K}x{N} rac={rac} gather={gather}")
+    rng = np.random.default_rng(rows * 31 + K + N)
+    src = rows + 3 if gather else rows
+    x = D.bf16_to_f32(D.bf16_bits(rng.standard_normal((src, K)).astype(np.float32)))
+    x[:, rng.integers(0, K, 4)] *= 30.0
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    d = orc.quantize_rac(x, K // 2)
+    a = (d["codes"], d["scales"], d["s_t"])
+    r = (d["res_codes"], d["res_scales"], d["s_tr"]) if rac else None
+    wc, ws, wt = orc.quantize(W)
+    w = (wc[None], ws[None], np.array([wt], np.float32))
+    g = rng.permutation(src)[:rows].astype(np.int32) if gather else None
+    offsets = np.array([0, rows], np.int32)
+    y_ref = orc.grouped_gemm(N, K, offsets, g, a, r, w)
+    y = L.w4a4_grouped_gemm_rac(
+        _nv(a), L.NVFP4(torch.from_numpy(w[0]).to(DEV), torch.from_numpy(w[1]).to(DEV),
+                        torch.from_numpy(w[2]).to(DEV)),
+        torch.from_numpy(offsets).to(DEV), N=N, K=K, total_rows=rows,
+        gather_rows=None if g is None else torch.from_numpy(g).to(DEV),
+        r=_nv(r) if rac else None)
+    err = rel_frob(host(y), y_ref)
+    say(f"  rel frob {err:.3e}")
+    assert err <= REL_F
+
+
 def test_gemm_onehot_reads_dequantized_weights(orc):
     """A = one-hot rows (value 1 at k = i): y[i, n] = s_ta * s_tw * W_deq[n, i]."""
     say("gemm one-hot")
