@@ -184,13 +184,31 @@ def main():
         "config": cfg,
         "roofline": {"bound": "mfma", "kernel": dom["name"], "achieved": round(ach, 3),
                      "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / PEAK_F16_TFLOPS, 4), "traffic": None},
+                     "frac": round(ach / PEAK_F16_TFLOPS, 4),
+                     "traffic": measured_traffic(w.name) if w.kind == "moe" else None},
         "breakdown": res,
         "setup_s": round(t_setup, 1),
     }
     if args.cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, x_np, args.cpu_sample_experts, rac)
     print(json.dumps(line), flush=True)
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per launch of the gate/up GEMM from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by a copy-kernel
+    calibration), or None when there is none for this workload or the GEMM
+    source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"gemm_gate_up_{workload_name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src) or \
+            hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+        return None
+    return int(round(rec["hbm_bytes"]))
 
 
 def cpu_baseline(w, x_np, n_experts, rac):

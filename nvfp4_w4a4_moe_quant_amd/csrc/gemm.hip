@@ -844,6 +844,9 @@ int launch_cfg(GemmParams& p, hipStream_t s) {
     case 1: return launch_t<128, 128, 2, 2, 2, 2, RAC, SILU, GATHER, false>(p, s);
     case 2: return launch_t<128, 128, 2, 2, 3, 1, RAC, SILU, GATHER, false>(p, s);
     case 3: return launch_t<64, 256, 1, 4, 2, 2, RAC, SILU, GATHER, false>(p, s);
+    case 4: return launch_t<128, 128, 4, 1, 2, 2, RAC, SILU, GATHER, false>(p, s);
+    case 5: return launch_t<64, 256, 2, 2, 2, 2, RAC, SILU, GATHER, false>(p, s);
+    case 6: return launch_t<128, 128, 4, 1, 3, 1, RAC, SILU, GATHER, false>(p, s);
     case 10: return launch3<128, 128, 2, 2, 1, RAC, SILU, GATHER>(p, s);
     case 11: return launch3<128, 256, 2, 4, 1, RAC, SILU, GATHER>(p, s);
     default: return launch_t<64, 128, 2, 2, 2, 2, RAC, SILU, GATHER, false>(p, s);
