@@ -230,13 +230,14 @@ __global__ __launch_bounds__(kQThreads) void k_quant(
 //   rank_k = #{j : s_j > s_k} + #{j < k : s_j == s_k},
 // is below n_sel: exactly the first n_sel channels of that order.  The ranks
 // are counted directly, which needs no sort and no serial passes.
-// k_rank: workgroup b ranks channels 64b .. 64b+63 (one per lane); its 16
-// waves split the j range and walk their part of the scores with uniform
-// loads; the partial counts are summed in LDS.  Per workgroup it also writes
-// the selection bytes, the 16-channel block masks and activity flags of its
-// four blocks, and the max |e| over its selected channels.
+// k_rank: workgroup b ranks the 16 channels of block b.  Lane l of wave w
+// holds channel 16b + l % 16 and counts over part 4w + l / 16 of the 64
+// parts of the j range, reading the scores from LDS tiles; the 64 partial
+// counts of a channel are summed in LDS.  The workgroup also writes the
+// block's mask, its activity flag and the max |e| over its selected channels.
 constexpr int kRankWaves = 16;
-constexpr int kRankTile = 4096;  // keys staged in LDS per pass (32 KiB)
+constexpr int kRankParts = 4 * kRankWaves;  // j parts per channel
+constexpr int kRankTile = 4096;             // scores staged in LDS per pass (32 KiB)
 constexpr int kSelThreads = 1024;
 constexpr int kMaxSelectK = 16384;
 
@@ -244,14 +245,14 @@ __global__ __launch_bounds__(64 * kRankWaves) void k_rank(
     const int64_t* __restrict__ score_in, const uint32_t* __restrict__ chmax, int K, int n_sel,
     uint16_t* __restrict__ mask16, uint8_t* __restrict__ kact, uint32_t* __restrict__ part_max) {
   __shared__ uint64_t tile[kRankTile];
-  __shared__ uint32_t cnt[kRankWaves][64];
+  __shared__ uint32_t cnt[kRankParts][16];
   const uint64_t* score = reinterpret_cast<const uint64_t*>(score_in);
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int k0 = blockIdx.x * 64;
-  const int k = k0 + lane;
-  const uint64_t sk = k < K ? score[k] : ~0ull;
-  const int d0 = k0, d1 = k0 + 64 < K ? k0 + 64 : K;  // this workgroup's own channels
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int part = 4 * w + (lane >> 4);
+  const int k0 = blockIdx.x * 16;
+  const int k = k0 + (lane & 15);  // K % 16 == 0: always a valid channel
+  const uint64_t sk = score[k];
+  const int d0 = k0, d1 = k0 + 16;  // this workgroup's own channels
 
   uint32_t c = 0;
   for (int t0 = 0; t0 < K; t0 += kRankTile) {
@@ -260,9 +261,9 @@ __global__ __launch_bounds__(64 * kRankWaves) void k_rank(
 #pragma unroll 4
     for (int i = threadIdx.x; i < n; i += 64 * kRankWaves) tile[i] = score[t0 + i];
     __syncthreads();
-    // this wave's share of the tile, split where the tie rule changes
-    const int per = (n + kRankWaves - 1) / kRankWaves;
-    const int j0 = t0 + w * per;
+    // this lane's part of the tile, split where the tie rule changes
+    const int per = (n + kRankParts - 1) / kRankParts;
+    const int j0 = t0 + part * per < t0 + n ? t0 + part * per : t0 + n;
     const int j1 = j0 + per < t0 + n ? j0 + per : t0 + n;
     {  // j below every channel of this workgroup: a tie ranks j first
       const int e = j1 < d0 ? j1 : d0;
@@ -270,33 +271,31 @@ __global__ __launch_bounds__(64 * kRankWaves) void k_rank(
       for (int j = j0; j < e; ++j) c += tile[j - t0] >= sk ? 1u : 0u;
     }
     {
-      const int b = j0 > d0 ? j0 : d0, e = j1 < d1 ? j1 : d1;
-#pragma unroll 8
-      for (int j = b; j < e; ++j) {
+      const int bj = j0 > d0 ? j0 : d0, e = j1 < d1 ? j1 : d1;
+      for (int j = bj; j < e; ++j) {
         const uint64_t sj = tile[j - t0];
         c += (sj > sk || (sj == sk && j < k)) ? 1u : 0u;
       }
     }
     {  // j above every channel of this workgroup: a tie ranks j after
-      const int b = j0 > d1 ? j0 : d1;
+      const int bj = j0 > d1 ? j0 : d1;
 #pragma unroll 8
-      for (int j = b; j < j1; ++j) c += tile[j - t0] > sk ? 1u : 0u;
+      for (int j = bj; j < j1; ++j) c += tile[j - t0] > sk ? 1u : 0u;
     }
   }
-  cnt[w][lane] = c;
+  cnt[part][lane & 15] = c;
   __syncthreads();
   if (w == 0) {
     uint32_t rank = 0;
-#pragma unroll
-    for (int i = 0; i < kRankWaves; ++i) rank += cnt[i][lane];
-    const bool s = k < K && rank < (uint32_t)n_sel;
-    const uint64_t m = __ballot(s);
-    if (lane < 4 && k0 + 16 * lane < K) {
-      const uint32_t bits = (uint32_t)(m >> (16 * lane)) & 0xFFFFu;
-      mask16[blockIdx.x * 4 + lane] = (uint16_t)bits;
-      kact[blockIdx.x * 4 + lane] = bits ? 1 : 0;
+    if (lane < 16)
+      for (int i = 0; i < kRankParts; ++i) rank += cnt[i][lane];
+    const bool sel = lane < 16 && rank < (uint32_t)n_sel;
+    const uint32_t bits = (uint32_t)__ballot(sel) & 0xFFFFu;
+    if (lane == 0) {
+      mask16[blockIdx.x] = (uint16_t)bits;
+      kact[blockIdx.x] = bits ? 1 : 0;
     }
-    const float a = nv_wave_max(s ? __uint_as_float(chmax[k]) : 0.0f);
+    const float a = nv_wave_max(sel ? __uint_as_float(chmax[k]) : 0.0f);
     if (lane == 0) part_max[blockIdx.x] = __float_as_uint(a);
   }
 }
@@ -516,7 +515,7 @@ int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ld
 }
 
 // Workspace of rac_select_residual: block masks [K/16] u16, then the
-// per-workgroup max |e| of the selected channels [ceil(K/64)] u32.
+// per-block max |e| of the selected channels [K/16] u32.
 struct RacWs {
   size_t mask_off, max_off, total;
 };
@@ -525,7 +524,7 @@ static RacWs rac_ws_layout(int64_t K) {
   const size_t k = (size_t)(K > 0 ? K : 0);
   w.mask_off = 0;
   w.max_off = nv_round256(sizeof(uint16_t) * (k / 16));
-  w.total = w.max_off + nv_round256(sizeof(uint32_t) * ((k + 63) / 64));
+  w.total = w.max_off + nv_round256(sizeof(uint32_t) * (k / 16));
   return w;
 }
 
@@ -557,7 +556,7 @@ int rac_select_residual(const void* x, int dtype, int64_t rows, int64_t K, int64
   unsigned char* base = reinterpret_cast<unsigned char*>(ws);
   uint16_t* mask16 = reinterpret_cast<uint16_t*>(base + L.mask_off);
   uint32_t* part_max = reinterpret_cast<uint32_t*>(base + L.max_off);
-  const int nrank = (int)((K + 63) / 64);
+  const int nrank = (int)(K / 16);
   hipLaunchKernelGGL(k_rank, dim3(nrank), dim3(64 * kRankWaves), 0, s, channel_score,
                      reinterpret_cast<const uint32_t*>(channel_max), (int)K, (int)n_select,
                      mask16, kblock_active, part_max);
