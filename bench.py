@@ -162,12 +162,31 @@ def main():
         f = 2.0 * w.rows * w.N * (w.K + 16 * bx)
         t_q, t_g = seg(0), seg(1)
         flops = f
-        dom = dict(name="w4a4_grouped_gemm_rac dense", flops=f, ms=t_g)
-        res.update(quant_x=dict(us=t_q * 1e3), gemm=dict(us=t_g * 1e3, tflops=f / t_g / 1e9))
+        # bytes the GEMM must move: W codes + scales, A and R codes + scales,
+        # FP32 output (the decode shape is bound by streaming W from HBM)
+        nv = lambda r, k: r * k // 2 + r * k // 16
+        g_bytes = nv(w.N, w.K) + (2 if rac else 1) * nv(w.rows, w.K) + 4 * w.rows * w.N
+        dom = dict(name="w4a4_grouped_gemm_rac dense", flops=f, ms=t_g, bytes=g_bytes)
+        q_bytes = w.rows * w.K * (2 if w.x_dtype == "bf16" else 4) + \
+            (2 if rac else 1) * nv(w.rows, w.K)
+        res.update(quant_x=dict(us=t_q * 1e3, bytes=q_bytes, gbs=q_bytes / t_q / 1e6),
+                   gemm=dict(us=t_g * 1e3, tflops=f / t_g / 1e9, bytes=g_bytes,
+                             gbs=g_bytes / t_g / 1e6,
+                             frac_hbm=g_bytes / t_g / 1e6 / PEAK_HBM_GBS))
         cfg = dict(workload=w.name, rows=w.rows, K=w.K, N=w.N, rac=rac, n_select_x=nsx)
 
     value = flops / (ms_step * 1e-3) / 1e12
-    ach = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
+    if "bytes" in dom:  # HBM-bound (decode shape): GB/s on the bytes the GEMM must move
+        ach = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": dom["name"], "achieved": round(ach, 3),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                    "traffic": None}
+    else:
+        ach = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom["name"], "achieved": round(ach, 3),
+                    "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / PEAK_F16_TFLOPS, 4),
+                    "traffic": measured_traffic(w.name)}
     line = {
         "metric": "NVFP4 W4A4+RAC MoE grouped GEMM TFLOP/s (whole step, algorithmic flops)",
         "value": round(value, 3),
@@ -182,10 +201,7 @@ def main():
         "dtype": "f16",
         "data": "synthetic (seeded; bf16 activations, N(0,0.02) weights pre-quantized to NVFP4)",
         "config": cfg,
-        "roofline": {"bound": "mfma", "kernel": dom["name"], "achieved": round(ach, 3),
-                     "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / PEAK_F16_TFLOPS, 4),
-                     "traffic": measured_traffic(w.name) if w.kind == "moe" else None},
+        "roofline": roofline,
         "breakdown": res,
         "setup_s": round(t_setup, 1),
     }

@@ -34,13 +34,22 @@ __global__ __launch_bounds__(kThreads) void k_amax(const void* __restrict__ x, i
   const int64_t cb_per_row = K >> 4;
   const int64_t nblk = rows * cb_per_row;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
+  // (row, block) advance incrementally: one 64-bit division per thread
+  const int64_t srow = stride / cb_per_row, scb = stride - srow * cb_per_row;
+  int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  int64_t r = b / cb_per_row, cb = b - r * cb_per_row;
   float m = 0.0f;
-  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += stride) {
-    const int64_t r = b / cb_per_row, cb = b - r * cb_per_row;
+  for (; b < nblk; b += stride) {
     float v[16];
     nv_load16(x, bf16, r * ldx + cb * 16, v);
 #pragma unroll
     for (int i = 0; i < 16; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(v[i]));
+    r += srow;
+    cb += scb;
+    if (cb >= cb_per_row) {
+      cb -= cb_per_row;
+      ++r;
+    }
   }
   if (score) {
     for (int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x; k < K; k += stride) {
@@ -376,16 +385,26 @@ __global__ __launch_bounds__(kThreads) void k_residual(
   const int64_t CB = K >> 4;
   const int64_t nblk = rows * CB;
   const float s_t = *tscale;
-  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk;
-       b += (int64_t)gridDim.x * kThreads) {
-    const int64_t r = b / CB, cb = b - r * CB;
-    const uint32_t m = mask16[cb];
+  // Blocks b = row * CB + cb, grid-stride; (row, cb) advance incrementally
+  // (one 64-bit division per thread), two blocks in flight per iteration.
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int64_t srow = stride / CB, scb = stride - srow * CB;
+  int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  int64_t r = b / CB, cb = b - r * CB;
+  auto advance = [&](int64_t& rr, int64_t& cc) {
+    rr += srow;
+    cc += scb;
+    if (cc >= CB) {
+      cc -= CB;
+      ++rr;
+    }
+  };
+  auto one = [&](int64_t rr, int64_t cc, const float* v) {
+    const uint32_t m = mask16[cc];
     uint32_t packed[2] = {0u, 0u};
     uint32_t sc = 0u;
     if (m) {
-      float v[16];
-      nv_load16(x, bf16, r * ldx + cb * 16, v);
-      const float sb = nv_e4m3_to_f32(scales[r * CB + cb]);
+      const float sb = nv_e4m3_to_f32(scales[rr * CB + cc]);
       const float rm = nv_block_recip(sb * s_t);
       float g[16], e[16];
       nv_decode8(nv_encode8(v, rm), g);
@@ -403,8 +422,21 @@ __global__ __launch_bounds__(kThreads) void k_residual(
       packed[0] = nv_encode8(e, rb);
       packed[1] = nv_encode8(e + 8, rb);
     }
-    *reinterpret_cast<uint2*>(res_codes + r * (K >> 1) + cb * 8) = make_uint2(packed[0], packed[1]);
-    res_scales[r * CB + cb] = (uint8_t)sc;
+    *reinterpret_cast<uint2*>(res_codes + rr * (K >> 1) + cc * 8) = make_uint2(packed[0], packed[1]);
+    res_scales[rr * CB + cc] = (uint8_t)sc;
+  };
+  for (; b < nblk; b += 2 * stride) {
+    int64_t r2 = r, cb2 = cb;
+    advance(r2, cb2);
+    const bool two = b + stride < nblk;
+    float v0[16], v1[16];
+    if (mask16[cb]) nv_load16(x, bf16, r * ldx + cb * 16, v0);
+    if (two && mask16[cb2]) nv_load16(x, bf16, r2 * ldx + cb2 * 16, v1);
+    one(r, cb, v0);
+    if (two) one(r2, cb2, v1);
+    r = r2;
+    cb = cb2;
+    advance(r, cb);
   }
 }
 
@@ -564,7 +596,7 @@ int rac_select_residual(const void* x, int dtype, int64_t rows, int64_t K, int64
   if (st) return st;
   // at least one workgroup: it also writes selected[] and the tensor scale
   const int64_t nblk = rows * (K / 16);
-  hipLaunchKernelGGL(k_residual, dim3((unsigned)blocks_for(nblk, kThreads, 8192)), dim3(kThreads),
+  hipLaunchKernelGGL(k_residual, dim3((unsigned)blocks_for(nblk, 2 * kThreads, 2048)), dim3(kThreads),
                      0, s, x, dtype == NVFP4_IN_BF16, rows, K, ldx, scales, tensor_scale, mask16,
                      part_max, nrank, selected, res_tensor_scale, res_codes, res_scales);
   return nv_launch_status();
