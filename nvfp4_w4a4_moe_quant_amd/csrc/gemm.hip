@@ -76,6 +76,12 @@ __device__ __forceinline__ half2v pick_scale(half2v s01, half2v s23, int blk) {
                   : __builtin_shufflevector(s23, s23, 1, 1);
 }
 
+// silu(g) * u in FP32 with the hardware exp and reciprocal (each within a few
+// FP32 ulp; the result is rounded to bf16, whose ulp is 2^16 times larger).
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 struct GemmParams {
@@ -378,20 +384,25 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
     if constexpr (RAC) y = y + s_tr * accr[a][b][e];
     return s_tw * y;
   };
+  // Element e of fragment (a, b) sits at row m0 + a*32 + (e>>2)*8 + (e&3) of
+  // the lane's column; the base pointer is formed once, and a wave whose 32
+  // x FM rows all lie inside the group stores without per-element checks.
+  const int m0 = row_beg + wm * WTM + lh * 4;
+  const bool full = row_beg + (wm + 1) * WTM <= row_end;  // wave-uniform
   if constexpr (!SILU) {
-    float* out = reinterpret_cast<float*>(p.out);
+    float* ob = reinterpret_cast<float*>(p.out) + (int64_t)m0 * p.N + nt * BN + wn * WTN + lr;
 #pragma unroll
     for (int a = 0; a < FM; ++a)
 #pragma unroll
       for (int b = 0; b < FN; ++b)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int m = row_beg + wm * WTM + a * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
-          const int n = nt * BN + wn * WTN + b * 32 + lr;
-          if (m < row_end) out[(int64_t)m * p.N + n] = yval(a, b, e);
+          const int dm = a * 32 + (e >> 2) * 8 + (e & 3);
+          if (full || m0 + dm < row_end) ob[(int64_t)dm * p.N + b * 32] = yval(a, b, e);
         }
   } else {
-    uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+    uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + (int64_t)m0 * I + nt * (BN / 2) +
+                   wn * (WTN / 2) + lr;
     float hmax = 0.0f;
 #pragma unroll
     for (int a = 0; a < FM; ++a)
@@ -399,13 +410,12 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
       for (int b = 0; b < FN; b += 2)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int m = row_beg + wm * WTM + a * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
-          const int hc = nt * (BN / 2) + wn * (WTN / 2) + (b >> 1) * 32 + lr;
-          if (m < row_end) {
+          const int dm = a * 32 + (e >> 2) * 8 + (e & 3);
+          if (full || m0 + dm < row_end) {
             const float g = yval(a, b, e), u = yval(a, b + 1, e);
-            const float hv = g / (1.0f + expf(-g)) * u;
+            const float hv = silu_mul(g, u);
             const uint32_t hb = nv_f32_to_bf16(hv);
-            out[(int64_t)m * I + hc] = (uint16_t)hb;
+            ob[(int64_t)dm * I + (b >> 1) * 32] = (uint16_t)hb;
             hmax = __builtin_fmaxf(hmax, __builtin_fabsf(nv_bf16_to_f32(hb)));
           }
         }
@@ -643,7 +653,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void k_gemm3(GemmPara
           const int hc = nt * (BN / 2) + wn * (WTN / 2) + (b >> 1) * 32 + lr;
           if (m < row_end) {
             const float g = yval(a, b, e), u = yval(a, b + 1, e);
-            const float hv = g / (1.0f + expf(-g)) * u;
+            const float hv = silu_mul(g, u);
             const uint32_t hb = nv_f32_to_bf16(hv);
             out[(int64_t)m * I + hc] = (uint16_t)hb;
             hmax = __builtin_fmaxf(hmax, __builtin_fabsf(nv_bf16_to_f32(hb)));

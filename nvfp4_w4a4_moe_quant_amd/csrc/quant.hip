@@ -350,9 +350,12 @@ __global__ __launch_bounds__(kThreads) void k_residual(
     float* __restrict__ res_ts, uint8_t* __restrict__ res_codes,
     uint8_t* __restrict__ res_scales) {
   __shared__ uint32_t wred[kThreads / 64];
+  __shared__ uint16_t lmask[kMaxSelectK / 16];  // block masks, so x loads wait on nothing
   float a = 0.0f;
-  for (int i = threadIdx.x; i < nparts; i += kThreads)
+  for (int i = threadIdx.x; i < nparts; i += kThreads) {  // nparts = K / 16 blocks
     a = __builtin_fmaxf(a, __uint_as_float(part_max[i]));
+    lmask[i] = mask16[i];
+  }
   a = nv_wave_max(a);
   if ((threadIdx.x & 63) == 0) wred[threadIdx.x >> 6] = __float_as_uint(a);
   __syncthreads();
@@ -400,7 +403,7 @@ __global__ __launch_bounds__(kThreads) void k_residual(
     }
   };
   auto one = [&](int64_t rr, int64_t cc, const float* v) {
-    const uint32_t m = mask16[cc];
+    const uint32_t m = lmask[cc];
     uint32_t packed[2] = {0u, 0u};
     uint32_t sc = 0u;
     if (m) {
@@ -430,8 +433,8 @@ __global__ __launch_bounds__(kThreads) void k_residual(
     advance(r2, cb2);
     const bool two = b + stride < nblk;
     float v0[16], v1[16];
-    if (mask16[cb]) nv_load16(x, bf16, r * ldx + cb * 16, v0);
-    if (two && mask16[cb2]) nv_load16(x, bf16, r2 * ldx + cb2 * 16, v1);
+    if (lmask[cb]) nv_load16(x, bf16, r * ldx + cb * 16, v0);
+    if (two && lmask[cb2]) nv_load16(x, bf16, r2 * ldx + cb2 * 16, v1);
     one(r, cb, v0);
     if (two) one(r2, cb2, v1);
     r = r2;
