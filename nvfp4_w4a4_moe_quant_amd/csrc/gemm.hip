@@ -22,8 +22,9 @@
 //    unchanged); each lane then reads 32 contiguous code bytes per row.
 //  * Tiles: (group, m-tile, n-tile) from the device-side group offsets; every
 //    workgroup finds its tile with a wave scan, tiles past the real count exit.
-//    Workgroup ids are remapped so that consecutive tiles (same expert, same
-//    rows) run on the same XCD and share its L2.
+//    Workgroup ids are remapped so that consecutive tiles run on the same XCD
+//    and share its L2; within an expert the m-tiles vary fastest, so the
+//    workgroups reading one W tile are adjacent.
 //  * Double-buffered LDS; 16-byte code pieces are XOR-swizzled per row so that
 //    the fragment reads of 8 (or 16) consecutive rows hit distinct banks.
 #include <stdlib.h>
@@ -130,10 +131,13 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
   const int bid = blockIdx.x;
   const int per = nblocks / 8, rem = nblocks % 8, xcd = bid % 8;
   const int L = xcd * per + (xcd < rem ? xcd : rem) + bid / 8;
-  const int mt = L / p.n_tiles, nt = L % p.n_tiles;
+  const int mt = L / p.n_tiles;
 
-  // ---- find the group that owns m-tile `mt` (a wave scan of per-group tiles)
-  int grp = -1, local = 0;
+  // ---- find the group that owns m-tile `mt` (a wave scan of per-group tiles).
+  // The group's workgroups form the range [first, first + tiles) * n_tiles of
+  // L; inside it the m-tiles vary fastest, so the m-tiles that share a W tile
+  // run next to each other (one fetch of the W tile serves them all).
+  int grp = -1, local = 0, nt = 0;
   {
     int run = 0;
     for (int c = 0; c < p.G; c += 64) {
@@ -152,7 +156,11 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
       if (bal) {
         const int hl = __ffsll((long long)bal) - 1;
         grp = c + hl;
-        local = mt - run - __shfl(excl, hl, 64);
+        const int first = run + __shfl(excl, hl, 64);
+        const int gt = __shfl(tiles, hl, 64);
+        const int i = L - first * p.n_tiles;
+        local = i % gt;
+        nt = i / gt;
         break;
       }
       run += __shfl(inc, 63, 64);
