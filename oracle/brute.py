@@ -190,3 +190,44 @@ def gemm(a, r, w, offsets, gather, N):
             row.append(wts * y)
         out.append(row)
     return out
+
+
+# --- FP8 W8A8 comparator -------------------------------------------------------
+def fp8_quantize_rows(x):
+    """Per-row E4M3 quantization: s = RN32(RN64(amax / 448)), r = RN32(RN64(1/s)),
+    code = sign(x) | nearest E4M3 of |RN32(x r)| (ties to the even byte,
+    saturating).  x: list of rows of Fractions; returns (code rows, scales)."""
+    codes, scales = [], []
+    for row in x:
+        amax = max((abs(v) for v in row), default=Fr(0))
+        s = rn32(rn64(Fr(amax) / 448))
+        r = rn32(rn64(1 / s)) if s > 0 else Fr(0)
+        crow = []
+        for v in row:
+            q = rn32(v * r)
+            crow.append((0x80 if v < 0 else 0) | e4m3_nearest(abs(q)))
+        codes.append(crow)
+        scales.append(s)
+    return codes, scales
+
+
+def fp8_value(b: int) -> Fr:
+    v = E4M3[b & 0x7F]
+    return -v if b & 0x80 else v
+
+
+def fp8_gemm(a_codes, a_scales, w, offsets, gather, N):
+    """Exact RN32 of s_a * s_w * sum_k A W as Fractions; w = list over groups of
+    (code rows [N], scales [N])."""
+    out = []
+    for j in range(offsets[-1]):
+        g = max(i for i in range(len(offsets) - 1) if offsets[i] <= j)
+        src = gather[j] if gather is not None else j
+        wc, wsc = w[g]
+        row = []
+        for n in range(N):
+            acc = sum(fp8_value(a_codes[src][k]) * fp8_value(wc[n][k])
+                      for k in range(len(wc[n])))
+            row.append(rn32(a_scales[src] * wsc[n] * acc))
+        out.append(row)
+    return out

@@ -534,3 +534,93 @@ void or_route(const float* logits, int64_t T, int64_t E, int64_t k,
   free(counts);
   free(keys);
 }
+
+/* ------------------------------------------------ FP8 W8A8 comparator */
+
+/* The pages measure QUADS against FP8 rollout (arXiv abstract; blog post,
+ * section "What it buys": about 16% higher rollout throughput than FP8) but
+ * do not say how the FP8 engine scales its tensors.  Reading: W8A8 with OCP
+ * E4M3 elements, one FP32 scale per activation row (token) and one per
+ * weight output channel, the usual dynamic per-token / static per-channel
+ * form, with the same rounding conventions as the NVFP4 quantizer above:
+ *   s = RN32(amax_row / 448)     (double quotient, rounded once)
+ *   r = RN32(1 / s)              (0 when s == 0)
+ *   code = sign(v) | E4M3(|v|),  v = RN32(x * r), nearest-even, saturating;
+ * the sign bit is that of v, so a negative value that rounds to zero keeps
+ * it (0x80).  A row of zeros gets s = 0 and zero codes. */
+float or_fp8_row_scale(float amax) {
+  return (float)((double)amax / 448.0);
+}
+
+int or_fp8_encode(float v) {
+  int c = or_e4m3_encode(fabsf(v));
+  return signbit(v) ? (0x80 | c) : c;
+}
+
+void or_fp8_quantize_rows(const float* x, int64_t rows, int64_t K, int64_t ldx,
+                          uint8_t* codes, float* scales) {
+  int64_t i;
+#pragma omp parallel for schedule(static)
+  for (i = 0; i < rows; i++) {
+    const float* xr = x + i * ldx;
+    float amax = 0.0f, s, r;
+    int64_t k;
+    for (k = 0; k < K; k++)
+      if (fabsf(xr[k]) > amax) amax = fabsf(xr[k]);
+    s = or_fp8_row_scale(amax);
+    r = (s > 0.0f) ? (float)(1.0 / (double)s) : 0.0f;
+    for (k = 0; k < K; k++) {
+      float v = xr[k] * r;
+      codes[i * K + k] = (uint8_t)or_fp8_encode(v);
+    }
+    scales[i] = s;
+  }
+}
+
+/* Exact integer image of an E4M3 byte: value * 2^9 (every E4M3 value is a
+ * multiple of 2^-9 and at most 448, so the image fits 18 bits). */
+static int32_t fp8_int(uint8_t b) {
+  return (int32_t)(or_e4m3_value(b) * 512.0);
+}
+
+/* FP8 grouped GEMM, the same grouping and gather as or_grouped_gemm:
+ *   Y[j, n] = RN32( s_a[src] * s_w[g*N + n] * sum_k A[src,k] W_g[n,k] )
+ * with the sum exact in int64 (images scaled by 2^-18) and the product formed
+ * in long double. */
+static float fp8_one(int64_t G, int64_t N, int64_t K, const int32_t* offsets,
+                     const int32_t* gather, const uint8_t* a_codes, const float* a_scales,
+                     const uint8_t* w_codes, const float* w_scales, int64_t j, int64_t n) {
+  int64_t g = group_of(offsets, G, j);
+  int64_t src = gather ? gather[j] : j;
+  const uint8_t* a = a_codes + src * K;
+  const uint8_t* w = w_codes + (g * N + n) * K;
+  int64_t acc = 0, k;
+  long double y;
+  for (k = 0; k < K; k++) acc += (int64_t)fp8_int(a[k]) * fp8_int(w[k]);
+  y = (long double)a_scales[src] * (long double)w_scales[g * N + n] *
+      ldexpl((long double)acc, -18);
+  return (float)y;
+}
+
+void or_fp8_grouped_gemm(int64_t G, int64_t N, int64_t K, int64_t total_rows,
+                         const int32_t* offsets, const int32_t* gather,
+                         const uint8_t* a_codes, const float* a_scales,
+                         const uint8_t* w_codes, const float* w_scales, float* out) {
+  int64_t idx;
+#pragma omp parallel for schedule(dynamic, 64)
+  for (idx = 0; idx < total_rows * N; idx++)
+    out[idx] = fp8_one(G, N, K, offsets, gather, a_codes, a_scales, w_codes, w_scales,
+                       idx / N, idx % N);
+}
+
+void or_fp8_grouped_gemm_sample(int64_t G, int64_t N, int64_t K, const int32_t* offsets,
+                                const int32_t* gather, const uint8_t* a_codes,
+                                const float* a_scales, const uint8_t* w_codes,
+                                const float* w_scales, int64_t n_samples,
+                                const int64_t* rows, const int64_t* cols, float* out) {
+  int64_t i;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (i = 0; i < n_samples; i++)
+    out[i] = fp8_one(G, N, K, offsets, gather, a_codes, a_scales, w_codes, w_scales,
+                     rows[i], cols[i]);
+}

@@ -63,6 +63,12 @@ _SIGS = {
     "or_bf16_rne": (ctypes.c_uint16, [ctypes.c_double]),
     "or_silu_mul": (None, [_P, _I64, _I64, _P, _P]),
     "or_route": (None, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "or_fp8_row_scale": (_F, [_F]),
+    "or_fp8_encode": (ctypes.c_int, [_F]),
+    "or_fp8_quantize_rows": (None, [_P, _I64, _I64, _I64, _P, _P]),
+    "or_fp8_grouped_gemm": (None, [_I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "or_fp8_grouped_gemm_sample": (None, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P,
+                                          _I64, _P, _P, _P]),
 }
 
 
@@ -245,6 +251,55 @@ def route(logits, k):
                    _p(row_of))
     return dict(topk_ids=ids, topk_weights=wts, offsets=off, gather=gather,
                 row_of=row_of)
+
+
+# ------------------------------------------------- FP8 W8A8 comparator
+def fp8_row_scale(amax: float) -> float:
+    return lib().or_fp8_row_scale(amax)
+
+
+def fp8_encode(v: float) -> int:
+    return lib().or_fp8_encode(v)
+
+
+def fp8_quantize_rows(x):
+    """x float32 [rows, K] -> (codes u8 [rows, K] E4M3, scales float32 [rows])."""
+    x = _c(x, np.float32)
+    rows, K = x.shape
+    codes = np.zeros((rows, K), np.uint8)
+    scales = np.zeros(rows, np.float32)
+    lib().or_fp8_quantize_rows(_p(x), rows, K, K, _p(codes), _p(scales))
+    return codes, scales
+
+
+def fp8_grouped_gemm(N, K, offsets, gather, a, w):
+    """a = (codes [src_rows, K], scales [src_rows]); w = (codes [G, N, K],
+    scales [G, N]); offsets int32 [G+1]; gather int32 [total_rows] or None."""
+    offsets = _c(offsets, np.int32)
+    G = offsets.shape[0] - 1
+    total = int(offsets[-1])
+    gather = None if gather is None else _c(gather, np.int32)
+    wc, ws = _c(w[0], np.uint8), _c(w[1], np.float32)
+    assert wc.shape == (G, N, K) and ws.shape == (G, N)
+    out = np.zeros((total, N), np.float32)
+    lib().or_fp8_grouped_gemm(G, N, K, total, _p(offsets), _p(gather),
+                              _p(_c(a[0], np.uint8)), _p(_c(a[1], np.float32)),
+                              _p(wc), _p(ws), _p(out))
+    return out
+
+
+def fp8_grouped_gemm_sample(N, K, offsets, gather, a, w, rows, cols):
+    offsets = _c(offsets, np.int32)
+    G = offsets.shape[0] - 1
+    gather = None if gather is None else _c(gather, np.int32)
+    rows = _c(rows, np.int64)
+    cols = _c(cols, np.int64)
+    out = np.zeros(rows.shape[0], np.float32)
+    lib().or_fp8_grouped_gemm_sample(G, N, K, _p(offsets), _p(gather),
+                                     _p(_c(a[0], np.uint8)), _p(_c(a[1], np.float32)),
+                                     _p(_c(w[0], np.uint8)), _p(_c(w[1], np.float32)),
+                                     rows.shape[0], _p(rows), _p(cols), _p(out))
+    return out
 
 
 # ------------------------------------------------------------- composites
