@@ -9,6 +9,11 @@ input already resident in HBM:
   dense workloads: nvfp4_quantize(X)+rac_select_residual(X) -> W4A4 GEMM
 Weights are quantized once before timing (offline, as in rollout).
 
+Comparators (timed after the main measurement, same inputs, same weights):
+the same path with RAC off (naive NVFP4 W4A4), and an FP8 (E4M3) W8A8 step
+with per-row activation and per-channel weight scales -- the format the pages
+compare QUADS's rollout throughput against.
+
 Prints one JSON line.  `value` is the algorithmic GEMM TFLOP/s of the whole
 step (main + residual passes of every GEMM, residual counted over the active
 K-blocks only) divided by the step time; `roofline` covers the dominant
@@ -30,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_F16_TFLOPS = 2516.6   # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5033.2   # MI355X dense fp8 MFMA
 
 
 def parse():
@@ -40,6 +46,13 @@ def parse():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-rac", action="store_true", help="naive W4A4 (RAC off)")
     ap.add_argument("--cpu-baseline", type=int, default=1)
+    ap.add_argument("--comparators", type=int, default=1,
+                    help="also time RAC-off NVFP4 and FP8 W8A8 steps")
+    ap.add_argument("--fp8-library-reference", type=int, default=0,
+                    help="also time the vendor FP8 GEMM (hipBLASLt through torch._scaled_mm, "
+                         "row/column scales, bf16 out) on the dense shape of each GEMM: a "
+                         "reference point for what an FP8 GEMM reaches on this chip, not a "
+                         "part of the path")
     ap.add_argument("--cpu-sample-experts", type=int, default=48)
     return ap.parse_args()
 
@@ -71,25 +84,42 @@ def main():
     x = to_dev(x_np, w.x_dtype)
     rac = not args.no_rac
     nsx = w.n_select_x if rac else None
+    cmp_ = bool(args.comparators)
+
+    def fp8_buf(G, N, K):
+        return L.FP8(torch.empty((G, N, K), dtype=torch.uint8, device=dev),
+                     torch.empty((G, N), dtype=torch.float32, device=dev)) if cmp_ else None
+
+    def tee(gen, dtype, f8):
+        """Upload each weight matrix once; FP8-quantize it for the comparator
+        while the NVFP4 quantizer takes it."""
+        for e, m in gen:
+            t = to_dev(m, dtype)
+            if f8 is not None:
+                L.fp8_quantize_rows(t, out=L.FP8(f8.codes[e], f8.scales[e]))
+            yield e, t
+
     if w.kind == "moe":
         lg_np = D.router_logits(w)
         lg = torch.from_numpy(lg_np).to(dev)
-        wgu = P.quantize_weights(((e, to_dev(m, "bf16")) for e, m in D.expert_weights(w, "gate_up")),
+        f8_gu, f8_d = fp8_buf(w.E, 2 * w.I, w.H), fp8_buf(w.E, w.H, w.I)
+        wgu = P.quantize_weights(tee(D.expert_weights(w, "gate_up"), "bf16", f8_gu),
                                  w.E, 2 * w.I, w.H, dev)
-        wd = P.quantize_weights(((e, to_dev(m, "bf16")) for e, m in D.expert_weights(w, "down")),
+        wd = P.quantize_weights(tee(D.expert_weights(w, "down"), "bf16", f8_d),
                                 w.E, w.H, w.I, dev)
         nsh = w.n_select_h if rac else None
         rows = w.T * w.topk
         amax_h = torch.zeros(1, dtype=torch.float32, device=dev)
     else:
-        wq = P.quantize_weights([(0, to_dev(D.dense_weight(w), w.x_dtype))], 1, w.N, w.K, dev)
+        f8_w = fp8_buf(1, w.N, w.K)
+        wq = P.quantize_weights(tee([(0, D.dense_weight(w))], w.x_dtype, f8_w), 1, w.N, w.K, dev)
         offs = torch.tensor([0, w.rows], dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
     t_setup = time.time() - t_setup
 
     NEV = 6 if w.kind == "moe" else 3
 
-    def step(ev):
+    def step(ev, nsx=nsx, nsh=nsh if w.kind == "moe" else None):
         if w.kind == "moe":
             amax_h.zero_()  # SiLU*mul epilogue max-combines into it
             ev[0].record()
@@ -112,19 +142,49 @@ def main():
         ev[2].record()
         return x_in, None, y, None
 
-    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(NEV)]
-    for _ in range(args.warmup):
-        out = step(mk())
-    torch.cuda.synchronize()
-    evs = [mk() for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        out = step(evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
+    def step_fp8(ev):
+        """FP8 W8A8 comparator: the same routing, per-row E4M3 activations."""
+        if w.kind == "moe":
+            ev[0].record()
+            rt = L.moe_route(lg, w.topk)
+            ev[1].record()
+            xq = L.fp8_quantize_rows(x)
+            ev[2].record()
+            h = L.fp8_grouped_gemm(xq, f8_gu, rt.expert_offsets, N=2 * w.I, K=w.H,
+                                   total_rows=rows, gather_rows=rt.gather_rows,
+                                   epilogue=L.NVFP4_EPI_SILU_MUL_BF16)
+            ev[3].record()
+            hq = L.fp8_quantize_rows(h)
+            ev[4].record()
+            y = L.fp8_grouped_gemm(hq, f8_d, rt.expert_offsets, N=w.H, K=w.I, total_rows=rows)
+            ev[5].record()
+            return y
+        ev[0].record()
+        xq = L.fp8_quantize_rows(x)
+        ev[1].record()
+        y = L.fp8_grouped_gemm(xq, f8_w, offs, N=w.N, K=w.K, total_rows=w.rows)
+        ev[2].record()
+        return y
 
-    def seg(i):  # mean ms of segment i over the timed steps
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(NEV)]
+
+    def timed(fn):
+        """W untimed steps, then K steps between synchronizations; returns the
+        last step's outputs, ms per step and the per-step events."""
+        for _ in range(args.warmup):
+            o = fn(mk())
+        torch.cuda.synchronize()
+        evs = [mk() for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            o = fn(evs[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return o, (t1 - t0) * 1e3 / args.steps, evs
+
+    out, ms_step, evs = timed(step)
+
+    def seg(i, evs=evs):  # mean ms of segment i over the timed steps
         return float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
 
     x_in, h_in, y, rt = out
@@ -176,6 +236,10 @@ def main():
         cfg = dict(workload=w.name, rows=w.rows, K=w.K, N=w.N, rac=rac, n_select_x=nsx)
 
     value = flops / (ms_step * 1e-3) / 1e12
+    if cmp_:
+        res["comparators"] = comparators(w, timed, step, step_fp8, seg, ms_step, rac, NEV)
+        if args.fp8_library_reference:
+            res["comparators"]["fp8_dense_library_reference"] = library_fp8_reference(w, dev)
     if "bytes" in dom:  # HBM-bound (decode shape): GB/s on the bytes the GEMM must move
         ach = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "kernel": dom["name"], "achieved": round(ach, 3),
@@ -208,6 +272,70 @@ def main():
     if args.cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, x_np, args.cpu_sample_experts, rac)
     print(json.dumps(line), flush=True)
+
+
+def comparators(w, timed, step, step_fp8, seg, ms_step, rac, nev):
+    """RAC-off NVFP4 and FP8 W8A8 steps on the same inputs and weights."""
+    out = {}
+    if rac:
+        _, ms_naive, ev_n = timed(lambda ev: step(ev, None, None))
+        gi = 2 if w.kind == "moe" else 1
+        out["nvfp4_rac_off"] = dict(ms_per_step=round(ms_naive, 4),
+                                    gemm_first_us=round(seg(gi, ev_n) * 1e3, 2),
+                                    rac_step_overhead=round(ms_step / ms_naive - 1.0, 4))
+    _, ms_f8, ev_f = timed(step_fp8)
+    if w.kind == "moe":
+        rows = w.T * w.topk
+        f_gu, f_d = 2.0 * rows * 2 * w.I * w.H, 2.0 * rows * w.H * w.I
+        t = [seg(i, ev_f) for i in range(nev - 1)]
+        out["fp8_w8a8"] = dict(
+            ms_per_step=round(ms_f8, 4), route_us=round(t[0] * 1e3, 2),
+            quant_x_us=round(t[1] * 1e3, 2), gemm_gate_up_us=round(t[2] * 1e3, 2),
+            gemm_gate_up_tflops=round(f_gu / t[2] / 1e9, 1),
+            gemm_gate_up_frac_fp8_mfma=round(f_gu / t[2] / 1e9 / PEAK_FP8_TFLOPS, 4),
+            quant_h_us=round(t[3] * 1e3, 2), gemm_down_us=round(t[4] * 1e3, 2),
+            gemm_down_tflops=round(f_d / t[4] / 1e9, 1),
+            nvfp4_rac_step_over_fp8_step=round(ms_step / ms_f8, 4))
+    else:
+        f = 2.0 * w.rows * w.N * w.K
+        t = [seg(i, ev_f) for i in range(nev - 1)]
+        out["fp8_w8a8"] = dict(ms_per_step=round(ms_f8, 4), quant_x_us=round(t[0] * 1e3, 2),
+                               gemm_us=round(t[1] * 1e3, 2),
+                               gemm_tflops=round(f / t[1] / 1e9, 1),
+                               nvfp4_rac_step_over_fp8_step=round(ms_step / ms_f8, 4))
+    return out
+
+
+def library_fp8_reference(w, dev):
+    """hipBLASLt's FP8 GEMM (torch._scaled_mm with per-row and per-column
+    scales, bf16 output) on the dense shape rows x N x K of each GEMM of the
+    workload: no grouping, no gather, one weight matrix."""
+    import torch
+    shapes = ([("gate_up", w.T * w.topk, 2 * w.I, w.H), ("down", w.T * w.topk, w.H, w.I)]
+              if w.kind == "moe" else [("gemm", w.rows, w.N, w.K)])
+    out = {}
+    for name, M, N, K in shapes:
+        a = (torch.randn(M, K, device=dev) * 0.5).to(torch.float8_e4m3fn)
+        b = (torch.randn(N, K, device=dev) * 0.5).to(torch.float8_e4m3fn)
+        sa = torch.ones((M, 1), device=dev)
+        sb = torch.ones((1, N), device=dev)
+        fn = lambda: torch._scaled_mm(a, b.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
+        try:
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / 20 * 1e3
+            out[name] = dict(shape=[M, N, K], us=round(us, 1),
+                             tflops=round(2.0 * M * N * K / us / 1e6, 1))
+        except Exception as ex:  # the library may lack a kernel for the shape
+            out[name] = dict(shape=[M, N, K], error=repr(ex)[:200])
+    return out
 
 
 def measured_traffic(workload_name):

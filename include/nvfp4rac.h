@@ -211,6 +211,50 @@ size_t w4a4_grouped_gemm_rac_workspace_size(const w4a4_gemm_args_t* args);
 int w4a4_grouped_gemm_rac(const w4a4_gemm_args_t* args, void* ws, size_t ws_bytes,
                           void* stream);
 
+/* ------------------------------------------------------------------------
+ * FP8 (E4M3) W8A8 comparator.  The pages measure QUADS against FP8 rollout
+ * (arXiv abstract on the mlsanity page; blog post, section "What it buys")
+ * without saying how the FP8 engine scales its tensors; these calls
+ * implement one FP32 scale per activation row (token) and per weight output
+ * channel, so that a QUADS step can be timed beside an FP8 step on the same
+ * workload.
+ *
+ * fp8_quantize_rows: for each row of x [rows, K] (FP32 or bf16, row-major):
+ *   s = RN32(amax_row / 448)   (double quotient rounded once; 0 for a zero row)
+ *   r = RN32(1 / s)            (0 when s == 0)
+ *   codes[row, k] = E4M3(RN32(x r)): OCP E4M3 (bias 7, max 448), nearest
+ *   even, saturating at +-448, sign bit from the product (so -0 may occur).
+ * codes is uint8 [rows, K]; row_scales is float [rows].  Requires K % 16 == 0,
+ * x 16-byte aligned, codes 8-byte aligned.
+ * ------------------------------------------------------------------------ */
+int fp8_quantize_rows(const void* x, int in_dtype, int64_t rows, int64_t K, uint8_t* codes,
+                      float* row_scales, void* stream);
+
+/* fp8_grouped_gemm: grouped (per-expert) FP8 GEMM with the grouping, gather
+ * and epilogues of w4a4_grouped_gemm_rac:
+ *   y[j, n] = a_scales[src] * w_scales[g*N + n] * sum_k A[src,k] W_g[n,k]
+ * with A, W the E4M3 values (products exact, FP32 accumulation).  Epilogue
+ * SILU_MUL_BF16 writes h[j, i] = bf16(silu(y[j, i]) * y[j, I + i]) to out
+ * [total_rows, I] (no amax: the FP8 quantizer scales per row).  Requires
+ * K % 128 == 0, N % 128 == 0, codes 16-byte aligned, scales 4-byte aligned.
+ * No workspace. */
+typedef struct {
+  int64_t num_groups;           /* G >= 1 */
+  int64_t N;                    /* output columns (2I for SILU_MUL) */
+  int64_t K;                    /* contraction length */
+  int64_t total_rows;           /* rows of the grouped output */
+  const int32_t* group_offsets; /* [G+1], ascending, [0] = 0, [G] = total_rows */
+  const int32_t* gather_rows;   /* [total_rows] or NULL (identity) */
+  const uint8_t* a_codes;       /* [src_rows, K] E4M3 */
+  const float* a_scales;        /* [src_rows] */
+  const uint8_t* w_codes;       /* [G, N, K] E4M3 */
+  const float* w_scales;        /* [G, N] */
+  int64_t epilogue;             /* nvfp4_epilogue_t */
+  void* out;                    /* float [total_rows, N] or bf16 [total_rows, N/2] */
+} fp8_gemm_args_t;
+
+int fp8_grouped_gemm(const fp8_gemm_args_t* args, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -39,6 +39,16 @@ class GemmArgs(ctypes.Structure):
     ]
 
 
+class Fp8GemmArgs(ctypes.Structure):
+    """Mirror of fp8_gemm_args_t."""
+    _fields_ = [
+        ("num_groups", _I64), ("N", _I64), ("K", _I64), ("total_rows", _I64),
+        ("group_offsets", _P), ("gather_rows", _P),
+        ("a_codes", _P), ("a_scales", _P), ("w_codes", _P), ("w_scales", _P),
+        ("epilogue", _I64), ("out", _P),
+    ]
+
+
 _SIGS = {
     "nvfp4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "nvfp4_quantize_workspace_size": (_SZ, [_I64, _I64]),
@@ -51,6 +61,8 @@ _SIGS = {
     "moe_route": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "w4a4_grouped_gemm_rac_workspace_size": (_SZ, [ctypes.POINTER(GemmArgs)]),
     "w4a4_grouped_gemm_rac": (ctypes.c_int, [ctypes.POINTER(GemmArgs), _P, _SZ, _P]),
+    "fp8_quantize_rows": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _P, _P, _P]),
+    "fp8_grouped_gemm": (ctypes.c_int, [ctypes.POINTER(Fp8GemmArgs), _P]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -218,4 +230,45 @@ def w4a4_grouped_gemm_rac(a: NVFP4, w: NVFP4, group_offsets: torch.Tensor, *, N:
     ws = _ws(nbytes, dev) if nbytes else None
     _check(L.w4a4_grouped_gemm_rac(ctypes.byref(args), _ptr(ws), 0 if ws is None else ws.numel(),
                                    _stream(dev)))
+    return out
+
+
+# ------------------------------------------------- FP8 W8A8 comparator
+class FP8(NamedTuple):
+    codes: torch.Tensor    # uint8 [rows, K] (E4M3), or [G, N, K] for weights
+    scales: torch.Tensor   # float32 [rows], or [G, N]
+
+
+def fp8_quantize_rows(x: torch.Tensor, out: Optional[FP8] = None) -> FP8:
+    """Per-row E4M3 quantization of x [rows, K] (bf16 or FP32)."""
+    assert x.dim() == 2 and x.is_contiguous()
+    rows, K = x.shape
+    dev = x.device
+    if out is None:
+        out = FP8(torch.empty((rows, K), dtype=torch.uint8, device=dev),
+                  torch.empty(rows, dtype=torch.float32, device=dev))
+    _check(lib().fp8_quantize_rows(_ptr(x), _dtype_code(x), rows, K, _ptr(out.codes),
+                                   _ptr(out.scales), _stream(dev)))
+    return out
+
+
+def fp8_grouped_gemm(a: FP8, w: FP8, group_offsets: torch.Tensor, *, N: int, K: int,
+                     total_rows: int, gather_rows: Optional[torch.Tensor] = None,
+                     epilogue: int = NVFP4_EPI_F32,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """w: codes [G, N, K], scales [G, N]."""
+    dev = a.codes.device
+    G = group_offsets.numel() - 1
+    if out is None:
+        if epilogue == NVFP4_EPI_F32:
+            out = torch.empty((total_rows, N), dtype=torch.float32, device=dev)
+        else:
+            out = torch.empty((total_rows, N // 2), dtype=torch.bfloat16, device=dev)
+    args = Fp8GemmArgs(
+        num_groups=G, N=N, K=K, total_rows=total_rows,
+        group_offsets=_ptr(group_offsets), gather_rows=_ptr(gather_rows),
+        a_codes=_ptr(a.codes), a_scales=_ptr(a.scales),
+        w_codes=_ptr(w.codes), w_scales=_ptr(w.scales),
+        epilogue=epilogue, out=_ptr(out))
+    _check(lib().fp8_grouped_gemm(ctypes.byref(args), _stream(dev)))
     return out

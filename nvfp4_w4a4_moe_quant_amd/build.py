@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libnvfp4rac.so")
-SOURCES = ["quant.hip", "route.hip", "gemm.hip"]
+SOURCES = ["quant.hip", "route.hip", "gemm.hip", "fp8.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -161,3 +161,57 @@ __device__ __forceinline__ void nv_decode8(uint32_t w, float* g) {
   g[0] = a.x; g[1] = a.y; g[2] = b.x; g[3] = b.y;
   g[4] = c.x; g[5] = c.y; g[6] = d.x; g[7] = d.y;
 }
+
+// ---------------------------------------------------------- grouped tiles
+
+// Tile of a grouped-GEMM workgroup: group `grp` (-1 past the real tile count),
+// m-tile `local` inside the group, n-tile `nt`.  The grid holds m_slots x
+// n_tiles workgroups, m_slots an upper bound on the groups' m-tiles.
+//  * The workgroup id is remapped so that consecutive tile indices run on one
+//    XCD (the hardware deals workgroups round-robin over the eight XCDs) and
+//    share its L2.
+//  * Inside a group the m-tiles vary fastest: the workgroups that read one W
+//    tile (one n-tile of one group) are adjacent.
+//  * A wave scan over per-group tile counts finds the group; every wave of the
+//    workgroup computes the same result.
+struct NvTile {
+  int grp, local, nt;
+};
+
+__device__ __forceinline__ NvTile nv_find_tile(const int32_t* offsets, int G, int bm,
+                                               int m_slots, int n_tiles) {
+  const int lane = threadIdx.x & 63;
+  const int nblocks = m_slots * n_tiles;
+  const int bid = blockIdx.x;
+  const int per = nblocks / 8, rem = nblocks % 8, xcd = bid % 8;
+  const int L = xcd * per + (xcd < rem ? xcd : rem) + bid / 8;
+  const int mt = L / n_tiles;
+  NvTile t{-1, 0, 0};
+  int run = 0;
+  for (int c = 0; c < G; c += 64) {
+    const int g = c + lane;
+    int tiles = 0;
+    if (g < G) tiles = (offsets[g + 1] - offsets[g] + bm - 1) / bm;
+    int inc = tiles;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int n = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += n;
+    }
+    const int excl = inc - tiles;
+    const bool hit = g < G && mt >= run + excl && mt < run + inc;
+    const unsigned long long bal = __ballot(hit);
+    if (bal) {
+      const int hl = __ffsll((long long)bal) - 1;
+      const int first = run + __shfl(excl, hl, 64);
+      const int gt = __shfl(tiles, hl, 64);
+      const int i = L - first * n_tiles;
+      t.grp = c + hl;
+      t.local = i % gt;
+      t.nt = i / gt;
+      return t;
+    }
+    run += __shfl(inc, 63, 64);
+  }
+  return t;
+}

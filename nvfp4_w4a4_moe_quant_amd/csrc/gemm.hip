@@ -126,46 +126,9 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int lr = lane & 31, lh = lane >> 5;
 
-  // ---- tile: XCD-aware remap of the workgroup id, then (m slot, n tile)
-  const int nblocks = p.m_slots * p.n_tiles;
-  const int bid = blockIdx.x;
-  const int per = nblocks / 8, rem = nblocks % 8, xcd = bid % 8;
-  const int L = xcd * per + (xcd < rem ? xcd : rem) + bid / 8;
-  const int mt = L / p.n_tiles;
-
-  // ---- find the group that owns m-tile `mt` (a wave scan of per-group tiles).
-  // The group's workgroups form the range [first, first + tiles) * n_tiles of
-  // L; inside it the m-tiles vary fastest, so the m-tiles that share a W tile
-  // run next to each other (one fetch of the W tile serves them all).
-  int grp = -1, local = 0, nt = 0;
-  {
-    int run = 0;
-    for (int c = 0; c < p.G; c += 64) {
-      const int g = c + lane;
-      int tiles = 0;
-      if (g < p.G) tiles = (p.offsets[g + 1] - p.offsets[g] + BM - 1) / BM;
-      int inc = tiles;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int n = __shfl_up(inc, o, 64);
-        if (lane >= o) inc += n;
-      }
-      const int excl = inc - tiles;
-      const bool hit = g < p.G && mt >= run + excl && mt < run + inc;
-      const unsigned long long bal = __ballot(hit);
-      if (bal) {
-        const int hl = __ffsll((long long)bal) - 1;
-        grp = c + hl;
-        const int first = run + __shfl(excl, hl, 64);
-        const int gt = __shfl(tiles, hl, 64);
-        const int i = L - first * p.n_tiles;
-        local = i % gt;
-        nt = i / gt;
-        break;
-      }
-      run += __shfl(inc, 63, 64);
-    }
-  }
+  // ---- tile (group, m-tile, n-tile), XCD-aware, m-tiles fastest in a group
+  const NvTile tile = nv_find_tile(p.offsets, p.G, BM, p.m_slots, p.n_tiles);
+  const int grp = tile.grp, local = tile.local, nt = tile.nt;
   if (grp < 0) return;  // wave-uniform and identical in every wave
   const int row_beg = p.offsets[grp] + local * BM;
   const int row_end = p.offsets[grp + 1];
@@ -465,37 +428,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void k_gemm3(GemmPara
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int lr = lane & 31, lh = lane >> 5;
 
-  const int nblocks = p.m_slots * p.n_tiles;
-  const int bid = blockIdx.x;
-  const int per = nblocks / 8, rem = nblocks % 8, xcd = bid % 8;
-  const int L = xcd * per + (xcd < rem ? xcd : rem) + bid / 8;
-  const int mt = L / p.n_tiles, nt = L % p.n_tiles;
-
-  int grp = -1, local = 0;
-  {
-    int run = 0;
-    for (int c = 0; c < p.G; c += 64) {
-      const int g = c + lane;
-      int tiles = 0;
-      if (g < p.G) tiles = (p.offsets[g + 1] - p.offsets[g] + BM - 1) / BM;
-      int inc = tiles;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int n = __shfl_up(inc, o, 64);
-        if (lane >= o) inc += n;
-      }
-      const int excl = inc - tiles;
-      const bool hit = g < p.G && mt >= run + excl && mt < run + inc;
-      const unsigned long long bal = __ballot(hit);
-      if (bal) {
-        const int hl = __ffsll((long long)bal) - 1;
-        grp = c + hl;
-        local = mt - run - __shfl(excl, hl, 64);
-        break;
-      }
-      run += __shfl(inc, 63, 64);
-    }
-  }
+  const NvTile tile = nv_find_tile(p.offsets, p.G, BM, p.m_slots, p.n_tiles);
+  const int grp = tile.grp, local = tile.local, nt = tile.nt;
   if (grp < 0) return;
   const int row_beg = p.offsets[grp] + local * BM;
   const int row_end = p.offsets[grp + 1];

@@ -117,3 +117,34 @@ def test_gemm_validation(lib):
     assert call(a_codes=FAKE_MIS) == EALIGN
     assert call(kblock_active=ctypes.c_void_p(0x100004), r_codes=FAKE, r_scales=FAKE,
                 r_tscale=FAKE) == EALIGN
+
+
+def test_fp8_validation(lib):
+    def q(x=FAKE, dt=1, rows=4, K=32, codes=FAKE, sc=FAKE):
+        return lib.fp8_quantize_rows(x, dt, rows, K, codes, sc, None)
+    assert q(x=None) == ENULL
+    assert q(sc=None) == ENULL
+    assert q(dt=3) == EDTYPE
+    assert q(K=24) == ESHAPE                        # K % 16
+    assert q(rows=-1) == ESHAPE
+    assert q(x=FAKE_MIS) == EALIGN
+    assert q(sc=ctypes.c_void_p(0x100002)) == EALIGN
+    assert q(rows=0, x=None) == OK                  # empty: nothing enqueued
+
+    def g(**kw):
+        a = L.Fp8GemmArgs(num_groups=2, N=256, K=256, total_rows=10, group_offsets=FAKE,
+                          a_codes=FAKE, a_scales=FAKE, w_codes=FAKE, w_scales=FAKE,
+                          epilogue=0, out=FAKE)
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return lib.fp8_grouped_gemm(ctypes.byref(a), None)
+    assert lib.fp8_grouped_gemm(None, None) == ENULL
+    assert g(out=None) == ENULL
+    assert g(w_scales=None) == ENULL
+    assert g(out=None, total_rows=0) == OK
+    assert g(epilogue=5) == EDTYPE
+    assert g(K=192) == ESHAPE                       # K % 128
+    assert g(N=96) == ESHAPE                        # N % 128
+    assert g(num_groups=0) == ESHAPE
+    assert g(a_codes=FAKE_MIS) == EALIGN
+    assert g(a_scales=ctypes.c_void_p(0x100002)) == EALIGN
