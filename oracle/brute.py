@@ -231,3 +231,15 @@ def fp8_gemm(a_codes, a_scales, w, offsets, gather, N):
             row.append(rn32(a_scales[src] * wsc[n] * acc))
         out.append(row)
     return out
+
+
+# --- trainer-side weight fake-quant --------------------------------------------
+def qdq(x, amax=None):
+    """Quantize then dequantize with exact rationals: (FP32 values as
+    Fractions, bf16 values as Fractions, s_t).  FP32 value = RN32(g s_b s_t)
+    formed as RN32(RN32(g s_b) s_t); bf16 value = RNbf16 of the FP32 value."""
+    codes, scales, s_t = quantize(x, amax)
+    f = [[dequant(codes[r][k], scales[r][k // 16], s_t) for k in range(len(x[0]))]
+         for r in range(len(x))]
+    b = [[rnbf16(v) for v in row] for row in f]
+    return f, b, s_t

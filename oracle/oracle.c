@@ -624,3 +624,35 @@ void or_fp8_grouped_gemm_sample(int64_t G, int64_t N, int64_t K, const int32_t* 
     out[i] = fp8_one(G, N, K, offsets, gather, a_codes, a_scales, w_codes, w_scales,
                      rows[i], cols[i]);
 }
+
+/* ------------------------------------- trainer-side weight fake-quant */
+
+/* Asymmetric QAT fake-quantizes the trainer's weights with the rollout's own
+ * NVFP4 quantize-dequantize path and leaves activations unquantized (blog
+ * post, section "Two fixes, on two different sides"; arXiv abstract: a shared
+ * quantization-dequantization path aligns the weights).  Reading: the
+ * trainer's weight is the rollout's dequantized value, formed in FP32 as
+ * RN32(RN32(g * s_b) * s_t) (g * s_b is exact, so this is the exact product
+ * rounded once), and, for a bf16 trainer, that value rounded to bf16
+ * (nearest even).  out_f32 and out_bf16 are each optional. */
+int or_qdq(const float* x, int64_t rows, int64_t K, const float* amax, float* out_f32,
+           uint16_t* out_bf16, float* s_t_out) {
+  uint8_t* codes = (uint8_t*)malloc((size_t)(rows * K / 2 > 0 ? rows * K / 2 : 1));
+  uint8_t* scales = (uint8_t*)malloc((size_t)(rows * K / 16 > 0 ? rows * K / 16 : 1));
+  float* deq = (float*)malloc(sizeof(float) * (size_t)(rows * K > 0 ? rows * K : 1));
+  float s_t = 0.0f;
+  int64_t i;
+  int rc = or_quantize(x, rows, K, K, amax, codes, scales, &s_t);
+  if (rc == 0) {
+    or_dequantize(codes, scales, s_t, rows, K, deq);
+    for (i = 0; i < rows * K; i++) {
+      if (out_f32) out_f32[i] = deq[i];
+      if (out_bf16) out_bf16[i] = or_bf16_rne((double)deq[i]);
+    }
+    if (s_t_out) *s_t_out = s_t;
+  }
+  free(codes);
+  free(scales);
+  free(deq);
+  return rc;
+}

@@ -63,6 +63,7 @@ _SIGS = {
     "or_bf16_rne": (ctypes.c_uint16, [ctypes.c_double]),
     "or_silu_mul": (None, [_P, _I64, _I64, _P, _P]),
     "or_route": (None, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "or_qdq": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P]),
     "or_fp8_row_scale": (_F, [_F]),
     "or_fp8_encode": (ctypes.c_int, [_F]),
     "or_fp8_quantize_rows": (None, [_P, _I64, _I64, _I64, _P, _P]),
@@ -251,6 +252,21 @@ def route(logits, k):
                    _p(row_of))
     return dict(topk_ids=ids, topk_weights=wts, offsets=off, gather=gather,
                 row_of=row_of)
+
+
+# ------------------------------------ trainer-side weight fake-quant
+def qdq(x, amax=None):
+    """x float32 [rows, K] -> (FP32 fake-quant [rows, K], bf16 bits u16
+    [rows, K], s_t): the rollout's NVFP4 quantize then dequantize."""
+    x = _c(x, np.float32)
+    rows, K = x.shape
+    f = np.zeros((rows, K), np.float32)
+    b = np.zeros((rows, K), np.uint16)
+    ts = np.zeros(1, np.float32)
+    am = None if amax is None else np.array([amax], np.float32)
+    if lib().or_qdq(_p(x), rows, K, _p(am), _p(f), _p(b), _p(ts)):
+        raise ValueError("K must be a multiple of 16")
+    return f, b, float(ts[0])
 
 
 # ------------------------------------------------- FP8 W8A8 comparator
