@@ -212,6 +212,34 @@ int w4a4_grouped_gemm_rac(const w4a4_gemm_args_t* args, void* ws, size_t ws_byte
                           void* stream);
 
 /* ------------------------------------------------------------------------
+ * Trainer-side weight fake-quantization (Asymmetric QAT).  The trainer
+ * fake-quantizes its weights, and only its weights, with the rollout's own
+ * NVFP4 quantize-dequantize path, so the two sides see the same weight error
+ * (blog post, section "Two fixes, on two different sides"; arXiv abstract:
+ * weights align through a shared quantization-dequantization path).
+ *
+ * nvfp4_qdq: runs the quantizer of nvfp4_quantize (same kernel, same
+ * arithmetic, tensor scale from max|x| or from amax_in) and stores, instead of
+ * codes and scales, the dequantized values v = RN32(RN32(g s_b) s_t) -- the
+ * exact product g s_b s_t rounded once -- to out [rows, K] (row stride K):
+ * FP32 for out_dtype NVFP4_IN_F32, bf16 (nearest even of v) for
+ * NVFP4_IN_BF16.  *tensor_scale receives s_t.  Workspace as
+ * nvfp4_quantize (none with amax_in).  Requires K % 16 == 0, x and out
+ * 16-byte aligned, ldx % 8 == 0.
+ *
+ * nvfp4_dequantize: the same values from stored codes [rows, K/2], scales
+ * [rows, K/16] and tensor scale; nvfp4_qdq(x) equals
+ * nvfp4_dequantize(nvfp4_quantize(x)) bit for bit.  Requires K % 16 == 0,
+ * codes 8-byte aligned, out 16-byte aligned.  No workspace.
+ * ------------------------------------------------------------------------ */
+size_t nvfp4_qdq_workspace_size(int64_t rows, int64_t K);
+int nvfp4_qdq(const void* x, int in_dtype, int64_t rows, int64_t K, int64_t ldx,
+              const float* amax_in, int out_dtype, void* out, float* tensor_scale, void* ws,
+              size_t ws_bytes, void* stream);
+int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                     int64_t rows, int64_t K, int out_dtype, void* out, void* stream);
+
+/* ------------------------------------------------------------------------
  * FP8 (E4M3) W8A8 comparator.  The pages measure QUADS against FP8 rollout
  * (arXiv abstract on the mlsanity page; blog post, section "What it buys")
  * without saying how the FP8 engine scales its tensors; these calls

@@ -61,6 +61,10 @@ _SIGS = {
     "moe_route": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "w4a4_grouped_gemm_rac_workspace_size": (_SZ, [ctypes.POINTER(GemmArgs)]),
     "w4a4_grouped_gemm_rac": (ctypes.c_int, [ctypes.POINTER(GemmArgs), _P, _SZ, _P]),
+    "nvfp4_qdq_workspace_size": (_SZ, [_I64, _I64]),
+    "nvfp4_qdq": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _P, ctypes.c_int, _P, _P,
+                                 _P, _SZ, _P]),
+    "nvfp4_dequantize": (ctypes.c_int, [_P, _P, _P, _I64, _I64, ctypes.c_int, _P, _P]),
     "fp8_quantize_rows": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _P, _P, _P]),
     "fp8_grouped_gemm": (ctypes.c_int, [ctypes.POINTER(Fp8GemmArgs), _P]),
 }
@@ -230,6 +234,34 @@ def w4a4_grouped_gemm_rac(a: NVFP4, w: NVFP4, group_offsets: torch.Tensor, *, N:
     ws = _ws(nbytes, dev) if nbytes else None
     _check(L.w4a4_grouped_gemm_rac(ctypes.byref(args), _ptr(ws), 0 if ws is None else ws.numel(),
                                    _stream(dev)))
+    return out
+
+
+# ------------------------------------ trainer-side weight fake-quant
+def nvfp4_qdq(x: torch.Tensor, *, out_dtype: torch.dtype = torch.bfloat16,
+              amax_in: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The rollout's NVFP4 quantize-dequantize of a 2-D bf16/fp32 tensor,
+    returned as bf16 or FP32 [rows, K]."""
+    assert x.dim() == 2 and x.stride(1) == 1
+    rows, K = x.shape
+    dev = x.device
+    out = torch.empty((rows, K), dtype=out_dtype, device=dev)
+    ts = torch.empty(1, dtype=torch.float32, device=dev)
+    L = lib()
+    ws = _ws(L.nvfp4_qdq_workspace_size(rows, K), dev)
+    _check(L.nvfp4_qdq(_ptr(x), _dtype_code(x), rows, K, x.stride(0), _ptr(amax_in),
+                       _dtype_code(out), _ptr(out), _ptr(ts), _ptr(ws), ws.numel(),
+                       _stream(dev)))
+    return out
+
+
+def nvfp4_dequantize(q: NVFP4, *, out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """Dequantized values of an NVFP4 tensor (codes [rows, K/2])."""
+    rows, K = q.codes.shape[0], q.codes.shape[1] * 2
+    dev = q.codes.device
+    out = torch.empty((rows, K), dtype=out_dtype, device=dev)
+    _check(lib().nvfp4_dequantize(_ptr(q.codes), _ptr(q.scales), _ptr(q.tscale), rows, K,
+                                  _dtype_code(out), _ptr(out), _stream(dev)))
     return out
 
 

@@ -133,13 +133,40 @@ struct RawBlock {
   }
 };
 
-template <bool kStats, bool kBf16>
+// 16 dequantized values RN32(RN32(g s_b) s_t) of one block -> FP32 (kDq 1) or
+// bf16 nearest even (kDq 2) at element offset o of out (row stride K).
+template <int kDq>
+__device__ __forceinline__ void dq_store16(void* out, int64_t o, uint32_t lo, uint32_t hi, float sb,
+                                           float s_t) {
+  float g[16];
+  nv_decode8(lo, g);
+  nv_decode8(hi, g + 8);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) g[i] = (g[i] * sb) * s_t;
+  if constexpr (kDq == 1) {
+    float4* d = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + o);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = make_float4(g[4 * i], g[4 * i + 1], g[4 * i + 2], g[4 * i + 3]);
+  } else {
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = nv_f32_to_bf16(g[2 * i]) | (nv_f32_to_bf16(g[2 * i + 1]) << 16);
+    uint4* d = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + o);
+    d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+
+// kDq 0: codes and block scales.  kDq 1 / 2: the dequantized values instead
+// (FP32 / bf16, row stride K) -- the trainer's weight fake-quantization runs
+// the same quantizer and stores what the rollout's dequantization would give.
+template <bool kStats, bool kBf16, int kDq = 0>
 __global__ __launch_bounds__(kQThreads) void k_quant(
     const void* __restrict__ x, int64_t rows, int64_t K, int64_t ldx,
     const float* __restrict__ partials, int nparts, const float* __restrict__ amax_in,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ tscale_out,
     int64_t* __restrict__ score, uint32_t* __restrict__ chmax, int tpr, int rpi,
-    int64_t rows_per_split) {
+    int64_t rows_per_split, void* __restrict__ dq_out) {
   extern __shared__ unsigned char dyn_lds[];
   __shared__ float red[kQThreads / 64];
   const float amax = workgroup_amax(partials, nparts, amax_in, red);
@@ -185,8 +212,12 @@ __global__ __launch_bounds__(kQThreads) void k_quant(
         emax[i] = __builtin_fmaxf(emax[i], __builtin_fabsf(e));
       }
     }
-    *reinterpret_cast<uint2*>(codes + r * (K >> 1) + cb * 8) = make_uint2(lo, hi);
-    scales[r * CB + cb] = (uint8_t)sc;
+    if constexpr (kDq == 0) {
+      *reinterpret_cast<uint2*>(codes + r * (K >> 1) + cb * 8) = make_uint2(lo, hi);
+      scales[r * CB + cb] = (uint8_t)sc;
+    } else {
+      dq_store16<kDq>(dq_out, r * K + cb * 16, lo, hi, sb, s_t);
+    }
   };
 
   // bf16: two rows per iteration, both loads issued before either is used
@@ -479,21 +510,14 @@ size_t nvfp4_quantize_workspace_size(int64_t, int64_t) {
   return nv_round256(sizeof(float) * kMaxParts);
 }
 
-int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx,
-                   const float* amax_in, uint8_t* codes, uint8_t* scales, float* tensor_scale,
-                   int64_t* channel_score, float* channel_max, void* ws, size_t ws_bytes,
-                   void* stream) {
-  int st = check_x(x, dtype, rows, K, ldx);
-  if (st) return st;
-  NV_RETURN_IF(!tensor_scale || (rows > 0 && (!codes || !scales)), NVFP4_ERR_NULL);
-  NV_RETURN_IF((channel_score == nullptr) != (channel_max == nullptr), NVFP4_ERR_NULL);
-  NV_RETURN_IF(!nv_aligned16(codes), NVFP4_ERR_ALIGN);
-  NV_RETURN_IF(channel_score && ((reinterpret_cast<uintptr_t>(channel_score) & 7) ||
-                                 (reinterpret_cast<uintptr_t>(channel_max) & 3)),
-               NVFP4_ERR_ALIGN);
-  NV_RETURN_IF(!amax_in && (!ws || ws_bytes < nvfp4_quantize_workspace_size(rows, K)),
-               NVFP4_ERR_WORKSPACE);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+}  // extern "C"
+
+// The quantizer's launches (after validation): tensor amax, then k_quant with
+// output mode dq (0: codes/scales, 1: FP32 dequantized, 2: bf16 dequantized).
+static int quantize_launch(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx,
+                           const float* amax_in, uint8_t* codes, uint8_t* scales,
+                           float* tensor_scale, int64_t* channel_score, float* channel_max,
+                           void* ws, int dq, void* dq_out, hipStream_t s) {
   const bool stats = channel_score != nullptr;
   uint32_t* chm = reinterpret_cast<uint32_t*>(channel_max);
   float* partials = reinterpret_cast<float*>(ws);
@@ -540,12 +564,96 @@ int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ld
 #define NV_QUANT_LAUNCH(ST, BF)                                                                 \
   hipLaunchKernelGGL((k_quant<ST, BF>), grid, dim3(kQThreads), ST ? lds : 0, s, x, rows, K, ldx, \
                      partials, nparts, amax_in, codes, scales, tensor_scale, sc, cm, tpr, rpi,   \
-                     rows_per_split)
-  if (stats && bf16) NV_QUANT_LAUNCH(true, true);
+                     rows_per_split, nullptr)
+#define NV_QUANT_LAUNCH_DQ(DQ, BF)                                                              \
+  hipLaunchKernelGGL((k_quant<false, BF, DQ>), grid, dim3(kQThreads), 0, s, x, rows, K, ldx,    \
+                     partials, nparts, amax_in, nullptr, nullptr, tensor_scale, nullptr, nullptr, \
+                     tpr, rpi, rows_per_split, dq_out)
+  if (dq == 1 && bf16) NV_QUANT_LAUNCH_DQ(1, true);
+  else if (dq == 1) NV_QUANT_LAUNCH_DQ(1, false);
+  else if (dq == 2 && bf16) NV_QUANT_LAUNCH_DQ(2, true);
+  else if (dq == 2) NV_QUANT_LAUNCH_DQ(2, false);
+  else if (stats && bf16) NV_QUANT_LAUNCH(true, true);
   else if (stats) NV_QUANT_LAUNCH(true, false);
   else if (bf16) NV_QUANT_LAUNCH(false, true);
   else NV_QUANT_LAUNCH(false, false);
 #undef NV_QUANT_LAUNCH
+#undef NV_QUANT_LAUNCH_DQ
+  return nv_launch_status();
+}
+
+// k_dequant: one thread per 16-element block (grid-stride).
+template <int kDq>
+__global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict__ codes,
+                                                      const uint8_t* __restrict__ scales,
+                                                      const float* __restrict__ tscale,
+                                                      int64_t rows, int64_t K, void* __restrict__ out) {
+  const float s_t = *tscale;
+  const int64_t CB = K >> 4, nblk = rows * CB;
+  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk;
+       b += (int64_t)gridDim.x * kThreads) {
+    const int64_t r = b / CB, cb = b - r * CB;
+    const uint2 c = *reinterpret_cast<const uint2*>(codes + r * (K >> 1) + cb * 8);
+    dq_store16<kDq>(out, r * K + cb * 16, c.x, c.y, nv_e4m3_to_f32(scales[b]), s_t);
+  }
+}
+
+extern "C" {
+
+int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx,
+                   const float* amax_in, uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                   int64_t* channel_score, float* channel_max, void* ws, size_t ws_bytes,
+                   void* stream) {
+  int st = check_x(x, dtype, rows, K, ldx);
+  if (st) return st;
+  NV_RETURN_IF(!tensor_scale || (rows > 0 && (!codes || !scales)), NVFP4_ERR_NULL);
+  NV_RETURN_IF((channel_score == nullptr) != (channel_max == nullptr), NVFP4_ERR_NULL);
+  NV_RETURN_IF(!nv_aligned16(codes), NVFP4_ERR_ALIGN);
+  NV_RETURN_IF(channel_score && ((reinterpret_cast<uintptr_t>(channel_score) & 7) ||
+                                 (reinterpret_cast<uintptr_t>(channel_max) & 3)),
+               NVFP4_ERR_ALIGN);
+  NV_RETURN_IF(!amax_in && (!ws || ws_bytes < nvfp4_quantize_workspace_size(rows, K)),
+               NVFP4_ERR_WORKSPACE);
+  return quantize_launch(x, dtype, rows, K, ldx, amax_in, codes, scales, tensor_scale,
+                         channel_score, channel_max, ws, 0, nullptr,
+                         reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t nvfp4_qdq_workspace_size(int64_t rows, int64_t K) {
+  return nvfp4_quantize_workspace_size(rows, K);
+}
+
+int nvfp4_qdq(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx,
+              const float* amax_in, int out_dtype, void* out, float* tensor_scale, void* ws,
+              size_t ws_bytes, void* stream) {
+  int st = check_x(x, dtype, rows, K, ldx);
+  if (st) return st;
+  NV_RETURN_IF(out_dtype != NVFP4_IN_F32 && out_dtype != NVFP4_IN_BF16, NVFP4_ERR_DTYPE);
+  NV_RETURN_IF(!tensor_scale || (rows > 0 && !out), NVFP4_ERR_NULL);
+  NV_RETURN_IF(!nv_aligned16(out), NVFP4_ERR_ALIGN);
+  NV_RETURN_IF(!amax_in && (!ws || ws_bytes < nvfp4_qdq_workspace_size(rows, K)),
+               NVFP4_ERR_WORKSPACE);
+  return quantize_launch(x, dtype, rows, K, ldx, amax_in, nullptr, nullptr, tensor_scale,
+                         nullptr, nullptr, ws, out_dtype == NVFP4_IN_F32 ? 1 : 2, out,
+                         reinterpret_cast<hipStream_t>(stream));
+}
+
+int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                     int64_t rows, int64_t K, int out_dtype, void* out, void* stream) {
+  NV_RETURN_IF(out_dtype != NVFP4_IN_F32 && out_dtype != NVFP4_IN_BF16, NVFP4_ERR_DTYPE);
+  NV_RETURN_IF(rows < 0 || K <= 0 || K % 16 || K > (1LL << 40) / (rows > 0 ? rows : 1),
+               NVFP4_ERR_SHAPE);
+  if (rows == 0) return NVFP4_OK;
+  NV_RETURN_IF(!codes || !scales || !tensor_scale || !out, NVFP4_ERR_NULL);
+  NV_RETURN_IF((reinterpret_cast<uintptr_t>(codes) & 7) || !nv_aligned16(out), NVFP4_ERR_ALIGN);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const unsigned grid = (unsigned)blocks_for(rows * (K >> 4), kThreads, 8192);
+  if (out_dtype == NVFP4_IN_F32)
+    hipLaunchKernelGGL(k_dequant<1>, dim3(grid), dim3(kThreads), 0, s, codes, scales,
+                       tensor_scale, rows, K, out);
+  else
+    hipLaunchKernelGGL(k_dequant<2>, dim3(grid), dim3(kThreads), 0, s, codes, scales,
+                       tensor_scale, rows, K, out);
   return nv_launch_status();
 }
 

@@ -97,3 +97,19 @@ def moe_forward(x: torch.Tensor, logits: torch.Tensor, wgu: QuantWeights, wd: Qu
     h_in = quantize_input(h, n_sel_h, amax_in=amax_h)
     y = gemm(h_in, wd, rt.expert_offsets, rows)
     return dict(route=rt, x_in=x_in, h=h, amax_h=amax_h, h_in=h_in, y=y)
+
+
+class NVFP4WeightFakeQuant(torch.autograd.Function):
+    """Trainer-side Asymmetric QAT for one weight matrix: the forward pass
+    uses the rollout's NVFP4 quantize-dequantize of W (nvfp4_qdq, bf16 out),
+    the backward pass hands the gradient to W unchanged (straight-through).
+    Activations stay unquantized (QUADS blog post, section "Two fixes, on two
+    different sides")."""
+
+    @staticmethod
+    def forward(ctx, w: torch.Tensor) -> torch.Tensor:
+        return L.nvfp4_qdq(w.detach().contiguous(), out_dtype=w.dtype)
+
+    @staticmethod
+    def backward(ctx, grad: torch.Tensor) -> torch.Tensor:
+        return grad

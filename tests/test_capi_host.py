@@ -148,3 +148,25 @@ def test_fp8_validation(lib):
     assert g(num_groups=0) == ESHAPE
     assert g(a_codes=FAKE_MIS) == EALIGN
     assert g(a_scales=ctypes.c_void_p(0x100002)) == EALIGN
+
+
+def test_qdq_validation(lib):
+    def q(x=FAKE, dt=1, rows=4, K=32, ldx=32, od=1, out=FAKE, ts=FAKE, ws=FAKE, wsb=1 << 20,
+          amax=None):
+        return lib.nvfp4_qdq(x, dt, rows, K, ldx, amax, od, out, ts, ws, wsb, None)
+    assert q(out=None) == ENULL
+    assert q(ts=None) == ENULL
+    assert q(od=4) == EDTYPE
+    assert q(K=24, ldx=32) == ESHAPE
+    assert q(out=FAKE_MIS) == EALIGN
+    assert q(ws=None) == EWS
+
+    def d(codes=FAKE, sc=FAKE, ts=FAKE, rows=4, K=32, od=0, out=FAKE):
+        return lib.nvfp4_dequantize(codes, sc, ts, rows, K, od, out, None)
+    assert d(codes=None) == ENULL
+    assert d(ts=None) == ENULL
+    assert d(od=3) == EDTYPE
+    assert d(K=24) == ESHAPE
+    assert d(rows=-1) == ESHAPE
+    assert d(codes=FAKE_MIS) == EALIGN
+    assert d(rows=0, codes=None) == OK
