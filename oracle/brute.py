@@ -243,3 +243,20 @@ def qdq(x, amax=None):
          for r in range(len(x))]
     b = [[rnbf16(v) for v in row] for row in f]
     return f, b, s_t
+
+
+# --- MoE combine -----------------------------------------------------------------
+def moe_combine(y, row_of, w):
+    """Exact rationals with explicit FP32 rounding of every product and sum,
+    slot order: returns (FP32 rows, bf16 rows) as Fractions."""
+    f, b = [], []
+    for t in range(len(row_of)):
+        row_f = []
+        for h in range(len(y[0])):
+            acc = Fr(0)
+            for s in range(len(row_of[t])):
+                acc = rn32(acc + rn32(w[t][s] * y[row_of[t][s]][h]))
+            row_f.append(acc)
+        f.append(row_f)
+        b.append([rnbf16(v) for v in row_f])
+    return f, b

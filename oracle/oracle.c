@@ -656,3 +656,29 @@ int or_qdq(const float* x, int64_t rows, int64_t K, const float* amax, float* ou
   free(deq);
   return rc;
 }
+
+/* ----------------------------------------------------------- MoE combine */
+
+/* Weighted combine of the expert outputs back to token order, the last step
+ * of the MoE layer whose expert GEMMs the pages quantize (arXiv abstract: MoE
+ * rollout).  Reading: for token t,
+ *   acc = 0; for s = 0 .. k-1: acc = RN32(acc + RN32(w[t,s] * y[row_of[t,s], :]))
+ * in slot order (the routing's (logit desc, index asc) order), then FP32
+ * out_f32 = acc and/or bf16 out_bf16 = bf16(acc) (nearest even). */
+void or_moe_combine(const float* y, const int32_t* row_of, const float* w, int64_t T,
+                    int64_t k, int64_t H, float* out_f32, uint16_t* out_bf16) {
+  int64_t t;
+#pragma omp parallel for schedule(static)
+  for (t = 0; t < T; t++) {
+    int64_t h, s;
+    for (h = 0; h < H; h++) {
+      float acc = 0.0f;
+      for (s = 0; s < k; s++) {
+        float p = w[t * k + s] * y[(int64_t)row_of[t * k + s] * H + h];
+        acc = acc + p;
+      }
+      if (out_f32) out_f32[t * H + h] = acc;
+      if (out_bf16) out_bf16[t * H + h] = or_bf16_rne((double)acc);
+    }
+  }
+}

@@ -64,6 +64,7 @@ _SIGS = {
     "or_silu_mul": (None, [_P, _I64, _I64, _P, _P]),
     "or_route": (None, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "or_qdq": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P]),
+    "or_moe_combine": (None, [_P, _P, _P, _I64, _I64, _I64, _P, _P]),
     "or_fp8_row_scale": (_F, [_F]),
     "or_fp8_encode": (ctypes.c_int, [_F]),
     "or_fp8_quantize_rows": (None, [_P, _I64, _I64, _I64, _P, _P]),
@@ -252,6 +253,20 @@ def route(logits, k):
                    _p(row_of))
     return dict(topk_ids=ids, topk_weights=wts, offsets=off, gather=gather,
                 row_of=row_of)
+
+
+def moe_combine(y, row_of, weights):
+    """y float32 [rows, H] (grouped order); row_of int32 [T, k]; weights
+    float32 [T, k] -> (FP32 [T, H], bf16 bits u16 [T, H])."""
+    y = _c(y, np.float32)
+    row_of = _c(row_of, np.int32)
+    weights = _c(weights, np.float32)
+    T, k = row_of.shape
+    H = y.shape[1]
+    f = np.zeros((T, H), np.float32)
+    b = np.zeros((T, H), np.uint16)
+    lib().or_moe_combine(_p(y), _p(row_of), _p(weights), T, k, H, _p(f), _p(b))
+    return f, b
 
 
 # ------------------------------------ trainer-side weight fake-quant
