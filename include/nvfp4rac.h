@@ -158,6 +158,20 @@ int moe_route(const float* logits, int64_t T, int64_t E, int64_t k,
               void* stream);
 
 /* ------------------------------------------------------------------------
+ * moe_combine -- weighted combine of the expert outputs back to token order
+ * (the end of the MoE layer whose expert GEMMs the pages quantize).  For each
+ * token t, in slot order s = 0 .. k-1 (the order moe_route writes):
+ *   acc = RN32(acc + RN32(topk_weights[t, s] * y[row_of[t, s], :])), acc from 0
+ * then out[t, :] = acc (FP32, out_dtype NVFP4_IN_F32) or bf16(acc) (nearest
+ * even, NVFP4_IN_BF16).  A gather, not an atomic scatter-add, so the result
+ * is deterministic.  y is float [rows, H] in grouped order; row_of and
+ * topk_weights are [T, k] from moe_route; out is [T, H].  Requires 1 <= k <=
+ * 16, H % 8 == 0, y and out 16-byte aligned.  No workspace.
+ * ------------------------------------------------------------------------ */
+int moe_combine(const float* y, const int32_t* row_of, const float* topk_weights, int64_t T,
+                int64_t k, int64_t H, int out_dtype, void* out, void* stream);
+
+/* ------------------------------------------------------------------------
  * w4a4_grouped_gemm_rac -- grouped (per-expert) W4A4 GEMM with the RAC
  * residual pass fused into the same kernel (abstract: 4-bit by 4-bit GEMMs;
  * blog, "Two fixes": the selected channels' residual pass adds to the

@@ -61,6 +61,7 @@ _SIGS = {
     "moe_route": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "w4a4_grouped_gemm_rac_workspace_size": (_SZ, [ctypes.POINTER(GemmArgs)]),
     "w4a4_grouped_gemm_rac": (ctypes.c_int, [ctypes.POINTER(GemmArgs), _P, _SZ, _P]),
+    "moe_combine": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P, _P]),
     "nvfp4_qdq_workspace_size": (_SZ, [_I64, _I64]),
     "nvfp4_qdq": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _P, ctypes.c_int, _P, _P,
                                  _P, _SZ, _P]),
@@ -234,6 +235,18 @@ def w4a4_grouped_gemm_rac(a: NVFP4, w: NVFP4, group_offsets: torch.Tensor, *, N:
     ws = _ws(nbytes, dev) if nbytes else None
     _check(L.w4a4_grouped_gemm_rac(ctypes.byref(args), _ptr(ws), 0 if ws is None else ws.numel(),
                                    _stream(dev)))
+    return out
+
+
+def moe_combine(y: torch.Tensor, row_of: torch.Tensor, topk_weights: torch.Tensor, *,
+                out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """Token-order output [T, H] from the grouped expert outputs y [rows, H]."""
+    T, k = row_of.shape
+    H = y.shape[1]
+    dev = y.device
+    out = torch.empty((T, H), dtype=out_dtype, device=dev)
+    _check(lib().moe_combine(_ptr(y), _ptr(row_of), _ptr(topk_weights), T, k, H,
+                             _dtype_code(out), _ptr(out), _stream(dev)))
     return out
 
 

@@ -161,6 +161,69 @@ __global__ __launch_bounds__(kTok) void k_scatter(const int32_t* __restrict__ id
   }
 }
 
+// ---------------------------------------------------------------- combine
+// out[t, :] = sum over the token's k slots, in slot order, of
+// w[t, s] * y[row_of[t, s], :]: one FP32 product and one FP32 addition per
+// slot (unfused, the same order for every element), then FP32 or bf16.  A
+// thread owns 8 consecutive columns of one token and loads all k rows before
+// the first addition; consecutive threads read consecutive 32-byte pieces.
+template <int KMAX, bool kBf16Out>
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
+                                                 const int32_t* __restrict__ row_of,
+                                                 const float* __restrict__ w, int64_t T, int k,
+                                                 int64_t H, void* __restrict__ out) {
+  const int64_t nv = H >> 3;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= T * nv) return;
+  const int64_t t = i / nv, hv = i - t * nv;
+  float4 a[KMAX], b[KMAX];
+  float ws[KMAX];
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    if (s < k) {
+      const int64_t r = row_of[t * k + s];
+      ws[s] = w[t * k + s];
+      const float4* p = reinterpret_cast<const float4*>(y + r * H + hv * 8);
+      a[s] = p[0];
+      b[s] = p[1];
+    }
+  }
+  float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    if (s < k) {
+      const float v[8] = {a[s].x, a[s].y, a[s].z, a[s].w, b[s].x, b[s].y, b[s].z, b[s].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = acc[e] + ws[s] * v[e];
+    }
+  }
+  if constexpr (kBf16Out) {
+    uint4 o;
+    o.x = nv_f32_to_bf16(acc[0]) | (nv_f32_to_bf16(acc[1]) << 16);
+    o.y = nv_f32_to_bf16(acc[2]) | (nv_f32_to_bf16(acc[3]) << 16);
+    o.z = nv_f32_to_bf16(acc[4]) | (nv_f32_to_bf16(acc[5]) << 16);
+    o.w = nv_f32_to_bf16(acc[6]) | (nv_f32_to_bf16(acc[7]) << 16);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + t * H + hv * 8) = o;
+  } else {
+    float4* d = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + t * H + hv * 8);
+    d[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    d[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
+}
+
+template <int KMAX>
+int launch_combine(const float* y, const int32_t* row_of, const float* w, int64_t T, int k,
+                   int64_t H, bool bf16, void* out, hipStream_t s) {
+  const unsigned grid = (unsigned)((T * (H >> 3) + 255) / 256);
+  if (bf16)
+    hipLaunchKernelGGL((k_combine<KMAX, true>), dim3(grid), dim3(256), 0, s, y, row_of, w, T, k,
+                       H, out);
+  else
+    hipLaunchKernelGGL((k_combine<KMAX, false>), dim3(grid), dim3(256), 0, s, y, row_of, w, T, k,
+                       H, out);
+  return nv_launch_status();
+}
+
 }  // namespace
 
 extern "C" {
@@ -203,6 +266,23 @@ int moe_route(const float* logits, int64_t T, int64_t E, int64_t k, int32_t* top
     hipLaunchKernelGGL(k_scatter, dim3((unsigned)nblk), dim3(kTok), 0, s, topk_ids, T, (int)E,
                        (int)k, cnt, expert_offsets, gather_rows, row_of);
   return nv_launch_status();
+}
+
+int moe_combine(const float* y, const int32_t* row_of, const float* topk_weights, int64_t T,
+                int64_t k, int64_t H, int out_dtype, void* out, void* stream) {
+  NV_RETURN_IF(out_dtype != NVFP4_IN_F32 && out_dtype != NVFP4_IN_BF16, NVFP4_ERR_DTYPE);
+  NV_RETURN_IF(T < 0 || k < 1 || k > kMaxK || H <= 0 || H % 8 || T * (H >> 3) > (1LL << 38),
+               NVFP4_ERR_SHAPE);
+  if (T == 0) return NVFP4_OK;
+  NV_RETURN_IF(!y || !row_of || !topk_weights || !out, NVFP4_ERR_NULL);
+  NV_RETURN_IF(!nv_aligned16(y) || !nv_aligned16(out), NVFP4_ERR_ALIGN);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool bf = out_dtype == NVFP4_IN_BF16;
+  if (k <= 1) return launch_combine<1>(y, row_of, topk_weights, T, (int)k, H, bf, out, s);
+  if (k <= 2) return launch_combine<2>(y, row_of, topk_weights, T, (int)k, H, bf, out, s);
+  if (k <= 4) return launch_combine<4>(y, row_of, topk_weights, T, (int)k, H, bf, out, s);
+  if (k <= 8) return launch_combine<8>(y, row_of, topk_weights, T, (int)k, H, bf, out, s);
+  return launch_combine<16>(y, row_of, topk_weights, T, (int)k, H, bf, out, s);
 }
 
 }  // extern "C"

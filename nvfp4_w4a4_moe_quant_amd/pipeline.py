@@ -11,6 +11,9 @@ blog post's section "Two fixes, on two different sides"):
                           bf16 and max|H|)
     nvfp4_quantize(H, amax_in = max|H|, stats) -> rac_select_residual(H)
     w4a4_grouped_gemm_rac(down) -> Y (FP32, rows in expert order)
+    moe_combine(Y, row_of, routing weights) -> token-order output (moe_block)
+GraphedMoEBlock captures the whole block once as a HIP graph for fixed
+shapes (decode), so a step replays every kernel with no host work per launch.
 Weights are quantized once, per expert and projection, by the same
 nvfp4_quantize (every engine quantizes the synchronized weights the same way:
 blog post, section "The failure mode").
@@ -97,6 +100,46 @@ def moe_forward(x: torch.Tensor, logits: torch.Tensor, wgu: QuantWeights, wd: Qu
     h_in = quantize_input(h, n_sel_h, amax_in=amax_h)
     y = gemm(h_in, wd, rt.expert_offsets, rows)
     return dict(route=rt, x_in=x_in, h=h, amax_h=amax_h, h_in=h_in, y=y)
+
+
+def moe_block(x: torch.Tensor, logits: torch.Tensor, wgu: QuantWeights, wd: QuantWeights,
+              topk: int, n_sel_x: Optional[int], n_sel_h: Optional[int],
+              out_dtype: torch.dtype = torch.bfloat16) -> Dict:
+    """The full MoE FFN block: moe_forward, then the weighted combine."""
+    d = moe_forward(x, logits, wgu, wd, topk, n_sel_x, n_sel_h)
+    d["out"] = L.moe_combine(d["y"], d["route"].row_of, d["route"].topk_weights,
+                             out_dtype=out_dtype)
+    return d
+
+
+class GraphedMoEBlock:
+    """moe_block captured once as a HIP graph (torch.cuda.CUDAGraph) for fixed
+    T, H, E.  A call copies the inputs into the graph's static buffers and
+    replays it; the returned tensor is the graph's static output, overwritten
+    by the next call.  Every kernel of the block only reads device memory the
+    graph owns or the caller's weights, and nothing in it is a memset node."""
+
+    def __init__(self, wgu: QuantWeights, wd: QuantWeights, topk: int, n_sel_x: Optional[int],
+                 n_sel_h: Optional[int], T: int, E: int, x_dtype: torch.dtype, device,
+                 out_dtype: torch.dtype = torch.bfloat16, warmup: int = 2):
+        self.x = torch.zeros((T, wgu.K), dtype=x_dtype, device=device)
+        self.logits = torch.zeros((T, E), dtype=torch.float32, device=device)
+        args = (wgu, wd, topk, n_sel_x, n_sel_h, out_dtype)
+        side = torch.cuda.Stream(device)
+        side.wait_stream(torch.cuda.current_stream(device))
+        with torch.cuda.stream(side):
+            for _ in range(warmup):
+                moe_block(self.x, self.logits, *args)
+        torch.cuda.current_stream(device).wait_stream(side)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.out = moe_block(self.x, self.logits, *args)["out"]
+
+    def __call__(self, x: torch.Tensor, logits: torch.Tensor) -> torch.Tensor:
+        self.x.copy_(x)
+        self.logits.copy_(logits)
+        self.graph.replay()
+        return self.out
 
 
 class NVFP4WeightFakeQuant(torch.autograd.Function):

@@ -170,3 +170,16 @@ def test_qdq_validation(lib):
     assert d(rows=-1) == ESHAPE
     assert d(codes=FAKE_MIS) == EALIGN
     assert d(rows=0, codes=None) == OK
+
+
+def test_combine_validation(lib):
+    def c(y=FAKE, ro=FAKE, w=FAKE, T=4, k=2, H=32, od=1, out=FAKE):
+        return lib.moe_combine(y, ro, w, T, k, H, od, out, None)
+    assert c(y=None) == ENULL
+    assert c(w=None) == ENULL
+    assert c(od=2) == EDTYPE
+    assert c(H=20) == ESHAPE                        # H % 8
+    assert c(k=0) == ESHAPE
+    assert c(k=17) == ESHAPE
+    assert c(out=FAKE_MIS) == EALIGN
+    assert c(T=0, y=None) == OK
