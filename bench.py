@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--cpu-baseline", type=int, default=1)
     ap.add_argument("--comparators", type=int, default=1,
                     help="also time RAC-off NVFP4 and FP8 W8A8 steps")
+    ap.add_argument("--extras", type=int, default=1,
+                    help="MoE workloads: also time the full block (weighted combine), a "
+                         "16-token decode call eager vs HIP-graph replay, and the trainer-side "
+                         "weight fake-quant")
     ap.add_argument("--fp8-library-reference", type=int, default=0,
                     help="also time the vendor FP8 GEMM (hipBLASLt through torch._scaled_mm, "
                          "row/column scales, bf16 out) on the dense shape of each GEMM: a "
@@ -240,6 +244,8 @@ def main():
         res["comparators"] = comparators(w, timed, step, step_fp8, seg, ms_step, rac, NEV)
         if args.fp8_library_reference:
             res["comparators"]["fp8_dense_library_reference"] = library_fp8_reference(w, dev)
+    if args.extras and w.kind == "moe":
+        res.update(moe_extras(w, dev, x, lg, wgu, wd, nsx, nsh, timed, step, ms_step, NEV))
     if "bytes" in dom:  # HBM-bound (decode shape): GB/s on the bytes the GEMM must move
         ach = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "kernel": dom["name"], "achieved": round(ach, 3),
@@ -303,6 +309,80 @@ def comparators(w, timed, step, step_fp8, seg, ms_step, rac, nev):
                                gemm_us=round(t[1] * 1e3, 2),
                                gemm_tflops=round(f / t[1] / 1e9, 1),
                                nvfp4_rac_step_over_fp8_step=round(ms_step / ms_f8, 4))
+    return out
+
+
+def moe_extras(w, dev, x, lg, wgu, wd, nsx, nsh, timed, step, ms_step, nev):
+    """Full MoE block (with the weighted combine), decode latency eager vs
+    HIP-graph replay, and the trainer-side weight fake-quant."""
+    import torch
+
+    from nvfp4_w4a4_moe_quant_amd import _lib as L
+    from nvfp4_w4a4_moe_quant_amd import pipeline as P
+
+    out = {}
+    # full block: the step plus the combine (bf16 out), and the combine alone
+    def block_step(ev):
+        x_in, h_in, y, rt = step(ev)
+        o = L.moe_combine(y, rt.row_of, rt.topk_weights, out_dtype=torch.bfloat16)
+        ev[nev - 1].record()
+        return y, rt, o
+    (y, rt, _), ms_block, _ = timed(block_step)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for _ in range(3):
+        L.moe_combine(y, rt.row_of, rt.topk_weights, out_dtype=torch.bfloat16)
+    ev[0].record()
+    for _ in range(20):
+        L.moe_combine(y, rt.row_of, rt.topk_weights, out_dtype=torch.bfloat16)
+    ev[1].record()
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) / 20 * 1e3
+    rows = w.T * w.topk
+    cbytes = rows * w.H * 4 + w.T * w.topk * 8 + w.T * w.H * 2
+    out["moe_block"] = dict(ms_per_step_with_combine=round(ms_block, 4),
+                            combine_us=round(us, 2), combine_bytes=cbytes,
+                            combine_gbs=round(cbytes / us / 1e3, 1),
+                            combine_frac_hbm=round(cbytes / us / 1e3 / PEAK_HBM_GBS, 4))
+    # decode: 16 tokens through the same layer, one call at a time
+    Td = 16
+    xd, lgd = x[:Td].contiguous(), lg[:Td].contiguous()
+    args = (wgu, wd, w.topk, w.H // 2 if nsx else None, w.I // 2 if nsh else None)
+    for _ in range(5):
+        P.moe_block(xd, lgd, *args)
+    torch.cuda.synchronize()
+    n = 50
+    t0 = time.perf_counter()
+    for _ in range(n):
+        P.moe_block(xd, lgd, *args)
+    torch.cuda.synchronize()
+    eager_us = (time.perf_counter() - t0) / n * 1e6
+    g = P.GraphedMoEBlock(*args, T=Td, E=w.E, x_dtype=x.dtype, device=dev)
+    for _ in range(5):
+        g(xd, lgd)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        g(xd, lgd)
+    torch.cuda.synchronize()
+    graph_us = (time.perf_counter() - t0) / n * 1e6
+    out["decode_graph"] = dict(tokens=Td, eager_us_per_call=round(eager_us, 1),
+                               graph_us_per_call=round(graph_us, 1),
+                               speedup=round(eager_us / graph_us, 3))
+    # trainer-side fake-quant of the gate/up weight bank (bf16 -> bf16)
+    wb = (torch.randn((w.E * 2 * w.I, w.H), device=dev) * 0.02).to(torch.bfloat16)
+    for _ in range(2):
+        L.nvfp4_qdq(wb, out_dtype=torch.bfloat16)
+    ev[0].record()
+    for _ in range(5):
+        L.nvfp4_qdq(wb, out_dtype=torch.bfloat16)
+    ev[1].record()
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) / 5 * 1e3
+    qbytes = wb.numel() * 4
+    out["trainer_qdq"] = dict(shape=list(wb.shape), us=round(us, 1), bytes=qbytes,
+                              gbs=round(qbytes / us / 1e3, 1),
+                              frac_hbm=round(qbytes / us / 1e3 / PEAK_HBM_GBS, 4))
+    del wb
     return out
 
 
