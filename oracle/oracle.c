@@ -357,9 +357,11 @@ static void gemm_one(int64_t G, int64_t N, int64_t K, const int32_t* offsets,
                      const uint8_t* a_scales, float a_ts,
                      const uint8_t* r_codes, const uint8_t* r_scales, float r_ts,
                      const uint8_t* w_codes, const uint8_t* w_scales,
-                     const float* w_ts, int64_t j, int64_t n, float* out,
-                     int64_t* main_sum, int64_t* res_sum) {
+                     const float* w_ts, const float* a_ts_g, const float* r_ts_g,
+                     int64_t j, int64_t n, float* out, int64_t* main_sum, int64_t* res_sum) {
   int64_t g = group_of(offsets, G, j);
+  if (a_ts_g) a_ts = a_ts_g[g];
+  if (r_ts_g) r_ts = r_ts_g[g];
   int64_t src = gather ? gather[j] : j;
   int64_t wr = g * N + n; /* row of the [G*N, K] weight image */
   int64_t m = dot_int(a_codes, a_scales, src, w_codes, w_scales, wr, K);
@@ -389,7 +391,8 @@ static int32_t* int_image(const uint8_t* codes, const uint8_t* scales,
 /* Full grouped GEMM: out[total_rows, N] (rows in group order), the same
  * definition as gemm_one with the operands decoded once.  src_rows is the
  * number of rows of A (and R); main_sum and res_sum (nullable) receive the
- * exact integer sums. */
+ * exact integer sums.  a_ts_g / r_ts_g (nullable, [G]) replace the scalar
+ * activation and residual tensor scales by per-group ones (per-expert RAC). */
 void or_grouped_gemm(int64_t G, int64_t N, int64_t K, int64_t total_rows,
                      int64_t src_rows, const int32_t* offsets,
                      const int32_t* gather,
@@ -397,7 +400,7 @@ void or_grouped_gemm(int64_t G, int64_t N, int64_t K, int64_t total_rows,
                      const uint8_t* r_codes, const uint8_t* r_scales, float r_ts,
                      const uint8_t* w_codes, const uint8_t* w_scales,
                      const float* w_ts, float* out, int64_t* main_sum,
-                     int64_t* res_sum) {
+                     int64_t* res_sum, const float* a_ts_g, const float* r_ts_g) {
   int32_t* ai = int_image(a_codes, a_scales, src_rows, K);
   int32_t* ri = r_codes ? int_image(r_codes, r_scales, src_rows, K) : NULL;
   int32_t* wi = int_image(w_codes, w_scales, G * N, K);
@@ -413,8 +416,8 @@ void or_grouped_gemm(int64_t G, int64_t N, int64_t K, int64_t total_rows,
     for (k = 0; k < K; k++) m += (int64_t)ai[src * K + k] * w[k];
     if (ri)
       for (k = 0; k < K; k++) rs += (int64_t)ri[src * K + k] * w[k];
-    y = (long double)a_ts * ldexpl((long double)m, -20);
-    if (ri) y += (long double)r_ts * ldexpl((long double)rs, -20);
+    y = (long double)(a_ts_g ? a_ts_g[g] : a_ts) * ldexpl((long double)m, -20);
+    if (ri) y += (long double)(r_ts_g ? r_ts_g[g] : r_ts) * ldexpl((long double)rs, -20);
     y *= (long double)w_ts[g];
     out[idx] = (float)y;
     if (main_sum) main_sum[idx] = m;
@@ -432,13 +435,14 @@ void or_grouped_gemm_sample(int64_t G, int64_t N, int64_t K,
                             const uint8_t* r_codes, const uint8_t* r_scales, float r_ts,
                             const uint8_t* w_codes, const uint8_t* w_scales,
                             const float* w_ts, int64_t n_samples,
-                            const int64_t* rows, const int64_t* cols, float* out) {
+                            const int64_t* rows, const int64_t* cols, float* out,
+                            const float* a_ts_g, const float* r_ts_g) {
   int64_t i;
 #pragma omp parallel for schedule(dynamic, 16)
   for (i = 0; i < n_samples; i++)
     gemm_one(G, N, K, offsets, gather, a_codes, a_scales, a_ts, r_codes,
-             r_scales, r_ts, w_codes, w_scales, w_ts, rows[i], cols[i],
-             out + i, NULL, NULL);
+             r_scales, r_ts, w_codes, w_scales, w_ts, a_ts_g, r_ts_g, rows[i],
+             cols[i], out + i, NULL, NULL);
 }
 
 /* ---------------------------------------------------------- SiLU * mul */
@@ -681,4 +685,50 @@ void or_moe_combine(const float* y, const int32_t* row_of, const float* w, int64
       if (out_bf16) out_bf16[t * H + h] = or_bf16_rne((double)acc);
     }
   }
+}
+
+
+/* ------------------------------------------------------ per-expert RAC */
+
+/* The pages do not say over which rows RAC's channel selection and the
+ * activation tensor scale are taken (blog post, section "Two fixes, on two
+ * different sides").  The per-tensor reading takes one GEMM input tensor;
+ * this is the per-expert one: the grouped rows of each group g, j in
+ * [offsets[g], offsets[g+1]), with input row gather[j] (or j), form their own
+ * tensor -- own amax and tensor scale, own channel statistics, own selection
+ * of n_sel channels, own residual tensor scale -- and each step is exactly
+ * the per-tensor oracle above applied to that tensor.  Outputs are in
+ * grouped row order (codes [rows, K/2], scales [rows, K/16], residual codes
+ * and scales likewise); per-group arrays: s_t[G], score[G, K], chmax[G, K],
+ * selected[G, n_sel], active[G, K/16], s_tr[G] (the selection's residual
+ * scale, max over the selected channels' max|e| / 2688).  score == NULL
+ * quantizes only (no RAC). */
+void or_quantize_rac_grouped(const float* x, int64_t K, const int32_t* offsets, int64_t G,
+                             const int32_t* gather, int64_t n_sel, uint8_t* codes,
+                             uint8_t* scales, float* s_t, int64_t* score, float* chmax,
+                             int32_t* selected, uint8_t* active, uint8_t* res_codes,
+                             uint8_t* res_scales, float* s_tr) {
+  int64_t g, i;
+  uint8_t* mask = (uint8_t*)malloc((size_t)(K > 0 ? K : 1));
+  for (g = 0; g < G; g++) {
+    const int64_t j0 = offsets[g], rows = offsets[g + 1] - offsets[g];
+    float* sub = (float*)malloc(sizeof(float) * (size_t)(rows * K > 0 ? rows * K : 1));
+    float s_tr_res;
+    for (i = 0; i < rows; i++) {
+      const int64_t src = gather ? gather[j0 + i] : j0 + i;
+      memcpy(sub + i * K, x + src * K, sizeof(float) * (size_t)K);
+    }
+    or_quantize(sub, rows, K, K, NULL, codes + j0 * (K / 2), scales + j0 * (K / 16), &s_t[g]);
+    if (score) {
+      or_channel_stats(sub, rows, K, K, codes + j0 * (K / 2), scales + j0 * (K / 16), s_t[g],
+                       score + g * K, chmax + g * K);
+      or_rac_select(score + g * K, chmax + g * K, K, n_sel, selected + g * n_sel, mask,
+                    active + g * (K / 16), &s_tr[g]);
+      or_rac_residual(sub, rows, K, K, codes + j0 * (K / 2), scales + j0 * (K / 16), s_t[g],
+                      mask, res_codes + j0 * (K / 2), res_scales + j0 * (K / 16), &s_tr_res,
+                      NULL);
+    }
+    free(sub);
+  }
+  free(mask);
 }

@@ -57,9 +57,11 @@ _SIGS = {
     "or_rac_select": (None, [_P, _P, _I64, _I64, _P, _P, _P, _P]),
     "or_rac_residual": (None, [_P, _I64, _I64, _I64, _P, _P, _F, _P, _P, _P, _P, _P]),
     "or_grouped_gemm": (None, [_I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _F,
-                               _P, _P, _F, _P, _P, _P, _P, _P, _P]),
+                               _P, _P, _F, _P, _P, _P, _P, _P, _P, _P, _P]),
     "or_grouped_gemm_sample": (None, [_I64, _I64, _I64, _P, _P, _P, _P, _F,
-                                      _P, _P, _F, _P, _P, _P, _I64, _P, _P, _P]),
+                                      _P, _P, _F, _P, _P, _P, _I64, _P, _P, _P, _P, _P]),
+    "or_quantize_rac_grouped": (None, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _P, _P, _P, _P,
+                                       _P, _P, _P, _P]),
     "or_bf16_rne": (ctypes.c_uint16, [ctypes.c_double]),
     "or_silu_mul": (None, [_P, _I64, _I64, _P, _P]),
     "or_route": (None, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
@@ -189,9 +191,17 @@ def rac_residual(x, codes, scales, s_t, mask):
     return rc, rs, float(ts[0]), r
 
 
+def _ts(v):
+    """A tensor scale: a float (per tensor) or an array [G] (per group)."""
+    if np.ndim(v) == 0:
+        return float(v), None
+    return 0.0, _c(v, np.float32)
+
+
 def grouped_gemm(N, K, offsets, gather, a, r, w, *, want_sums=False):
     """a = (codes, scales, s_t) of A [src_rows, K]; r likewise or None;
-    w = (codes [G, N, K/2], scales [G, N, K/16], s_t[G]).
+    w = (codes [G, N, K/2], scales [G, N, K/16], s_t[G]).  The activation and
+    residual tensor scales are floats, or arrays [G] for per-group scales.
     offsets: int32 [G+1]; gather: int32 [total_rows] or None."""
     offsets = _c(offsets, np.int32)
     G = offsets.shape[0] - 1
@@ -205,11 +215,12 @@ def grouped_gemm(N, K, offsets, gather, a, r, w, *, want_sums=False):
     rsum = np.zeros((total, N), np.int64) if want_sums else None
     rc_ = None if r is None else _c(r[0], np.uint8)
     rs_ = None if r is None else _c(r[1], np.uint8)
-    rt = 0.0 if r is None else r[2]
+    at, atg = _ts(a[2])
+    rt, rtg = (0.0, None) if r is None else _ts(r[2])
     lib().or_grouped_gemm(G, N, K, total, src_rows, _p(offsets), _p(gather),
-                          _p(_c(a[0], np.uint8)), _p(_c(a[1], np.uint8)), a[2],
+                          _p(_c(a[0], np.uint8)), _p(_c(a[1], np.uint8)), at,
                           _p(rc_), _p(rs_), rt, _p(wc), _p(ws), _p(wt),
-                          _p(out), _p(ms), _p(rsum))
+                          _p(out), _p(ms), _p(rsum), _p(atg), _p(rtg))
     return (out, ms, rsum) if want_sums else out
 
 
@@ -222,12 +233,13 @@ def grouped_gemm_sample(N, K, offsets, gather, a, r, w, rows, cols):
     out = np.zeros(rows.shape[0], np.float32)
     rc_ = None if r is None else _c(r[0], np.uint8)
     rs_ = None if r is None else _c(r[1], np.uint8)
-    rt = 0.0 if r is None else r[2]
+    at, atg = _ts(a[2])
+    rt, rtg = (0.0, None) if r is None else _ts(r[2])
     lib().or_grouped_gemm_sample(G, N, K, _p(offsets), _p(gather),
-                                 _p(_c(a[0], np.uint8)), _p(_c(a[1], np.uint8)), a[2],
+                                 _p(_c(a[0], np.uint8)), _p(_c(a[1], np.uint8)), at,
                                  _p(rc_), _p(rs_), rt, _p(_c(w[0], np.uint8)),
                                  _p(_c(w[1], np.uint8)), _p(_c(w[2], np.float32)),
-                                 rows.shape[0], _p(rows), _p(cols), _p(out))
+                                 rows.shape[0], _p(rows), _p(cols), _p(out), _p(atg), _p(rtg))
     return out
 
 
@@ -331,6 +343,32 @@ def fp8_grouped_gemm_sample(N, K, offsets, gather, a, w, rows, cols):
                                      _p(_c(w[0], np.uint8)), _p(_c(w[1], np.float32)),
                                      rows.shape[0], _p(rows), _p(cols), _p(out))
     return out
+
+
+def quantize_rac_grouped(x, offsets, gather, n_select):
+    """Per-expert RAC: each group's rows (x[gather[j]] or x[j] for grouped row
+    j) form their own tensor.  n_select None quantizes only.  Returns a dict
+    of grouped-order codes/scales/residual and per-group arrays."""
+    x = _c(x, np.float32)
+    K = x.shape[1]
+    offsets = _c(offsets, np.int32)
+    G = offsets.shape[0] - 1
+    rows = int(offsets[-1])
+    gather = None if gather is None else _c(gather, np.int32)
+    rac = n_select is not None
+    ns = n_select if rac else 0
+    d = dict(codes=np.zeros((rows, K // 2), np.uint8), scales=np.zeros((rows, K // 16), np.uint8),
+             s_t=np.zeros(G, np.float32))
+    if rac:
+        d.update(score=np.zeros((G, K), np.int64), chmax=np.zeros((G, K), np.float32),
+                 selected=np.zeros((G, ns), np.int32), active=np.zeros((G, K // 16), np.uint8),
+                 res_codes=np.zeros((rows, K // 2), np.uint8),
+                 res_scales=np.zeros((rows, K // 16), np.uint8), s_tr=np.zeros(G, np.float32))
+    lib().or_quantize_rac_grouped(
+        _p(x), K, _p(offsets), G, _p(gather), ns, _p(d["codes"]), _p(d["scales"]),
+        _p(d["s_t"]), _p(d.get("score")), _p(d.get("chmax")), _p(d.get("selected")),
+        _p(d.get("active")), _p(d.get("res_codes")), _p(d.get("res_scales")), _p(d.get("s_tr")))
+    return d
 
 
 # ------------------------------------------------------------- composites
