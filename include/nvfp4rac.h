@@ -158,6 +158,41 @@ int moe_route(const float* logits, int64_t T, int64_t E, int64_t k,
               void* stream);
 
 /* ------------------------------------------------------------------------
+ * Per-expert RAC.  The pages leave open over which rows RAC's tensor scale and
+ * channel selection are taken (blog post, section "Two fixes, on two
+ * different sides").  The calls above take one GEMM-input tensor; these take
+ * each expert group on its own: the grouped rows j of group g,
+ * group_offsets[g] <= j < group_offsets[g+1], read from x row gather_rows[j]
+ * (or row j when gather_rows is NULL), form a tensor with its own amax and
+ * tensor scale, channel statistics, selection of n_select channels and
+ * residual tensor scale.  Every step is the per-tensor definition applied to
+ * that tensor.  Outputs are in grouped row order: codes / res_codes
+ * [total_rows, K/2], scales / res_scales [total_rows, K/16]; per group:
+ * tensor_scales / res_tensor_scales [G], channel_score [G, K] (int64),
+ * channel_max [G, K], selected [G, n_select] (ascending per group),
+ * kblock_active [G, K/16].  The GEMM then runs without a gather, with
+ * NVFP4_GEMM_PER_GROUP_SCALES.  Requires 1 <= G <= 65535, K % 16 == 0,
+ * total_rows * K / 16 < 2^31, x 16-byte aligned, ldx % 16 == 0; the
+ * selection needs K <= 16384.  Empty groups get zero tensor scales and the
+ * n_select lowest channels.
+ * ------------------------------------------------------------------------ */
+size_t nvfp4_quantize_grouped_workspace_size(int64_t G, int64_t K);
+int nvfp4_quantize_grouped(const void* x, int in_dtype, int64_t K, int64_t ldx,
+                           const int32_t* group_offsets, int64_t G, int64_t total_rows,
+                           const int32_t* gather_rows, uint8_t* codes, uint8_t* scales,
+                           float* tensor_scales, int64_t* channel_score, float* channel_max,
+                           void* ws, size_t ws_bytes, void* stream);
+size_t rac_select_residual_grouped_workspace_size(int64_t G, int64_t K);
+int rac_select_residual_grouped(const void* x, int in_dtype, int64_t K, int64_t ldx,
+                                const int32_t* group_offsets, int64_t G, int64_t total_rows,
+                                const int32_t* gather_rows, const uint8_t* scales,
+                                const float* tensor_scales, const int64_t* channel_score,
+                                const float* channel_max, int64_t n_select, int32_t* selected,
+                                uint8_t* kblock_active, uint8_t* res_codes, uint8_t* res_scales,
+                                float* res_tensor_scales, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/* ------------------------------------------------------------------------
  * moe_combine -- weighted combine of the expert outputs back to token order
  * (the end of the MoE layer whose expert GEMMs the pages quantize).  For each
  * token t, in slot order s = 0 .. k-1 (the order moe_route writes):
@@ -220,6 +255,10 @@ typedef struct {
 } w4a4_gemm_args_t;
 
 #define NVFP4_GEMM_SKIP_INACTIVE_BLOCKS 1
+/* Per-expert RAC: a_tscale and r_tscale are [G] (group g's tensor scales) and
+ * kblock_active is [G, K/16], as nvfp4_quantize_grouped and
+ * rac_select_residual_grouped write them. */
+#define NVFP4_GEMM_PER_GROUP_SCALES 2
 
 size_t w4a4_grouped_gemm_rac_workspace_size(const w4a4_gemm_args_t* args);
 int w4a4_grouped_gemm_rac(const w4a4_gemm_args_t* args, void* ws, size_t ws_bytes,

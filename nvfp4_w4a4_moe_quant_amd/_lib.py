@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4rac.so")
 NVFP4_IN_F32, NVFP4_IN_BF16 = 0, 1
 NVFP4_EPI_F32, NVFP4_EPI_SILU_MUL_BF16 = 0, 1
 NVFP4_GEMM_SKIP_INACTIVE_BLOCKS = 1
+NVFP4_GEMM_PER_GROUP_SCALES = 2
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -62,6 +63,13 @@ _SIGS = {
     "w4a4_grouped_gemm_rac_workspace_size": (_SZ, [ctypes.POINTER(GemmArgs)]),
     "w4a4_grouped_gemm_rac": (ctypes.c_int, [ctypes.POINTER(GemmArgs), _P, _SZ, _P]),
     "moe_combine": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P, _P]),
+    "nvfp4_quantize_grouped_workspace_size": (_SZ, [_I64, _I64]),
+    "nvfp4_quantize_grouped": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _P, _I64, _I64, _P,
+                                              _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "rac_select_residual_grouped_workspace_size": (_SZ, [_I64, _I64]),
+    "rac_select_residual_grouped": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _P, _I64, _I64,
+                                                   _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P, _P,
+                                                   _P, _SZ, _P]),
     "nvfp4_qdq_workspace_size": (_SZ, [_I64, _I64]),
     "nvfp4_qdq": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _P, ctypes.c_int, _P, _P,
                                  _P, _SZ, _P]),
@@ -189,6 +197,52 @@ def rac_select_residual(x: torch.Tensor, qo: QuantOut, n_select: int) -> RacOut:
     return RacOut(NVFP4(rc, rs, rts), sel, kact)
 
 
+def nvfp4_quantize_grouped(x: torch.Tensor, group_offsets: torch.Tensor, total_rows: int, *,
+                           gather_rows: Optional[torch.Tensor] = None,
+                           stats: bool = False) -> QuantOut:
+    """Per-expert quantization: each group's rows (x[gather[j]] or x[j]) as
+    their own tensor.  Returns grouped-order codes/scales, tscale [G] and, with
+    stats, score [G, K] and channel max [G, K]."""
+    assert x.dim() == 2 and x.stride(1) == 1
+    K = x.shape[1]
+    G = group_offsets.numel() - 1
+    dev = x.device
+    codes = torch.empty((total_rows, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((total_rows, K // 16), dtype=torch.uint8, device=dev)
+    ts = torch.empty(G, dtype=torch.float32, device=dev)
+    score = torch.empty((G, K), dtype=torch.int64, device=dev) if stats else None
+    chmax = torch.empty((G, K), dtype=torch.float32, device=dev) if stats else None
+    L = lib()
+    ws = _ws(L.nvfp4_quantize_grouped_workspace_size(G, K), dev)
+    _check(L.nvfp4_quantize_grouped(_ptr(x), _dtype_code(x), K, x.stride(0), _ptr(group_offsets),
+                                    G, total_rows, _ptr(gather_rows), _ptr(codes), _ptr(scales),
+                                    _ptr(ts), _ptr(score), _ptr(chmax), _ptr(ws), ws.numel(),
+                                    _stream(dev)))
+    return QuantOut(NVFP4(codes, scales, ts), score, chmax)
+
+
+def rac_select_residual_grouped(x: torch.Tensor, qo: QuantOut, group_offsets: torch.Tensor,
+                                total_rows: int, n_select: int, *,
+                                gather_rows: Optional[torch.Tensor] = None) -> RacOut:
+    """Per-expert RAC: selection, masks and residual per group."""
+    K = x.shape[1]
+    G = group_offsets.numel() - 1
+    dev = x.device
+    sel = torch.empty((G, max(n_select, 1)), dtype=torch.int32, device=dev)
+    kact = torch.empty((G, K // 16), dtype=torch.uint8, device=dev)
+    rc = torch.empty((total_rows, K // 2), dtype=torch.uint8, device=dev)
+    rs = torch.empty((total_rows, K // 16), dtype=torch.uint8, device=dev)
+    rts = torch.empty(G, dtype=torch.float32, device=dev)
+    L = lib()
+    ws = _ws(L.rac_select_residual_grouped_workspace_size(G, K), dev)
+    _check(L.rac_select_residual_grouped(
+        _ptr(x), _dtype_code(x), K, x.stride(0), _ptr(group_offsets), G, total_rows,
+        _ptr(gather_rows), _ptr(qo.q.scales), _ptr(qo.q.tscale), _ptr(qo.channel_score),
+        _ptr(qo.channel_max), n_select, _ptr(sel), _ptr(kact), _ptr(rc), _ptr(rs), _ptr(rts),
+        _ptr(ws), ws.numel(), _stream(dev)))
+    return RacOut(NVFP4(rc, rs, rts), sel[:, :n_select], kact)
+
+
 def moe_route(logits: torch.Tensor, k: int) -> RouteOut:
     assert logits.dtype == torch.float32 and logits.is_contiguous()
     T, E = logits.shape
@@ -212,7 +266,8 @@ def w4a4_grouped_gemm_rac(a: NVFP4, w: NVFP4, group_offsets: torch.Tensor, *, N:
                           epilogue: int = NVFP4_EPI_F32,
                           out: Optional[torch.Tensor] = None,
                           out_amax: Optional[torch.Tensor] = None,
-                          skip_inactive: bool = False) -> torch.Tensor:
+                          skip_inactive: bool = False,
+                          per_group_scales: bool = False) -> torch.Tensor:
     """w: codes [G, N, K/2], scales [G, N, K/16], tscale [G]."""
     dev = a.codes.device
     G = group_offsets.numel() - 1
@@ -229,7 +284,8 @@ def w4a4_grouped_gemm_rac(a: NVFP4, w: NVFP4, group_offsets: torch.Tensor, *, N:
         r_tscale=_ptr(r.tscale if r else None), kblock_active=_ptr(kblock_active),
         w_codes=_ptr(w.codes), w_scales=_ptr(w.scales), w_tscale=_ptr(w.tscale),
         epilogue=epilogue, out=_ptr(out), out_amax=_ptr(out_amax),
-        flags=NVFP4_GEMM_SKIP_INACTIVE_BLOCKS if skip_inactive else 0)
+        flags=(NVFP4_GEMM_SKIP_INACTIVE_BLOCKS if skip_inactive else 0) |
+              (NVFP4_GEMM_PER_GROUP_SCALES if per_group_scales else 0))
     L = lib()
     nbytes = L.w4a4_grouped_gemm_rac_workspace_size(ctypes.byref(args))
     ws = _ws(nbytes, dev) if nbytes else None

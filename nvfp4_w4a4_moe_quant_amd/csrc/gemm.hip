@@ -101,6 +101,7 @@ struct GemmParams {
   int m_slots;  // m-tile slots in the grid
   int n_tiles;
   int skip;     // NVFP4_GEMM_SKIP_INACTIVE_BLOCKS
+  int per_group;  // NVFP4_GEMM_PER_GROUP_SCALES: a_ts, r_ts [G], kact [G, K/16]
 };
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int MINW, bool RAC, bool SILU,
@@ -226,7 +227,10 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
   // residual block activity, 8 blocks (one chunk) per 64-bit word
   if constexpr (RAC) {
     for (int c = tid; c < nchunks; c += kThreads)
-      kact_lds[c] = p.kact ? *reinterpret_cast<const uint64_t*>(p.kact + (int64_t)c * 8) : ~0ull;
+      kact_lds[c] = p.kact ? *reinterpret_cast<const uint64_t*>(
+                                 p.kact + (p.per_group ? (int64_t)grp * (p.K >> 4) : 0) +
+                                 (int64_t)c * 8)
+                           : ~0ull;
   }
 
   // One chunk (8 MFMA steps).  With RSKIP, the residual MFMAs of a step run
@@ -347,8 +351,8 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
   }
 
   // ---- epilogue
-  const float s_ta = *p.a_ts;
-  const float s_tr = RAC ? *p.r_ts : 0.0f;
+  const float s_ta = p.a_ts[p.per_group ? grp : 0];
+  const float s_tr = RAC ? p.r_ts[p.per_group ? grp : 0] : 0.0f;
   const float s_tw = p.w_ts[grp];
   auto yval = [&](int a, int b, int e) -> float {
     float y = s_ta * accm[a][b][e];
@@ -510,7 +514,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void k_gemm3(GemmPara
   const int nchunks = p.K / KC3;
   if constexpr (RAC) {
     for (int c = tid; c < nchunks; c += NT)
-      kact_lds[c] = p.kact ? *reinterpret_cast<const uint32_t*>(p.kact + (int64_t)c * 4) : ~0u;
+      kact_lds[c] = p.kact ? *reinterpret_cast<const uint32_t*>(
+                                 p.kact + (p.per_group ? (int64_t)grp * (p.K >> 4) : 0) +
+                                 (int64_t)c * 4)
+                           : ~0u;
   }
   // fragment bases (in 1 KiB units) of this wave's A, R and W operands
   const int fa0 = (wm * WTM) >> 5, fr0 = (BM + wm * WTM) >> 5, fw0 = (AR + wn * WTN) >> 5;
@@ -562,8 +569,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void k_gemm3(GemmPara
     __syncthreads();
   }
 
-  const float s_ta = *p.a_ts;
-  const float s_tr = RAC ? *p.r_ts : 0.0f;
+  const float s_ta = p.a_ts[p.per_group ? grp : 0];
+  const float s_tr = RAC ? p.r_ts[p.per_group ? grp : 0] : 0.0f;
   const float s_tw = p.w_ts[grp];
   auto yval = [&](int a, int b, int e) -> float {
     float y = s_ta * accm[a][b][e];
@@ -678,8 +685,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv16(GemmParams p) {
   const int c = lane & 15, q = lane >> 4;
   const int K = p.K;
   const int kw = K / WAVES;  // k per wave
-  const float s_ta = *p.a_ts;
-  const float s_tr = RAC ? *p.r_ts : 0.0f;
+  const float s_ta = p.a_ts[0];  // one group
+  const float s_tr = RAC ? p.r_ts[0] : 0.0f;
   const float s_tw = p.w_ts[0];
   const int m = (int)blockIdx.y * 16 + c;  // A row fed by this lane
   const bool mv = m < p.total_rows;
@@ -872,6 +879,7 @@ int w4a4_grouped_gemm_rac(const w4a4_gemm_args_t* a, void*, size_t, void* stream
   p.out = a->out;
   p.out_amax = a->epilogue == NVFP4_EPI_SILU_MUL_BF16 ? a->out_amax : nullptr;
   p.skip = (a->flags & NVFP4_GEMM_SKIP_INACTIVE_BLOCKS) && a->kblock_active ? 1 : 0;
+  p.per_group = (a->flags & NVFP4_GEMM_PER_GROUP_SCALES) ? 1 : 0;
   const bool rac = a->r_codes != nullptr, gather = a->gather_rows != nullptr;
   if (p.G == 1 && p.total_rows <= kGvMaxRows && p.K % 512 == 0 &&
       a->epilogue == NVFP4_EPI_F32) {

@@ -68,6 +68,46 @@ __global__ __launch_bounds__(kThreads) void k_amax(const void* __restrict__ x, i
   }
 }
 
+// Per-group tensor amax (per-expert RAC): workgroup (p, g) takes part p of
+// the 16-element blocks of group g's rows, read through the gather when one
+// is given, and writes partials[g * gridDim.x + p].  The grid also zeroes the
+// per-group statistics [G, K].
+__global__ __launch_bounds__(kThreads) void k_amax_grouped(
+    const void* __restrict__ x, int bf16, int64_t K, int64_t ldx,
+    const int32_t* __restrict__ goff, const int32_t* __restrict__ gather, int G,
+    float* __restrict__ partials, int64_t* __restrict__ score, uint32_t* __restrict__ chmax) {
+  const int g = blockIdx.y;
+  const int CB = (int)(K >> 4);
+  const int row0 = goff[g];
+  const int nblk = (goff[g + 1] - row0) * CB;
+  float m = 0.0f;
+  for (int b = blockIdx.x * kThreads + threadIdx.x; b < nblk; b += gridDim.x * kThreads) {
+    const int j = row0 + b / CB, cb = b - (b / CB) * CB;
+    const int64_t src = gather ? (int64_t)gather[j] : (int64_t)j;
+    float v[16];
+    nv_load16(x, bf16, src * ldx + (int64_t)cb * 16, v);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(v[i]));
+  }
+  if (score) {
+    const int64_t nwg = (int64_t)gridDim.x * gridDim.y;
+    const int64_t wg = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    for (int64_t k = wg * kThreads + threadIdx.x; k < (int64_t)G * K; k += nwg * kThreads) {
+      score[k] = 0;
+      chmax[k] = 0u;
+    }
+  }
+  __shared__ float red[kThreads / 64];
+  m = nv_wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = red[0];
+    for (int w = 1; w < kThreads / 64; ++w) t = __builtin_fmaxf(t, red[w]);
+    partials[g * gridDim.x + blockIdx.x] = t;
+  }
+}
+
 __global__ void k_zero_stats(int64_t K, int64_t* __restrict__ score, uint32_t* __restrict__ chmax) {
   for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < K;
        k += (int64_t)gridDim.x * blockDim.x) {
@@ -166,10 +206,27 @@ __global__ __launch_bounds__(kQThreads) void k_quant(
     const float* __restrict__ partials, int nparts, const float* __restrict__ amax_in,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ tscale_out,
     int64_t* __restrict__ score, uint32_t* __restrict__ chmax, int tpr, int rpi,
-    int64_t rows_per_split, void* __restrict__ dq_out) {
+    int64_t rows_per_split, void* __restrict__ dq_out, const int32_t* __restrict__ goff,
+    const int32_t* __restrict__ gather) {
   extern __shared__ unsigned char dyn_lds[];
   __shared__ float red[kQThreads / 64];
-  const float amax = workgroup_amax(partials, nparts, amax_in, red);
+  // With goff (per-expert RAC) workgroup z quantizes group z's rows, grouped
+  // rows [goff[z], goff[z+1]) read through the gather, as their own tensor:
+  // its partial maxima, tensor scale and statistics are the group's.
+  int64_t row0 = 0;
+  if (goff) {
+    const int g = blockIdx.z;
+    row0 = goff[g];
+    rows = goff[g + 1] - row0;
+    partials += (int64_t)g * nparts;
+    tscale_out += g;
+    if (kStats) {
+      score += (int64_t)g * K;
+      chmax += (int64_t)g * K;
+    }
+    rows_per_split = (rows + gridDim.y - 1) / gridDim.y;
+  }
+  const float amax = workgroup_amax(partials, nparts, goff ? nullptr : amax_in, red);
   const float s_t = nv_tensor_scale(amax);
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *tscale_out = s_t;
 
@@ -178,8 +235,8 @@ __global__ __launch_bounds__(kQThreads) void k_quant(
   const int cbl = threadIdx.x - sub * tpr;
   const int64_t cb = (int64_t)blockIdx.x * tpr + cbl;
   const bool active = sub < rpi && cb < CB;
-  const int64_t r0 = (int64_t)blockIdx.y * rows_per_split;
-  const int64_t r1 = r0 + rows_per_split < rows ? r0 + rows_per_split : rows;
+  const int64_t r0 = row0 + (int64_t)blockIdx.y * rows_per_split;
+  const int64_t r1 = r0 + rows_per_split < row0 + rows ? r0 + rows_per_split : row0 + rows;
   const int shift = nv_score_shift(s_t);
 
   double acc[16];
@@ -228,7 +285,10 @@ __global__ __launch_bounds__(kQThreads) void k_quant(
       RawBlock<kBf16> b[kIn];
 #pragma unroll
       for (int u = 0; u < kIn; ++u)
-        if (r + u * rpi < r1) b[u].load(x, (r + u * rpi) * ldx + cb * 16);
+        if (r + u * rpi < r1) {
+          const int64_t rr = r + u * rpi;
+          b[u].load(x, (gather ? (int64_t)gather[rr] : rr) * ldx + cb * 16);
+        }
 #pragma unroll
       for (int u = 0; u < kIn; ++u)
         if (r + u * rpi < r1) block(b[u], r + u * rpi);
@@ -286,6 +346,14 @@ __global__ __launch_bounds__(64 * kRankWaves) void k_rank(
     uint16_t* __restrict__ mask16, uint8_t* __restrict__ kact, uint32_t* __restrict__ part_max) {
   __shared__ uint64_t tile[kRankTile];
   __shared__ uint32_t cnt[kRankParts][16];
+  {  // group blockIdx.y (per-expert RAC): its statistics and outputs
+    const int64_t g = blockIdx.y;
+    score_in += g * K;
+    chmax += g * K;
+    mask16 += g * (K >> 4);
+    kact += g * (K >> 4);
+    part_max += g * (K >> 4);
+  }
   const uint64_t* score = reinterpret_cast<const uint64_t*>(score_in);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int part = 4 * w + (lane >> 4);
@@ -379,8 +447,23 @@ __global__ __launch_bounds__(kThreads) void k_residual(
     const uint16_t* __restrict__ mask16, const uint32_t* __restrict__ part_max, int nparts,
     int32_t* __restrict__ selected,
     float* __restrict__ res_ts, uint8_t* __restrict__ res_codes,
-    uint8_t* __restrict__ res_scales) {
+    uint8_t* __restrict__ res_scales, const int32_t* __restrict__ goff,
+    const int32_t* __restrict__ gather, int n_sel) {
   __shared__ uint32_t wred[kThreads / 64];
+  // With goff (per-expert RAC) workgroups y handle group y: grouped rows
+  // [goff[y], goff[y+1]) read through the gather, the group's masks, tensor
+  // scales and selected list.
+  int64_t row0 = 0;
+  if (goff) {
+    const int g = blockIdx.y;
+    row0 = goff[g];
+    rows = goff[g + 1] - row0;
+    mask16 += (int64_t)g * nparts;
+    part_max += (int64_t)g * nparts;
+    tscale += g;
+    res_ts += g;
+    if (selected) selected += (int64_t)g * n_sel;
+  }
   __shared__ uint16_t lmask[kMaxSelectK / 16];  // block masks, so x loads wait on nothing
   float a = 0.0f;
   for (int i = threadIdx.x; i < nparts; i += kThreads) {  // nparts = K / 16 blocks
@@ -464,10 +547,12 @@ __global__ __launch_bounds__(kThreads) void k_residual(
     advance(r2, cb2);
     const bool two = b + stride < nblk;
     float v0[16], v1[16];
-    if (lmask[cb]) nv_load16(x, bf16, r * ldx + cb * 16, v0);
-    if (two && lmask[cb2]) nv_load16(x, bf16, r2 * ldx + cb2 * 16, v1);
-    one(r, cb, v0);
-    if (two) one(r2, cb2, v1);
+    const int64_t j = row0 + r, j2 = row0 + r2;  // grouped rows
+    if (lmask[cb]) nv_load16(x, bf16, (gather ? (int64_t)gather[j] : j) * ldx + cb * 16, v0);
+    if (two && lmask[cb2])
+      nv_load16(x, bf16, (gather ? (int64_t)gather[j2] : j2) * ldx + cb2 * 16, v1);
+    one(j, cb, v0);
+    if (two) one(j2, cb2, v1);
     r = r2;
     cb = cb2;
     advance(r, cb);
@@ -564,11 +649,11 @@ static int quantize_launch(const void* x, int dtype, int64_t rows, int64_t K, in
 #define NV_QUANT_LAUNCH(ST, BF)                                                                 \
   hipLaunchKernelGGL((k_quant<ST, BF>), grid, dim3(kQThreads), ST ? lds : 0, s, x, rows, K, ldx, \
                      partials, nparts, amax_in, codes, scales, tensor_scale, sc, cm, tpr, rpi,   \
-                     rows_per_split, nullptr)
+                     rows_per_split, nullptr, nullptr, nullptr)
 #define NV_QUANT_LAUNCH_DQ(DQ, BF)                                                              \
   hipLaunchKernelGGL((k_quant<false, BF, DQ>), grid, dim3(kQThreads), 0, s, x, rows, K, ldx,    \
                      partials, nparts, amax_in, nullptr, nullptr, tensor_scale, nullptr, nullptr, \
-                     tpr, rpi, rows_per_split, dq_out)
+                     tpr, rpi, rows_per_split, dq_out, nullptr, nullptr)
   if (dq == 1 && bf16) NV_QUANT_LAUNCH_DQ(1, true);
   else if (dq == 1) NV_QUANT_LAUNCH_DQ(1, false);
   else if (dq == 2 && bf16) NV_QUANT_LAUNCH_DQ(2, true);
@@ -709,7 +794,119 @@ int rac_select_residual(const void* x, int dtype, int64_t rows, int64_t K, int64
   const int64_t nblk = rows * (K / 16);
   hipLaunchKernelGGL(k_residual, dim3((unsigned)blocks_for(nblk, 2 * kThreads, 2048)), dim3(kThreads),
                      0, s, x, dtype == NVFP4_IN_BF16, rows, K, ldx, scales, tensor_scale, mask16,
-                     part_max, nrank, selected, res_tensor_scale, res_codes, res_scales);
+                     part_max, nrank, selected, res_tensor_scale, res_codes, res_scales, nullptr,
+                     nullptr, 0);
+  return nv_launch_status();
+}
+
+// ------------------------------------------------------- per-expert RAC
+constexpr int kGroupParts = 8;  // amax partials per group
+
+static int check_grouped(const void* x, int dtype, int64_t K, int64_t ldx, const int32_t* goff,
+                         int64_t G, int64_t total_rows) {
+  NV_RETURN_IF(!goff || (!x && total_rows > 0), NVFP4_ERR_NULL);
+  NV_RETURN_IF(dtype != NVFP4_IN_F32 && dtype != NVFP4_IN_BF16, NVFP4_ERR_DTYPE);
+  NV_RETURN_IF(G < 1 || G > 65535 || total_rows < 0 || K <= 0 || (K & 15) || ldx < K ||
+                   total_rows * (K >> 4) > 0x7fffffffLL,
+               NVFP4_ERR_SHAPE);
+  NV_RETURN_IF((ldx & 15) || !nv_aligned16(x), NVFP4_ERR_ALIGN);
+  return NVFP4_OK;
+}
+
+size_t nvfp4_quantize_grouped_workspace_size(int64_t G, int64_t) {
+  return nv_round256(sizeof(float) * (size_t)(G > 0 ? G : 0) * kGroupParts);
+}
+
+int nvfp4_quantize_grouped(const void* x, int dtype, int64_t K, int64_t ldx,
+                           const int32_t* group_offsets, int64_t G, int64_t total_rows,
+                           const int32_t* gather_rows, uint8_t* codes, uint8_t* scales,
+                           float* tensor_scales, int64_t* channel_score, float* channel_max,
+                           void* ws, size_t ws_bytes, void* stream) {
+  int st = check_grouped(x, dtype, K, ldx, group_offsets, G, total_rows);
+  if (st) return st;
+  NV_RETURN_IF(!tensor_scales || (total_rows > 0 && (!codes || !scales)), NVFP4_ERR_NULL);
+  NV_RETURN_IF((channel_score == nullptr) != (channel_max == nullptr), NVFP4_ERR_NULL);
+  NV_RETURN_IF(!nv_aligned16(codes) ||
+                   (channel_score && ((reinterpret_cast<uintptr_t>(channel_score) & 7) ||
+                                      (reinterpret_cast<uintptr_t>(channel_max) & 3))),
+               NVFP4_ERR_ALIGN);
+  NV_RETURN_IF(!ws || ws_bytes < nvfp4_quantize_grouped_workspace_size(G, K),
+               NVFP4_ERR_WORKSPACE);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool stats = channel_score != nullptr;
+  uint32_t* chm = reinterpret_cast<uint32_t*>(channel_max);
+  float* partials = reinterpret_cast<float*>(ws);
+  const int bf16 = dtype == NVFP4_IN_BF16;
+  hipLaunchKernelGGL(k_amax_grouped, dim3(kGroupParts, (unsigned)G), dim3(kThreads), 0, s, x,
+                     bf16, K, ldx, group_offsets, gather_rows, (int)G, partials,
+                     stats ? channel_score : nullptr, chm);
+  // the column tiles of k_quant; row splits per group from the mean group size
+  const int64_t CB = K / 16;
+  const int tile_max = 16;
+  const int64_t ntile = (CB + tile_max - 1) / tile_max;
+  const int tpr = (int)((CB + ntile - 1) / ntile);
+  const int rpi = kQThreads / tpr;
+  int64_t splits = blocks_for((total_rows + G - 1) / G, (int64_t)rpi * 2, 64);
+  const size_t lds = stats ? (size_t)tpr * 16 * (sizeof(uint64_t) + sizeof(uint32_t)) : 0;
+  const dim3 grid((unsigned)ntile, (unsigned)splits, (unsigned)G);
+  int64_t* sc = stats ? channel_score : nullptr;
+  uint32_t* cm = stats ? chm : nullptr;
+#define NV_QUANT_LAUNCH_G(ST, BF)                                                                \
+  hipLaunchKernelGGL((k_quant<ST, BF>), grid, dim3(kQThreads), ST ? lds : 0, s, x, total_rows, K, \
+                     ldx, partials, kGroupParts, nullptr, codes, scales, tensor_scales, sc, cm,  \
+                     tpr, rpi, (int64_t)0, nullptr, group_offsets, gather_rows)
+  if (stats && bf16) NV_QUANT_LAUNCH_G(true, true);
+  else if (stats) NV_QUANT_LAUNCH_G(true, false);
+  else if (bf16) NV_QUANT_LAUNCH_G(false, true);
+  else NV_QUANT_LAUNCH_G(false, false);
+#undef NV_QUANT_LAUNCH_G
+  return nv_launch_status();
+}
+
+size_t rac_select_residual_grouped_workspace_size(int64_t G, int64_t K) {
+  return rac_ws_layout((G > 0 ? G : 0) * K).total;
+}
+
+int rac_select_residual_grouped(const void* x, int dtype, int64_t K, int64_t ldx,
+                                const int32_t* group_offsets, int64_t G, int64_t total_rows,
+                                const int32_t* gather_rows, const uint8_t* scales,
+                                const float* tensor_scales, const int64_t* channel_score,
+                                const float* channel_max, int64_t n_select, int32_t* selected,
+                                uint8_t* kblock_active, uint8_t* res_codes, uint8_t* res_scales,
+                                float* res_tensor_scales, void* ws, size_t ws_bytes,
+                                void* stream) {
+  int st = check_grouped(x, dtype, K, ldx, group_offsets, G, total_rows);
+  if (st) return st;
+  NV_RETURN_IF(!tensor_scales || !channel_score || !channel_max || !kblock_active ||
+                   !res_tensor_scales,
+               NVFP4_ERR_NULL);
+  NV_RETURN_IF(total_rows > 0 && (!scales || !res_codes || !res_scales), NVFP4_ERR_NULL);
+  NV_RETURN_IF(n_select < 0 || n_select > K || K > kMaxSelectK, NVFP4_ERR_SHAPE);
+  NV_RETURN_IF(n_select > 0 && !selected, NVFP4_ERR_NULL);
+  NV_RETURN_IF(!nv_aligned16(res_codes) || (reinterpret_cast<uintptr_t>(channel_score) & 7) ||
+                   (reinterpret_cast<uintptr_t>(channel_max) & 3),
+               NVFP4_ERR_ALIGN);
+  NV_RETURN_IF(!ws || ws_bytes < rac_select_residual_grouped_workspace_size(G, K) ||
+                   (reinterpret_cast<uintptr_t>(ws) & 3),
+               NVFP4_ERR_WORKSPACE);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const RacWs L = rac_ws_layout(G * K);
+  unsigned char* base = reinterpret_cast<unsigned char*>(ws);
+  uint16_t* mask16 = reinterpret_cast<uint16_t*>(base + L.mask_off);
+  uint32_t* part_max = reinterpret_cast<uint32_t*>(base + L.max_off);
+  const int nrank = (int)(K / 16);
+  hipLaunchKernelGGL(k_rank, dim3(nrank, (unsigned)G), dim3(64 * kRankWaves), 0, s, channel_score,
+                     reinterpret_cast<const uint32_t*>(channel_max), (int)K, (int)n_select,
+                     mask16, kblock_active, part_max);
+  st = nv_launch_status();
+  if (st) return st;
+  // at least one workgroup per group: it writes the group's selected[] and
+  // residual tensor scale
+  const int64_t per_group = ((total_rows + G - 1) / G) * (K / 16);
+  hipLaunchKernelGGL(k_residual, dim3((unsigned)blocks_for(per_group, 2 * kThreads, 256), (unsigned)G),
+                     dim3(kThreads), 0, s, x, dtype == NVFP4_IN_BF16, total_rows, K, ldx, scales,
+                     tensor_scales, mask16, part_max, nrank, selected, res_tensor_scales,
+                     res_codes, res_scales, group_offsets, gather_rows, (int)n_select);
   return nv_launch_status();
 }
 

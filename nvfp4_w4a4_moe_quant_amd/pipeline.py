@@ -53,6 +53,7 @@ class GemmInput(NamedTuple):
     qo: L.QuantOut
     rac: Optional[L.RacOut]
     skip_inactive: bool = False
+    per_group: bool = False  # per-expert tensor scales (quantize_input_grouped)
 
 
 # Below this selected fraction of channels, many 16-blocks are likely to hold
@@ -70,6 +71,20 @@ def quantize_input(x: torch.Tensor, n_select: Optional[int],
     return GemmInput(qo, rac, skip)
 
 
+def quantize_input_grouped(x: torch.Tensor, offsets: torch.Tensor, total_rows: int,
+                           n_select: Optional[int],
+                           gather: Optional[torch.Tensor] = None) -> GemmInput:
+    """Per-expert RAC: each expert's rows (gathered from x when gather is
+    given) are quantized and compensated as their own tensor; the GEMM then
+    runs on grouped rows without a gather."""
+    qo = L.nvfp4_quantize_grouped(x, offsets, total_rows, gather_rows=gather,
+                                  stats=n_select is not None)
+    rac = (L.rac_select_residual_grouped(x, qo, offsets, total_rows, n_select, gather_rows=gather)
+           if n_select is not None else None)
+    skip = n_select is not None and n_select <= SKIP_BELOW_FRACTION * x.shape[1]
+    return GemmInput(qo, rac, skip, True)
+
+
 def gemm(inp: GemmInput, wq: QuantWeights, offsets: torch.Tensor, total_rows: int, *,
          gather: Optional[torch.Tensor] = None, epilogue: int = L.NVFP4_EPI_F32,
          out_amax: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -77,7 +92,8 @@ def gemm(inp: GemmInput, wq: QuantWeights, offsets: torch.Tensor, total_rows: in
         inp.qo.q, wq.w, offsets, N=wq.N, K=wq.K, total_rows=total_rows, gather_rows=gather,
         r=inp.rac.r if inp.rac else None,
         kblock_active=inp.rac.kblock_active if inp.rac else None,
-        epilogue=epilogue, out_amax=out_amax, skip_inactive=inp.skip_inactive)
+        epilogue=epilogue, out_amax=out_amax, skip_inactive=inp.skip_inactive,
+        per_group_scales=inp.per_group)
 
 
 def dense_forward(x: torch.Tensor, wq: QuantWeights, n_select: Optional[int]) -> Dict:
@@ -89,15 +105,25 @@ def dense_forward(x: torch.Tensor, wq: QuantWeights, n_select: Optional[int]) ->
 
 
 def moe_forward(x: torch.Tensor, logits: torch.Tensor, wgu: QuantWeights, wd: QuantWeights,
-                topk: int, n_sel_x: Optional[int], n_sel_h: Optional[int]) -> Dict:
+                topk: int, n_sel_x: Optional[int], n_sel_h: Optional[int],
+                per_expert: bool = False) -> Dict:
+    """per_expert: RAC (and the activation tensor scales) per expert group
+    instead of per GEMM-input tensor; the gate/up input is then quantized per
+    expert from the gathered token rows."""
     T = x.shape[0]
     rt = L.moe_route(logits, topk)
     rows = T * topk
-    x_in = quantize_input(x, n_sel_x)
     amax_h = torch.zeros(1, dtype=torch.float32, device=x.device)
-    h = gemm(x_in, wgu, rt.expert_offsets, rows, gather=rt.gather_rows,
-             epilogue=L.NVFP4_EPI_SILU_MUL_BF16, out_amax=amax_h)
-    h_in = quantize_input(h, n_sel_h, amax_in=amax_h)
+    if per_expert:
+        x_in = quantize_input_grouped(x, rt.expert_offsets, rows, n_sel_x, gather=rt.gather_rows)
+        h = gemm(x_in, wgu, rt.expert_offsets, rows, epilogue=L.NVFP4_EPI_SILU_MUL_BF16,
+                 out_amax=amax_h)
+        h_in = quantize_input_grouped(h, rt.expert_offsets, rows, n_sel_h)
+    else:
+        x_in = quantize_input(x, n_sel_x)
+        h = gemm(x_in, wgu, rt.expert_offsets, rows, gather=rt.gather_rows,
+                 epilogue=L.NVFP4_EPI_SILU_MUL_BF16, out_amax=amax_h)
+        h_in = quantize_input(h, n_sel_h, amax_in=amax_h)
     y = gemm(h_in, wd, rt.expert_offsets, rows)
     return dict(route=rt, x_in=x_in, h=h, amax_h=amax_h, h_in=h_in, y=y)
 

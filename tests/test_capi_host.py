@@ -183,3 +183,29 @@ def test_combine_validation(lib):
     assert c(k=17) == ESHAPE
     assert c(out=FAKE_MIS) == EALIGN
     assert c(T=0, y=None) == OK
+
+
+def test_grouped_rac_validation(lib):
+    def q(x=FAKE, dt=1, K=32, ldx=32, off=FAKE, G=2, rows=8, codes=FAKE, ts=FAKE, ws=FAKE,
+          wsb=1 << 20):
+        return lib.nvfp4_quantize_grouped(x, dt, K, ldx, off, G, rows, None, codes, FAKE, ts,
+                                          None, None, ws, wsb, None)
+    assert q(off=None) == ENULL
+    assert q(ts=None) == ENULL
+    assert q(G=0) == ESHAPE
+    assert q(G=70000) == ESHAPE
+    assert q(K=24, ldx=32) == ESHAPE
+    assert q(dt=5) == EDTYPE
+    assert q(x=FAKE_MIS) == EALIGN
+    assert q(ws=None) == EWS
+
+    def r(nsel=16, K=32, sel=FAKE, ws=FAKE, wsb=1 << 20, kact=FAKE):
+        return lib.rac_select_residual_grouped(FAKE, 1, K, K, FAKE, 2, 8, None, FAKE, FAKE, FAKE,
+                                               FAKE, nsel, sel, kact, FAKE, FAKE, FAKE, ws, wsb,
+                                               None)
+    assert r(nsel=33) == ESHAPE
+    assert r(sel=None) == ENULL
+    assert r(kact=None) == ENULL
+    assert r(K=32768) == ESHAPE
+    assert r(ws=None) == EWS
+    assert r(wsb=16) == EWS
