@@ -146,6 +146,24 @@ def main():
         ev[2].record()
         return x_in, None, y, None
 
+    def step_pe(ev):
+        """Per-expert RAC: each expert's gathered rows quantized and
+        compensated as their own tensor, GEMMs with per-group scales."""
+        amax_h.zero_()
+        ev[0].record()
+        rt = L.moe_route(lg, w.topk)
+        ev[1].record()
+        x_in = P.quantize_input_grouped(x, rt.expert_offsets, rows, nsx, gather=rt.gather_rows)
+        ev[2].record()
+        h = P.gemm(x_in, wgu, rt.expert_offsets, rows, epilogue=L.NVFP4_EPI_SILU_MUL_BF16,
+                   out_amax=amax_h)
+        ev[3].record()
+        h_in = P.quantize_input_grouped(h, rt.expert_offsets, rows, nsh)
+        ev[4].record()
+        y = P.gemm(h_in, wd, rt.expert_offsets, rows)
+        ev[5].record()
+        return y
+
     def step_fp8(ev):
         """FP8 W8A8 comparator: the same routing, per-row E4M3 activations."""
         if w.kind == "moe":
@@ -241,7 +259,8 @@ def main():
 
     value = flops / (ms_step * 1e-3) / 1e12
     if cmp_:
-        res["comparators"] = comparators(w, timed, step, step_fp8, seg, ms_step, rac, NEV)
+        res["comparators"] = comparators(w, timed, step, step_fp8, seg, ms_step, rac, NEV,
+                                         step_pe if w.kind == "moe" else None)
         if args.fp8_library_reference:
             res["comparators"]["fp8_dense_library_reference"] = library_fp8_reference(w, dev)
     if args.extras and w.kind == "moe":
@@ -280,7 +299,7 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def comparators(w, timed, step, step_fp8, seg, ms_step, rac, nev):
+def comparators(w, timed, step, step_fp8, seg, ms_step, rac, nev, step_pe=None):
     """RAC-off NVFP4 and FP8 W8A8 steps on the same inputs and weights."""
     out = {}
     if rac:
@@ -289,6 +308,13 @@ def comparators(w, timed, step, step_fp8, seg, ms_step, rac, nev):
         out["nvfp4_rac_off"] = dict(ms_per_step=round(ms_naive, 4),
                                     gemm_first_us=round(seg(gi, ev_n) * 1e3, 2),
                                     rac_step_overhead=round(ms_step / ms_naive - 1.0, 4))
+        if step_pe is not None:
+            _, ms_pe, ev_p = timed(step_pe)
+            out["nvfp4_rac_per_expert"] = dict(
+                ms_per_step=round(ms_pe, 4),
+                stages_us=[round(seg(i, ev_p) * 1e3, 2) for i in range(nev - 1)],
+                stages=["route", "quantize+RAC X per expert (gathered)", "gate/up GEMM",
+                        "quantize+RAC H per expert", "down GEMM"])
     _, ms_f8, ev_f = timed(step_fp8)
     if w.kind == "moe":
         rows = w.T * w.topk
