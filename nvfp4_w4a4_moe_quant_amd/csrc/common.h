@@ -164,34 +164,49 @@ __device__ __forceinline__ void nv_decode8(uint32_t w, float* g) {
 
 // ---------------------------------------------------------- grouped tiles
 
-// Tile of a grouped-GEMM workgroup: group `grp` (-1 past the real tile count),
-// m-tile `local` inside the group, n-tile `nt`.  The grid holds m_slots x
-// n_tiles workgroups, m_slots an upper bound on the groups' m-tiles.
-//  * The workgroup id is remapped so that consecutive tile indices run on one
-//    XCD (the hardware deals workgroups round-robin over the eight XCDs) and
-//    share its L2.
+// Tile of a grouped-GEMM workgroup: group `grp` (-1 for a surplus
+// workgroup), m-tile `local` inside the group, n-tile `nt`.  The grid holds
+// m_slots x n_tiles workgroups, m_slots an upper bound on the groups'
+// m-tiles; the real count is only known on the device.
+//  * A first wave-wide pass sums the groups' m-tiles, so the real tiles --
+//    not the grid's upper bound -- are split evenly over the eight XCDs (the
+//    hardware deals workgroups round-robin over them).  Each XCD gets one
+//    contiguous range of tile indices, so consecutive tiles run on one XCD
+//    and share its L2; workgroups past their XCD's share exit.
 //  * Inside a group the m-tiles vary fastest: the workgroups that read one W
 //    tile (one n-tile of one group) are adjacent.
-//  * A wave scan over per-group tile counts finds the group; every wave of the
+//  * A second wave scan finds the group of the tile; every wave of the
 //    workgroup computes the same result.
 struct NvTile {
   int grp, local, nt;
 };
 
+__device__ __forceinline__ int nv_group_tiles(const int32_t* offsets, int G, int g, int bm) {
+  return g < G ? (offsets[g + 1] - offsets[g] + bm - 1) / bm : 0;
+}
+
 __device__ __forceinline__ NvTile nv_find_tile(const int32_t* offsets, int G, int bm,
                                                int m_slots, int n_tiles) {
+  (void)m_slots;
   const int lane = threadIdx.x & 63;
-  const int nblocks = m_slots * n_tiles;
-  const int bid = blockIdx.x;
-  const int per = nblocks / 8, rem = nblocks % 8, xcd = bid % 8;
-  const int L = xcd * per + (xcd < rem ? xcd : rem) + bid / 8;
-  const int mt = L / n_tiles;
   NvTile t{-1, 0, 0};
+  int total = 0;
+  for (int c = 0; c < G; c += 64) {
+    int v = nv_group_tiles(offsets, G, c + lane, bm);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    total += v;
+  }
+  const int nblocks = total * n_tiles;  // real tiles
+  const int bid = blockIdx.x;
+  const int per = nblocks / 8, rem = nblocks % 8, xcd = bid % 8, li = bid / 8;
+  if (li >= per + (xcd < rem ? 1 : 0)) return t;
+  const int L = xcd * per + (xcd < rem ? xcd : rem) + li;
+  const int mt = L / n_tiles;
   int run = 0;
   for (int c = 0; c < G; c += 64) {
     const int g = c + lane;
-    int tiles = 0;
-    if (g < G) tiles = (offsets[g + 1] - offsets[g] + bm - 1) / bm;
+    const int tiles = nv_group_tiles(offsets, G, g, bm);
     int inc = tiles;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
