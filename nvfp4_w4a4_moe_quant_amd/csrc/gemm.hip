@@ -104,8 +104,10 @@ struct GemmParams {
   int per_group;  // NVFP4_GEMM_PER_GROUP_SCALES: a_ts, r_ts [G], kact [G, K/16]
 };
 
+// CPB chunks are computed between two barriers; NSTAGE LDS buffers hold the
+// CPB chunks being computed and the NSTAGE - CPB chunks in flight.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int MINW, bool RAC, bool SILU,
-          bool GATHER, bool RSKIP = true>
+          bool GATHER, bool RSKIP = true, int CPB = 1>
 __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
   static_assert(WAVES_M * WAVES_N == 4, "4 waves");
   constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
   constexpr int NSI = ROWS * 2 / kThreads;  // 4-byte scale words per thread per chunk
   constexpr int STAGE_CODES = ROWS * CODE_ROW;
   constexpr int STAGE = STAGE_CODES + ROWS * SCALE_ROW;
-  static_assert(NSTAGE >= 2 && (NSTAGE - 2) * (NPI + NSI) <= 63, "vmcnt range");
+  static_assert(NSTAGE >= 2 * CPB && (NSTAGE - 2 * CPB) * (NPI + NSI) <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * STAGE];
   __shared__ uint64_t kact_lds[kMaxKChunks];
 
@@ -323,31 +325,38 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
     }
   };
 
-  // NSTAGE-deep pipeline: chunk ch + NSTAGE - 1 is in flight while chunk ch
-  // is computed; before the barrier that ends iteration ch, chunk ch + 1 must
-  // have landed, i.e. at most the DMA of the later chunks may be outstanding.
+  // NSTAGE-deep pipeline, CPB chunks per barrier: chunks ch .. ch+CPB-1 are
+  // computed while chunks up to ch + NSTAGE - 1 are in flight; before the
+  // barrier that ends the iteration, chunks ch+CPB .. ch+2CPB-1 must have
+  // landed, i.e. at most the DMA of the later chunks may be outstanding.
   constexpr int PER_CHUNK = NPI + NSI;
+  constexpr int AHEAD = NSTAGE - CPB;  // chunks in flight while CPB are computed
 #pragma unroll
-  for (int c = 0; c < NSTAGE - 1; ++c)
+  for (int c = 0; c < AHEAD; ++c)
     if (c < nchunks) issue(c, c);
-  if (nchunks > 1 && NSTAGE > 2)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NSTAGE - 2) * PER_CHUNK) : "memory");
+  if (nchunks > CPB && NSTAGE > 2 * CPB)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NSTAGE - 2 * CPB) * PER_CHUNK) : "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  int buf = 0;
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int nxt = ch + NSTAGE - 1;
-    if (nxt < nchunks) issue(nxt, nxt % NSTAGE);
+  for (int ch = 0; ch < nchunks; ch += CPB) {
+#pragma unroll
+    for (int u = 0; u < CPB; ++u) {
+      const int nxt = ch + AHEAD + u;
+      if (nxt < nchunks) issue(nxt, nxt % NSTAGE);
+    }
     // A wave whose rows all lie past the group's end (the padded half of an
     // expert's last tile) has nothing to compute; it still loads and syncs.
-    if (wave_live) compute(ch, lds + buf * STAGE);
-    if (nxt < nchunks && NSTAGE > 2)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NSTAGE - 2) * PER_CHUNK) : "memory");
+    if (wave_live) {
+#pragma unroll
+      for (int u = 0; u < CPB; ++u)
+        if (ch + u < nchunks) compute(ch + u, lds + ((ch + u) % NSTAGE) * STAGE);
+    }
+    if (ch + AHEAD + CPB - 1 < nchunks && NSTAGE > 2 * CPB)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NSTAGE - 2 * CPB) * PER_CHUNK) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    buf = buf + 1 == NSTAGE ? 0 : buf + 1;
   }
 
   // ---- epilogue
@@ -636,7 +645,7 @@ int launch3(GemmParams& p, hipStream_t s) {
 }
 
 template <int BM, int BN, int WM, int WN, int NS, int MINW, bool RAC, bool SILU, bool GATHER,
-          bool RSKIP = true>
+          bool RSKIP = true, int CPB = 1>
 int launch_t(GemmParams& p, hipStream_t s) {
   constexpr int rows = (RAC ? 2 * BM : BM) + BN;
   if constexpr (rows % 128 != 0) {
@@ -647,7 +656,7 @@ int launch_t(GemmParams& p, hipStream_t s) {
     p.n_tiles = p.N / BN;
     const int64_t nb = (int64_t)p.m_slots * p.n_tiles;
     if (nb > 0x7fffffff) return NVFP4_ERR_SHAPE;
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, NS, MINW, RAC, SILU, GATHER, RSKIP>), dim3((unsigned)nb),
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, NS, MINW, RAC, SILU, GATHER, RSKIP, CPB>), dim3((unsigned)nb),
                        dim3(kThreads), 0, s, p);
     return nv_launch_status();
   }
@@ -802,7 +811,7 @@ int launch_cfg(GemmParams& p, hipStream_t s) {
     const char* e = getenv("NVFP4RAC_GEMM_CFG");
     return e ? atoi(e) : 0;
   }();
-  if (RAC && p.skip) return launch_t<64, 128, 2, 2, 2, 4, RAC, SILU, GATHER, true>(p, s);
+  if (RAC && p.skip) return launch_t<64, 128, 2, 2, 2, 2, RAC, SILU, GATHER, true>(p, s);
   switch (cfg) {
     case 1: return launch_t<128, 128, 2, 2, 2, 2, RAC, SILU, GATHER, false>(p, s);
     case 2: return launch_t<128, 128, 2, 2, 3, 1, RAC, SILU, GATHER, false>(p, s);
@@ -810,6 +819,11 @@ int launch_cfg(GemmParams& p, hipStream_t s) {
     case 4: return launch_t<128, 128, 4, 1, 2, 2, RAC, SILU, GATHER, false>(p, s);
     case 5: return launch_t<64, 256, 2, 2, 2, 2, RAC, SILU, GATHER, false>(p, s);
     case 6: return launch_t<128, 128, 4, 1, 3, 1, RAC, SILU, GATHER, false>(p, s);
+    case 7: return launch_t<64, 128, 2, 2, 4, 2, RAC, SILU, GATHER, false, 2>(p, s);
+    case 8: return launch_t<64, 256, 2, 2, 4, 1, RAC, SILU, GATHER, false, 2>(p, s);
+    case 9: return launch_t<64, 128, 2, 2, 3, 2, RAC, SILU, GATHER, false, 1>(p, s);
+    case 12: return launch_t<64, 128, 2, 2, 2, 4, RAC, SILU, GATHER, false, 1>(p, s);
+    case 13: return launch_t<64, 128, 2, 2, 2, 3, RAC, SILU, GATHER, false, 1>(p, s);
     case 10: return launch3<128, 128, 2, 2, 1, RAC, SILU, GATHER>(p, s);
     case 11: return launch3<128, 256, 2, 4, 1, RAC, SILU, GATHER>(p, s);
     default:
