@@ -17,6 +17,8 @@
 //    scales (E8M0 127).  The operands go from LDS to the matrix cores as they
 //    are; the row and channel scales factor out of the K sum and are applied
 //    in the epilogue.
+//  * Decode shape (one group, <= 64 rows): k_fp8_gemv16, the FP8 counterpart
+//    of the NVFP4 decode kernel (16 columns per workgroup, waves split K).
 //  * Grouping, gather, XCD-aware tile order and the SiLU gate/up pairing are
 //    those of the NVFP4 kernel.  K is consumed in chunks of 128 bytes per row
 //    (two MFMA steps of 64); the global->LDS DMA runs NSTAGE - 1 chunks ahead.
@@ -391,6 +393,88 @@ int launch_f8_cfg(F8Params& p, hipStream_t s) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode shape (one group, at most 64 rows, K % 512 == 0, F32 epilogue): a
+// workgroup owns 16 output columns and one 16-row tile over the whole of K,
+// so N/16 workgroups stream W once; its waves split K.  Each 128-k group is
+// one v_mfma_scale_f32_16x16x128_f8f6f4: lane l feeds row (or column) l % 16
+// with the 32 contiguous bytes k = 32 (l / 16) + 0..31 of the group, the same
+// layout for both operands.  Every lane issues all its loads of a pass before
+// the first use; the waves add their accumulators through LDS in a fixed
+// order.
+typedef float float4v __attribute__((ext_vector_type(4)));
+constexpr int kF8GvGroups = 4;   // 128-k groups per wave per load pass
+constexpr int kF8GvMaxRows = 64;
+
+template <int WAVES, bool GATHER>
+__global__ __launch_bounds__(64 * WAVES) void k_fp8_gemv16(F8Params p) {
+  __shared__ float4v red[WAVES][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int w = (wave + (int)blockIdx.x) % WAVES;  // spread the A reads over lines
+  const int c = lane & 15, q = lane >> 4;
+  const int K = p.K, kw = K / WAVES;
+  const int m = (int)blockIdx.y * 16 + c;  // A row fed by this lane
+  const bool mv = m < p.total_rows;
+  const int64_t n = (int64_t)blockIdx.x * 16 + c;  // W row fed by this lane
+  const uint8_t* wr = p.w_codes + n * K;
+  const int64_t src = mv ? (GATHER ? (int64_t)p.gather[m] : (int64_t)m) : 0;
+  const uint8_t* ar = p.a_codes + src * K;
+  float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int g0 = 0; g0 < kw; g0 += 128 * kF8GvGroups) {
+    const int ng = (kw - g0) / 128 < kF8GvGroups ? (kw - g0) / 128 : kF8GvGroups;
+    uint4 wv[kF8GvGroups][2], av[kF8GvGroups][2];
+#pragma unroll
+    for (int g = 0; g < kF8GvGroups; ++g) {
+      const int kb = w * kw + g0 + g * 128 + q * 32;
+      wv[g][0] = wv[g][1] = av[g][0] = av[g][1] = make_uint4(0u, 0u, 0u, 0u);
+      if (g < ng) {
+        wv[g][0] = *reinterpret_cast<const uint4*>(wr + kb);
+        wv[g][1] = *reinterpret_cast<const uint4*>(wr + kb + 16);
+        if (mv) {
+          av[g][0] = *reinterpret_cast<const uint4*>(ar + kb);
+          av[g][1] = *reinterpret_cast<const uint4*>(ar + kb + 16);
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < kF8GvGroups; ++g) {
+      if (g >= ng) break;
+      int8v a, b;
+      a[0] = (int)av[g][0].x; a[1] = (int)av[g][0].y; a[2] = (int)av[g][0].z; a[3] = (int)av[g][0].w;
+      a[4] = (int)av[g][1].x; a[5] = (int)av[g][1].y; a[6] = (int)av[g][1].z; a[7] = (int)av[g][1].w;
+      b[0] = (int)wv[g][0].x; b[1] = (int)wv[g][0].y; b[2] = (int)wv[g][0].z; b[3] = (int)wv[g][0].w;
+      b[4] = (int)wv[g][1].x; b[5] = (int)wv[g][1].y; b[6] = (int)wv[g][1].z; b[7] = (int)wv[g][1].w;
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
+    }
+  }
+  red[w][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  float4v sum = red[0][lane];
+#pragma unroll
+  for (int i = 1; i < WAVES; ++i) sum += red[i][lane];
+  const float sw = p.w_scales[n];
+  float* out = reinterpret_cast<float*>(p.out);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (int)blockIdx.y * 16 + 4 * q + i;  // D row of element i
+    if (row < p.total_rows) {
+      const int64_t sr = GATHER ? (int64_t)p.gather[row] : (int64_t)row;
+      out[(int64_t)row * p.N + n] = (p.a_scales[sr] * sw) * sum[i];
+    }
+  }
+}
+
+template <bool GATHER>
+int launch_f8_gemv(F8Params& p, hipStream_t s) {
+  const dim3 grid((unsigned)(p.N / 16), (unsigned)((p.total_rows + 15) / 16));
+  if (p.K % 1024 == 0)
+    hipLaunchKernelGGL((k_fp8_gemv16<8, GATHER>), grid, dim3(512), 0, s, p);
+  else
+    hipLaunchKernelGGL((k_fp8_gemv16<4, GATHER>), grid, dim3(256), 0, s, p);
+  return nv_launch_status();
+}
+
 }  // namespace
 
 extern "C" {
@@ -439,6 +523,8 @@ int fp8_grouped_gemm(const fp8_gemm_args_t* a, void* stream) {
   p.out = a->out;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool silu = a->epilogue == NVFP4_EPI_SILU_MUL_BF16, gather = a->gather_rows != nullptr;
+  if (p.G == 1 && p.total_rows <= kF8GvMaxRows && p.K % 512 == 0 && !silu)
+    return gather ? launch_f8_gemv<true>(p, s) : launch_f8_gemv<false>(p, s);
   if (silu) return gather ? launch_f8_cfg<true, true>(p, s) : launch_f8_cfg<true, false>(p, s);
   return gather ? launch_f8_cfg<false, true>(p, s) : launch_f8_cfg<false, false>(p, s);
 }

@@ -147,6 +147,32 @@ def test_fp8_gemm_parity(orc, seed, G, N, K, mean_rows, src_rows, gather, silu):
     _run(orc, seed, G, N, K, mean_rows, src_rows, gather, silu)
 
 
+@pytest.mark.parametrize("rows,N,K,gather", [(16, 4096, 4096, False), (1, 256, 512, False),
+                                           (7, 384, 1024, True), (64, 128, 2048, False),
+                                           (65, 256, 512, False)])
+def test_fp8_gemm_decode_shape(orc, rows, N, K, gather):
+    """One group and at most 64 rows run the decode kernel (65 rows: the
+    prefill tiles), checked with the same bound."""
+    say(f"fp8 decode-shaped gemm rows={rows} N={N} K={K} gather={gather}")
+    rng = np.random.default_rng(rows * 3 + K)
+    src_rows = rows + 5 if gather else rows
+    x = D.bf16_to_f32(D.bf16_bits(_edge_rows(rng, src_rows, K, "f32")))
+    ac, as_ = orc.fp8_quantize_rows(x)
+    wc, wsc = _weights(orc, rng, 1, N, K)
+    off = np.array([0, rows], np.int32)
+    gat = rng.integers(0, src_rows, rows).astype(np.int32) if gather else None
+    y = orc.fp8_grouped_gemm(N, K, off, gat, (ac, as_), (wc, wsc))
+    bound = _fp8_bound(orc, ac, as_, wc, wsc, off, gat) + 2.0 ** -23 * np.abs(y)
+    out = L.fp8_grouped_gemm(L.FP8(torch.from_numpy(ac).to(DEV), torch.from_numpy(as_).to(DEV)),
+                             L.FP8(torch.from_numpy(wc).to(DEV), torch.from_numpy(wsc).to(DEV)),
+                             torch.from_numpy(off).to(DEV), N=N, K=K, total_rows=rows,
+                             gather_rows=None if gat is None else torch.from_numpy(gat).to(DEV))
+    yg = host(out).astype(np.float64)
+    bad = np.abs(yg - y) > bound
+    assert not bad.any(), f"{bad.sum()} outputs beyond the bound"
+    print(f"rel Frobenius error {rel_frob(yg, y):.3e}")
+
+
 def test_fp8_gemm_empty(orc):
     say("fp8 gemm empty problem")
     a = L.FP8(torch.zeros((1, 128), dtype=torch.uint8, device=DEV),
