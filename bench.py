@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--extras", type=int, default=1,
                     help="MoE workloads: also time the full block (weighted combine), a "
                          "16-token decode call eager vs HIP-graph replay, and the trainer-side "
-                         "weight fake-quant")
+                         "weight fake-quant; dense workloads: the step eager vs HIP-graph replay")
     ap.add_argument("--fp8-library-reference", type=int, default=0,
                     help="also time the vendor FP8 GEMM (hipBLASLt through torch._scaled_mm, "
                          "row/column scales, bf16 out) on the dense shape of each GEMM: a "
@@ -265,6 +265,8 @@ def main():
             res["comparators"]["fp8_dense_library_reference"] = library_fp8_reference(w, dev)
     if args.extras and w.kind == "moe":
         res.update(moe_extras(w, dev, x, lg, wgu, wd, nsx, nsh, timed, step, ms_step, NEV))
+    if args.extras and w.kind == "dense":
+        res["graph"] = dense_graph(w, dev, x, wq, nsx, flops)
     if "bytes" in dom:  # HBM-bound (decode shape): GB/s on the bytes the GEMM must move
         ach = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "kernel": dom["name"], "achieved": round(ach, 3),
@@ -410,6 +412,30 @@ def moe_extras(w, dev, x, lg, wgu, wd, nsx, nsh, timed, step, ms_step, nev):
                               frac_hbm=round(qbytes / us / 1e3 / PEAK_HBM_GBS, 4))
     del wb
     return out
+
+
+def dense_graph(w, dev, x, wq, nsx, flops):
+    """The dense step (quantize + RAC + GEMM) eager against a HIP-graph
+    replay of the same calls: at decode sizes the eager step is bound by host
+    launch work, the replay by the kernels."""
+    import torch
+
+    from nvfp4_w4a4_moe_quant_amd import pipeline as P
+
+    def per_call(fn, n=200):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / n * 1e6
+    eager = per_call(lambda: P.dense_forward(x, wq, nsx))
+    g = P.GraphedDense(wq, nsx, w.rows, x.dtype, dev)
+    graph = per_call(lambda: g(x))
+    return dict(eager_us_per_step=round(eager, 2), graph_us_per_step=round(graph, 2),
+                graph_tflops=round(flops / graph / 1e6, 3), speedup=round(eager / graph, 3))
 
 
 def library_fp8_reference(w, dev):

@@ -96,9 +96,14 @@ def gemm(inp: GemmInput, wq: QuantWeights, offsets: torch.Tensor, total_rows: in
         per_group_scales=inp.per_group)
 
 
-def dense_forward(x: torch.Tensor, wq: QuantWeights, n_select: Optional[int]) -> Dict:
+def dense_forward(x: torch.Tensor, wq: QuantWeights, n_select: Optional[int],
+                  offsets: Optional[torch.Tensor] = None) -> Dict:
+    """offsets: the one-group offsets [0, rows] (int32, on the device); made
+    here when not given (a host-to-device copy, so a graph capture passes
+    its own)."""
     rows = x.shape[0]
-    offsets = torch.tensor([0, rows], dtype=torch.int32, device=x.device)
+    if offsets is None:
+        offsets = torch.tensor([0, rows], dtype=torch.int32, device=x.device)
     inp = quantize_input(x, n_select)
     y = gemm(inp, wq, offsets, rows)
     return dict(x_in=inp, y=y, offsets=offsets)
@@ -166,6 +171,31 @@ class GraphedMoEBlock:
         self.logits.copy_(logits)
         self.graph.replay()
         return self.out
+
+
+class GraphedDense:
+    """dense_forward captured once as a HIP graph for fixed [rows, K] (the
+    decode shape): a call copies x into the static input and replays every
+    kernel of quantize + RAC + GEMM with no host work per launch."""
+
+    def __init__(self, wq: QuantWeights, n_select: Optional[int], rows: int,
+                 x_dtype: torch.dtype, device, warmup: int = 2):
+        self.x = torch.zeros((rows, wq.K), dtype=x_dtype, device=device)
+        self.offsets = torch.tensor([0, rows], dtype=torch.int32, device=device)
+        side = torch.cuda.Stream(device)
+        side.wait_stream(torch.cuda.current_stream(device))
+        with torch.cuda.stream(side):
+            for _ in range(warmup):
+                dense_forward(self.x, wq, n_select, self.offsets)
+        torch.cuda.current_stream(device).wait_stream(side)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.y = dense_forward(self.x, wq, n_select, self.offsets)["y"]
+
+    def __call__(self, x: torch.Tensor) -> torch.Tensor:
+        self.x.copy_(x)
+        self.graph.replay()
+        return self.y
 
 
 class NVFP4WeightFakeQuant(torch.autograd.Function):

@@ -84,3 +84,22 @@ def test_moe_block_combines_grouped_rows(orc):
     for s in range(c["k"]):
         acc = (acc + (w[:, s:s + 1] * y[rt["row_of"][:, s]]).astype(np.float32)).astype(np.float32)
     eq(host(d["out"]), acc, "block output")
+
+
+def test_graphed_dense_matches_eager(orc):
+    """The graph-captured dense step (decode shape) equals the eager step bit
+    for bit on several replays with other work between them."""
+    say("graph-captured dense step vs eager")
+    rng = np.random.default_rng(31)
+    rows, K, N = 16, 1024, 512
+    wq = P.quantize_weights([(0, to_dev((rng.standard_normal((N, K)) * 0.02).astype(np.float32),
+                                        "bf16"))], 1, N, K, DEV)
+    g = P.GraphedDense(wq, K // 2, rows, torch.bfloat16, DEV)
+    for rep in range(3):
+        x = to_dev(rng.standard_normal((rows, K)).astype(np.float32), "bf16")
+        ref = P.dense_forward(x, wq, K // 2)["y"].clone()
+        _ = P.dense_forward(to_dev(rng.standard_normal((rows, K)).astype(np.float32), "bf16"), wq, 8)
+        torch.cuda.synchronize()
+        out = g(x)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {rep}"
