@@ -278,7 +278,7 @@ int w4a4_grouped_gemm_rac(const w4a4_gemm_args_t* args, void* ws, size_t ws_byte
  * FP32 for out_dtype NVFP4_IN_F32, bf16 (nearest even of v) for
  * NVFP4_IN_BF16.  *tensor_scale receives s_t.  Workspace as
  * nvfp4_quantize (none with amax_in).  Requires K % 16 == 0, x and out
- * 16-byte aligned, ldx % 8 == 0.
+ * 16-byte aligned, ldx % 16 == 0 (elements), as nvfp4_quantize.
  *
  * nvfp4_dequantize: the same values from stored codes [rows, K/2], scales
  * [rows, K/16] and tensor scale; nvfp4_qdq(x) equals
