@@ -433,6 +433,108 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* t
   return before + inc - v;
 }
 
+// ------------------------------------------------ per-group selection
+// Per-expert RAC selects within each of many groups, where the all-pairs rank
+// count (K^2 compares per group) is too costly.  k_select_group takes one
+// group per workgroup with its scores staged in LDS and finds the n-th
+// largest score by an MSB-first radix select (8 passes of 8 bits: histogram
+// of the candidates' digit, then the digit where the count from the top
+// reaches n).  Scores above that threshold are selected; of the scores equal
+// to it, the lowest-index ones fill the remaining places (a prefix count in
+// index order) -- the same set as the first n of (score desc, index asc).
+constexpr int kGroupSelectMaxK = 8192;  // scores staged in LDS (64 KiB)
+
+__global__ __launch_bounds__(kSelThreads) void k_select_group(
+    const int64_t* __restrict__ score_in, const uint32_t* __restrict__ chmax, int K, int n_sel,
+    uint16_t* __restrict__ mask16, uint8_t* __restrict__ kact, uint32_t* __restrict__ part_max) {
+  __shared__ uint64_t sc[kGroupSelectMaxK];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t wsum[kSelThreads / 64];
+  __shared__ uint32_t res_digit, res_above;
+  const int64_t g = blockIdx.x;
+  const uint64_t* score = reinterpret_cast<const uint64_t*>(score_in + g * K);
+  chmax += g * K;
+  mask16 += g * (K >> 4);
+  kact += g * (K >> 4);
+  part_max += g * (K >> 4);
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int i = tid; i < K; i += kSelThreads) sc[i] = score[i];
+
+  uint64_t prefix = 0, pmask = 0;
+  uint32_t remaining = (uint32_t)n_sel;  // places left among the candidates
+  if (n_sel > 0) {
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+      __syncthreads();  // also publishes sc on the first pass
+      for (int i = tid; i < K; i += kSelThreads) {
+        const uint64_t v = sc[i];
+        if ((v & pmask) == prefix) atomicAdd(&hist[(uint32_t)(v >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid < 64) {
+        // lane l holds digits 4l .. 4l+3; counts from the top (digit 255 down)
+        uint32_t h[4], sfx[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = hist[4 * lane + i];
+        sfx[3] = h[3];
+        sfx[2] = sfx[3] + h[2];
+        sfx[1] = sfx[2] + h[1];
+        sfx[0] = sfx[1] + h[0];
+        // sum over the lanes above this one (higher digits)
+        uint32_t above = 0, inc = sfx[0];
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t n = __shfl_down(inc, o, 64);
+          if (lane + o < 64) inc += n;
+        }
+        above = inc - sfx[0];
+        // the digit d with count(>= d) >= remaining > count(> d) is unique
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t ge = above + sfx[i], gt = ge - h[i];
+          if (ge >= remaining && gt < remaining) {
+            res_digit = (uint32_t)(4 * lane + i);
+            res_above = gt;
+          }
+        }
+      }
+      __syncthreads();
+      prefix |= (uint64_t)res_digit << shift;
+      pmask |= (uint64_t)255u << shift;
+      remaining -= res_above;
+    }
+  } else {
+    __syncthreads();
+  }
+  // threshold T = prefix; `remaining` of the scores equal to T are taken,
+  // lowest index first.  Thread t owns block t (channels 16t .. 16t+15).
+  const int nb = K >> 4;
+  uint32_t eqbits = 0, gtbits = 0;
+  if (tid < nb && n_sel > 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint64_t v = sc[tid * 16 + i];
+      if (v > prefix) gtbits |= 1u << i;
+      if (v == prefix) eqbits |= 1u << i;
+    }
+  }
+  uint32_t total;
+  const uint32_t before = block_exclusive_scan<kSelThreads>((uint32_t)__builtin_popcount(eqbits), wsum, &total);
+  if (tid < nb) {
+    uint32_t bits = gtbits, rank = before;
+    for (uint32_t m = eqbits; m; m &= m - 1) {
+      if (rank < remaining) bits |= m & (~m + 1u);
+      ++rank;
+    }
+    mask16[tid] = (uint16_t)bits;
+    kact[tid] = bits ? 1 : 0;
+    float a = 0.0f;
+    for (uint32_t m = bits; m; m &= m - 1)
+      a = __builtin_fmaxf(a, __uint_as_float(chmax[tid * 16 + __builtin_ctz(m)]));
+    part_max[tid] = __float_as_uint(a);
+  }
+}
+
 // -------------------------------------------------------------- residual
 // r = mask * e in every block with a selected channel, e = x - deq(q(x)).
 // The main codes are recomputed from x, the block scale and the tensor scale
@@ -895,9 +997,15 @@ int rac_select_residual_grouped(const void* x, int dtype, int64_t K, int64_t ldx
   uint16_t* mask16 = reinterpret_cast<uint16_t*>(base + L.mask_off);
   uint32_t* part_max = reinterpret_cast<uint32_t*>(base + L.max_off);
   const int nrank = (int)(K / 16);
-  hipLaunchKernelGGL(k_rank, dim3(nrank, (unsigned)G), dim3(64 * kRankWaves), 0, s, channel_score,
-                     reinterpret_cast<const uint32_t*>(channel_max), (int)K, (int)n_select,
-                     mask16, kblock_active, part_max);
+  // many groups: a radix select per group; very long rows: the rank count
+  if (K <= kGroupSelectMaxK)
+    hipLaunchKernelGGL(k_select_group, dim3((unsigned)G), dim3(kSelThreads), 0, s, channel_score,
+                       reinterpret_cast<const uint32_t*>(channel_max), (int)K, (int)n_select,
+                       mask16, kblock_active, part_max);
+  else
+    hipLaunchKernelGGL(k_rank, dim3(nrank, (unsigned)G), dim3(64 * kRankWaves), 0, s,
+                       channel_score, reinterpret_cast<const uint32_t*>(channel_max), (int)K,
+                       (int)n_select, mask16, kblock_active, part_max);
   st = nv_launch_status();
   if (st) return st;
   // at least one workgroup per group: it writes the group's selected[] and

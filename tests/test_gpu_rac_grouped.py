@@ -125,3 +125,43 @@ def test_per_expert_moe_gate_up(orc):
     h_ref, _ = orc.silu_mul(y, I)
     ok = bf16_ulp_ok(host(d["h"].view(torch.int16)).view(np.uint16), h_ref)
     assert ok.all(), f"{(~ok).sum()} beyond one bf16 ulp"
+
+
+@pytest.mark.parametrize("K,n_sel", [(2048, 1024), (768, 384), (8192, 4096), (256, 1),
+                                     (512, 511), (256, 256), (128, 0)])
+def test_grouped_select_crafted_scores(orc, K, n_sel):
+    """Per-group selection on hand-made int64 scores -- one group each of heavy
+    ties, values near 2^63, all zeros, all equal, random -- against the
+    oracle's per-group sort (score desc, index asc); the residual uses the
+    real per-channel max |e|, so its scale and bytes are checked too."""
+    say(f"grouped select crafted K={K} n_sel={n_sel}")
+    rng = np.random.default_rng(K + 7 * n_sel)
+    sizes = [3, 2, 4, 1, 3]
+    off = _offsets(sizes)
+    total, G = int(off[-1]), len(sizes)
+    x = _x(K, total, K, "bf16")
+    xd, od = to_dev(x, "bf16"), _t(off)
+    qo = L.nvfp4_quantize_grouped(xd, od, total, stats=True)
+    score = np.zeros((G, K), np.int64)
+    score[0] = rng.integers(0, 5, K).astype(np.int64) << 40
+    score[1] = (np.int64(2 ** 62) + rng.integers(0, 2 ** 61, K)).astype(np.int64)
+    score[1, rng.integers(0, K, K // 8)] = np.iinfo(np.int64).max
+    score[1, rng.integers(0, K, K // 8)] = 0
+    score[2] = 0
+    score[3] = 123456789
+    score[4] = rng.integers(0, 2 ** 40, K)
+    chmax = host(qo.channel_max)
+    qo2 = L.QuantOut(qo.q, _t(score), qo.channel_max)
+    rac = L.rac_select_residual_grouped(xd, qo2, od, total, n_sel)
+    sel_g, act_g = host(rac.selected), host(rac.kblock_active)
+    s_tr_g = host(rac.r.tscale)
+    codes, scales, s_t = host(qo.q.codes), host(qo.q.scales), host(qo.q.tscale)
+    for g in range(G):
+        sel, mask, active, s_tr = orc.rac_select(score[g], chmax[g], n_sel)
+        eq(sel_g[g], sel, f"selected group {g}")
+        eq(act_g[g], active, f"kblock_active group {g}")
+        eq(s_tr_g[g], np.float32(s_tr), f"residual tensor scale group {g}")
+        j0, j1 = off[g], off[g + 1]
+        rc, rs, _, _ = orc.rac_residual(x[j0:j1], codes[j0:j1], scales[j0:j1], float(s_t[g]), mask)
+        eq(host(rac.r.codes)[j0:j1], rc, f"residual codes group {g}")
+        eq(host(rac.r.scales)[j0:j1], rs, f"residual scales group {g}")
