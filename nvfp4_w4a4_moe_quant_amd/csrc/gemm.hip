@@ -684,9 +684,10 @@ constexpr int kGvMaxRows = 64;    // rows up to which the decode kernel is used
 // WAVES waves split K (K % (128 * WAVES) == 0).  The only device values the
 // loads wait for are the gather indices; the group spans rows [0, total_rows)
 // (offsets[0] == 0, offsets[1] == total_rows).
-template <int WAVES, bool RAC, bool GATHER>
+template <int WAVES, int GRP, bool RAC, bool GATHER>
 __global__ __launch_bounds__(64 * WAVES) void k_gemv16(GemmParams p) {
-  __shared__ float4v red[WAVES][2][64];
+  constexpr int NCG = 1;  // 16-column groups per workgroup (2 measured slower)
+  __shared__ float4v red[WAVES][2][NCG][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // K slice of this wave, rotated by the workgroup id so that the workgroups
   // (which all read the same A and R rows) spread over different lines
@@ -699,32 +700,28 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv16(GemmParams p) {
   const float s_tw = p.w_ts[0];
   const int m = (int)blockIdx.y * 16 + c;  // A row fed by this lane
   const bool mv = m < p.total_rows;
-  const int64_t n = (int64_t)blockIdx.x * 16 + c;   // W row fed by this lane
-  const uint8_t* wc = p.w_codes + n * (K >> 1);
-  const uint8_t* wsc = p.w_scales + n * (K >> 4);
+  // W rows fed by this lane: one per 16-column group of the workgroup
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * NCG + c;
+  const uint8_t* wc = p.w_codes + n0 * (K >> 1);
+  const uint8_t* wsc = p.w_scales + n0 * (K >> 4);
+  const int64_t cgc = (int64_t)16 * (K >> 1), cgs = (int64_t)16 * (K >> 4);  // next group
 
-  float4v accm = {0.0f, 0.0f, 0.0f, 0.0f}, accr = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int g0 = 0; g0 < kw; g0 += 128 * kGvGroups) {
-    const int ng = (kw - g0) / 128 < kGvGroups ? (kw - g0) / 128 : kGvGroups;
-    uint4 wv[kGvGroups], av[kGvGroups], rv[kGvGroups];
-    uint32_t wsv[kGvGroups], asv[kGvGroups], rsv[kGvGroups];
+  float4v accm[NCG], accr[NCG];
 #pragma unroll
-    for (int g = 0; g < kGvGroups; ++g) {
-      const int kb = w * kw + g0 + g * 128 + q * 32;
-      wv[g] = make_uint4(0u, 0u, 0u, 0u);
-      wsv[g] = 0u;
-      if (g < ng) {
-        wv[g] = *reinterpret_cast<const uint4*>(wc + (kb >> 1));
-        wsv[g] = *reinterpret_cast<const uint16_t*>(wsc + (kb >> 4));
-      }
-    }
-    const int64_t src = mv ? (GATHER ? (int64_t)p.gather[m] : (int64_t)m) : 0;
-    const uint8_t* ac = p.a_codes + src * (K >> 1);
-    const uint8_t* asc = p.a_scales + src * (K >> 4);
-    const uint8_t* rc = RAC ? p.r_codes + src * (K >> 1) : nullptr;
-    const uint8_t* rsc = RAC ? p.r_scales + src * (K >> 4) : nullptr;
+  for (int j = 0; j < NCG; ++j) accm[j] = accr[j] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+  const int64_t src = mv ? (GATHER ? (int64_t)p.gather[m] : (int64_t)m) : 0;
+  const uint8_t* ac = p.a_codes + src * (K >> 1);
+  const uint8_t* asc = p.a_scales + src * (K >> 4);
+  const uint8_t* rc = RAC ? p.r_codes + src * (K >> 1) : nullptr;
+  const uint8_t* rsc = RAC ? p.r_scales + src * (K >> 4) : nullptr;
+  for (int g0 = 0; g0 < kw; g0 += 128 * GRP) {
+    const int ng = (kw - g0) / 128 < GRP ? (kw - g0) / 128 : GRP;
+    uint4 wv[GRP][NCG], av[GRP], rv[GRP];
+    uint32_t wsv[GRP][NCG], asv[GRP], rsv[GRP];
+    // loads in group order (A, R, then the W rows), so that group g can be
+    // computed once its own loads have landed
 #pragma unroll
-    for (int g = 0; g < kGvGroups; ++g) {
+    for (int g = 0; g < GRP; ++g) {
       const int kb = w * kw + g0 + g * 128 + q * 32;
       av[g] = rv[g] = make_uint4(0u, 0u, 0u, 0u);
       asv[g] = rsv[g] = 0u;
@@ -736,48 +733,72 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv16(GemmParams p) {
           rsv[g] = *reinterpret_cast<const uint16_t*>(rsc + (kb >> 4));
         }
       }
+#pragma unroll
+      for (int j = 0; j < NCG; ++j) {
+        wv[g][j] = make_uint4(0u, 0u, 0u, 0u);
+        wsv[g][j] = 0u;
+        if (g < ng) {
+          wv[g][j] = *reinterpret_cast<const uint4*>(wc + j * cgc + (kb >> 1));
+          wsv[g][j] = *reinterpret_cast<const uint16_t*>(wsc + j * cgs + (kb >> 4));
+        }
+      }
     }
 #pragma unroll
-    for (int g = 0; g < kGvGroups; ++g) {
+    for (int g = 0; g < GRP; ++g) {
       if (g >= ng) break;
-      const half2v sw = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wsv[g], 1.0f, false);
       const half2v sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(asv[g], 1.0f, false);
       half2v sr = sa;
       if constexpr (RAC) sr = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rsv[g], 1.0f, false);
-      const uint32_t wword[4] = {wv[g].x, wv[g].y, wv[g].z, wv[g].w};
+      half2v sw[NCG];
+#pragma unroll
+      for (int j = 0; j < NCG; ++j)
+        sw[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wsv[g][j], 1.0f, false);
       const uint32_t aword[4] = {av[g].x, av[g].y, av[g].z, av[g].w};
       const uint32_t rword[4] = {rv[g].x, rv[g].y, rv[g].z, rv[g].w};
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const int hi = st >> 1;  // steps 0-1: first block, 2-3: second
-        const half2v s_w = hi ? __builtin_shufflevector(sw, sw, 1, 1)
-                              : __builtin_shufflevector(sw, sw, 0, 0);
         const half2v s_a = hi ? __builtin_shufflevector(sa, sa, 1, 1)
                               : __builtin_shufflevector(sa, sa, 0, 0);
-        const half8 bw = dequant8(wword[st], s_w);
         const half8 ba = dequant8(aword[st], s_a);
-        accm = __builtin_amdgcn_mfma_f32_16x16x32_f16(ba, bw, accm, 0, 0, 0);
+        half8 br;
         if constexpr (RAC) {
           const half2v s_r = hi ? __builtin_shufflevector(sr, sr, 1, 1)
                                 : __builtin_shufflevector(sr, sr, 0, 0);
-          const half8 br = dequant8(rword[st], s_r);
-          accr = __builtin_amdgcn_mfma_f32_16x16x32_f16(br, bw, accr, 0, 0, 0);
+          br = dequant8(rword[st], s_r);
+        }
+#pragma unroll
+        for (int j = 0; j < NCG; ++j) {
+          const uint32_t ww = st == 0 ? wv[g][j].x : st == 1 ? wv[g][j].y
+                            : st == 2 ? wv[g][j].z : wv[g][j].w;
+          const half2v s_w = hi ? __builtin_shufflevector(sw[j], sw[j], 1, 1)
+                                : __builtin_shufflevector(sw[j], sw[j], 0, 0);
+          const half8 bw = dequant8(ww, s_w);
+          accm[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ba, bw, accm[j], 0, 0, 0);
+          if constexpr (RAC)
+            accr[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(br, bw, accr[j], 0, 0, 0);
         }
       }
     }
   }
 
-  red[w][0][lane] = accm;
-  red[w][1][lane] = accr;
+#pragma unroll
+  for (int j = 0; j < NCG; ++j) {
+    red[w][0][j][lane] = accm[j];
+    red[w][1][j][lane] = accr[j];
+  }
   __syncthreads();
-  if (wave != 0) return;
-  float4v sm = red[0][0][lane], sr = red[0][1][lane];
+  // wave j adds the K slices of column group j in slice order
+  if (wave >= NCG) return;
+  const int j = wave;
+  float4v sm = red[0][0][j][lane], sr = red[0][1][j][lane];
 #pragma unroll
   for (int i = 1; i < WAVES; ++i) {
-    sm += red[i][0][lane];
-    sr += red[i][1][lane];
+    sm += red[i][0][j][lane];
+    sr += red[i][1][j][lane];
   }
   float* out = reinterpret_cast<float*>(p.out);
+  const int64_t n = n0 + 16 * j;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = (int)blockIdx.y * 16 + 4 * q + i;  // D row of element i
@@ -793,9 +814,9 @@ template <bool RAC, bool GATHER>
 int launch_gemv(GemmParams& p, hipStream_t s) {
   const dim3 grid((unsigned)(p.N / 16), (unsigned)((p.total_rows + 15) / 16));
   if (p.K % 1024 == 0)
-    hipLaunchKernelGGL((k_gemv16<8, RAC, GATHER>), grid, dim3(512), 0, s, p);
+    hipLaunchKernelGGL((k_gemv16<8, kGvGroups, RAC, GATHER>), grid, dim3(512), 0, s, p);
   else
-    hipLaunchKernelGGL((k_gemv16<4, RAC, GATHER>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_gemv16<4, kGvGroups, RAC, GATHER>), grid, dim3(256), 0, s, p);
   return nv_launch_status();
 }
 

@@ -521,6 +521,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select_group(
   uint32_t total;
   const uint32_t before = block_exclusive_scan<kSelThreads>((uint32_t)__builtin_popcount(eqbits), wsum, &total);
   if (tid < nb) {
+    uint32_t cm[16];  // all 16 loads issued before the first use
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cm[i] = chmax[tid * 16 + i];
     uint32_t bits = gtbits, rank = before;
     for (uint32_t m = eqbits; m; m &= m - 1) {
       if (rank < remaining) bits |= m & (~m + 1u);
@@ -529,8 +532,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select_group(
     mask16[tid] = (uint16_t)bits;
     kact[tid] = bits ? 1 : 0;
     float a = 0.0f;
-    for (uint32_t m = bits; m; m &= m - 1)
-      a = __builtin_fmaxf(a, __uint_as_float(chmax[tid * 16 + __builtin_ctz(m)]));
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if ((bits >> i) & 1u) a = __builtin_fmaxf(a, __uint_as_float(cm[i]));
     part_max[tid] = __float_as_uint(a);
   }
 }
