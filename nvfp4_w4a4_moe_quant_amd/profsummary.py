@@ -15,6 +15,15 @@ counter shows on a plain copy of known size (copycal: 3 copies of MiB MiB):
 The JSON records the kernel, the raw and scaled byte counts, the factors and
 the SHA-256 of the kernel's source file, so that a reader can tell whether the
 counters still describe the current kernel.
+
+Clock and matrix-core utilisation of the GEMM kernels from a kernel trace and
+two counter passes (GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES
+SQ_VALU_MFMA_COEXEC_CYCLES SQ_WAVE_CYCLES SQ_ACTIVE_INST_VALU SQ_WAIT_ANY, then
+GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU_MFMA_MOPS_F8
+SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT):
+
+    python -m nvfp4_w4a4_moe_quant_amd.profsummary mfma \\
+        <kernel_trace.csv> <pass1.csv> <pass2.csv> <XCDs> <SIMDs> [command]
 """
 import collections
 import csv
@@ -94,8 +103,68 @@ def traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, mib, match, sour
     print("\n".join(lines))
 
 
+def _per_dispatch(path):
+    """{kernel: {counter: [value per dispatch]}} from a counter_collection.csv
+    (values summed over the rows of one dispatch)."""
+    d = collections.defaultdict(lambda: collections.defaultdict(float))
+    names = {}
+    for r in csv.DictReader(open(path)):
+        key = r["Dispatch_Id"]
+        names[key] = short(r["Kernel_Name"])
+        d[key][r["Counter_Name"]] += float(r["Counter_Value"])
+    out = collections.defaultdict(lambda: collections.defaultdict(list))
+    for key, cs in d.items():
+        for c, v in cs.items():
+            out[names[key]][c].append(v)
+    return out
+
+
+def mfma(trace_csv, pass1_csv, pass2_csv, n_xcd, n_simd, command=""):
+    """Clock, matrix-core utilisation and wait/LDS fractions per GEMM kernel:
+    clock = GRBM_GUI_ACTIVE per XCD / kernel duration (kernel trace); MFMA
+    busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x SIMDs);
+    co-exec = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES (matrix-core
+    cycles during which the SIMD also ran VALU work); executed MFMA FLOPs =
+    (SQ_INSTS_VALU_MFMA_MOPS_F16 + _F8) x 512."""
+    n_xcd, n_simd = int(n_xcd), int(n_simd)
+    dur = collections.defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        dur[short(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    c1, c2 = _per_dispatch(pass1_csv), _per_dispatch(pass2_csv)
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    lines = [f"command: {command}"] if command else []
+    lines.append(f"{'kernel':58s} {'n':>3s} {'us':>7s} {'GHz':>5s} {'MFMA%':>6s} {'coex%':>6s} "
+                 f"{'GFLOP':>7s} {'TF/s':>6s} {'VALU%':>6s} {'wait%':>6s} {'LDS%':>5s} "
+                 f"{'bank%':>6s}")
+    for k in sorted(c1):
+        if "gemm" not in k or k not in c2 or k not in dur:
+            continue
+        a = {c: med(v) for c, v in c1[k].items()}
+        b = {c: med(v) for c, v in c2[k].items()}
+        t = med(dur[k])
+        gui = a["GRBM_GUI_ACTIVE"] / n_xcd
+        flops = (b.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) +
+                 b.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0)) * 512
+        lines.append(
+            f"{k[:58]:58s} {len(c1[k]['GRBM_GUI_ACTIVE']):3d} {t:7.1f} {gui / t / 1e3:5.2f} "
+            f"{100 * a['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * n_simd):6.1f} "
+            f"{100 * a['SQ_VALU_MFMA_COEXEC_CYCLES'] / max(a['SQ_VALU_MFMA_BUSY_CYCLES'], 1.0):6.1f} "
+            f"{flops / 1e9:7.1f} "
+            f"{flops / t / 1e6:6.0f} {100 * a['SQ_ACTIVE_INST_VALU'] / a['SQ_WAVE_CYCLES']:6.1f} "
+            f"{100 * a['SQ_WAIT_ANY'] / a['SQ_WAVE_CYCLES']:6.1f} "
+            f"{100 * b['SQ_LDS_IDX_ACTIVE'] / (gui * n_simd / 4):5.1f} "
+            f"{100 * b['SQ_LDS_BANK_CONFLICT'] / max(b['SQ_LDS_IDX_ACTIVE'], 1.0):6.1f}")
+    lines.append("columns: median over dispatches; MFMA% = matrix cores busy; coex% = share of "
+                 "those cycles with VALU work running beside; VALU% and wait% "
+                 "= SQ_ACTIVE_INST_VALU and SQ_WAIT_ANY over SQ_WAVE_CYCLES; LDS% = LDS "
+                 "active cycles per CU; bank% = bank-conflict cycles over LDS active cycles")
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
     if len(sys.argv) > 1 and sys.argv[1] == "traffic":
         traffic(*sys.argv[2:10], command=" ".join(sys.argv[10:]))
+    elif len(sys.argv) > 1 and sys.argv[1] == "mfma":
+        mfma(*sys.argv[2:7], command=" ".join(sys.argv[7:]))
     else:
         main(sys.argv[1], " ".join(sys.argv[2:]))
