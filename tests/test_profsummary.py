@@ -1,0 +1,74 @@
+"""Host checks of the rocprofv3 summary tool (no GPU): the counter arithmetic
+behind the committed profiles, on small hand-made CSV files whose expected
+figures follow from the definitions by hand."""
+import csv
+import json
+
+from nvfp4_w4a4_moe_quant_amd import profsummary as S
+
+TRACE_HDR = ["Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+PMC_HDR = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def _write(path, header, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_mfma_summary(tmp_path, capsys):
+    k = "void (anonymous namespace)::k_gemm<64, 256, true>(GemmParams)"
+    other = "void (anonymous namespace)::k_quant<true>(float const*)"
+    # two dispatches of 100 us each (timestamps in ns)
+    _write(tmp_path / "t.csv", TRACE_HDR,
+           [[k, 0, 100_000], [k, 200_000, 300_000], [other, 0, 5_000]])
+    # per dispatch: GRBM_GUI_ACTIVE summed over 2 XCDs = 2 x 200000 cycles
+    # -> 200000 cycles per XCD in 100 us = 2.0 GHz; 4 SIMDs busy 50% of them
+    p1, p2 = [], []
+    for d in ("1", "2"):
+        p1 += [[d, k, "GRBM_GUI_ACTIVE", 200_000], [d, k, "GRBM_GUI_ACTIVE", 200_000],
+               [d, k, "SQ_VALU_MFMA_BUSY_CYCLES", 400_000],
+               [d, k, "SQ_VALU_MFMA_COEXEC_CYCLES", 100_000],
+               [d, k, "SQ_WAVE_CYCLES", 1_000_000], [d, k, "SQ_ACTIVE_INST_VALU", 250_000],
+               [d, k, "SQ_WAIT_ANY", 300_000]]
+        p2 += [[d, k, "GRBM_GUI_ACTIVE", 400_000],
+               [d, k, "SQ_INSTS_VALU_MFMA_MOPS_F16", 1_000_000],
+               [d, k, "SQ_LDS_IDX_ACTIVE", 20_000], [d, k, "SQ_LDS_BANK_CONFLICT", 5_000]]
+    p1.append(["3", other, "GRBM_GUI_ACTIVE", 1])
+    _write(tmp_path / "p1.csv", PMC_HDR, p1)
+    _write(tmp_path / "p2.csv", PMC_HDR, p2)
+    S.mfma(str(tmp_path / "t.csv"), str(tmp_path / "p1.csv"), str(tmp_path / "p2.csv"), 2, 4,
+           command="cmd")
+    out = capsys.readouterr().out.splitlines()
+    row = [l for l in out if l.startswith("k_gemm")]
+    assert len(row) == 1 and "k_quant" not in "\n".join(out[2:-1])
+    f = row[0].split()[-10:]
+    # us, GHz, MFMA% (400000 / (200000 * 4)), co-exec% (100000 / 400000),
+    # GFLOP (1e6 * 512), TF/s (5.12e8 / 100 us), VALU%, wait%,
+    # LDS% (20000 / (200000 * 4 / 4)), bank% (5000 / 20000)
+    assert f == ["100.0", "2.00", "50.0", "25.0", "0.5", "5", "25.0", "30.0", "10.0", "25.0"]
+
+
+def test_traffic_scaling(tmp_path, capsys):
+    k = "void (anonymous namespace)::k_gemm<64, 256, true, true, true>(GemmParams)"
+    cp = "void at::native::vectorized_elementwise_kernel<4, add>(int)"  # the copy
+    # calibration: a 1 MiB copy reads 512 KiB by FETCH_SIZE (factor 2) and
+    # writes 1024 KiB by WRITE_SIZE (factor 1)
+    _write(tmp_path / "cf.csv", PMC_HDR, [["1", cp, "FETCH_SIZE", 512.0]])
+    _write(tmp_path / "cw.csv", PMC_HDR, [["1", cp, "WRITE_SIZE", 1024.0]])
+    _write(tmp_path / "f.csv", PMC_HDR, [["1", k, "FETCH_SIZE", 100.0],
+                                         ["2", k, "FETCH_SIZE", 300.0]])
+    _write(tmp_path / "w.csv", PMC_HDR, [["1", k, "WRITE_SIZE", 50.0],
+                                         ["2", k, "WRITE_SIZE", 50.0]])
+    src = tmp_path / "src.hip"
+    src.write_text("kernel source\n")
+    out_json = tmp_path / "t.json"
+    S.traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(tmp_path / "cf.csv"),
+              str(tmp_path / "cw.csv"), "1", "true, true, true", str(src), str(out_json))
+    rec = json.load(open(out_json))
+    # mean fetch 200 KiB x 2, write 50 KiB x 1
+    assert abs(rec["fetch_bytes"] - 200 * 1024 * 2) < 1e-6
+    assert abs(rec["write_bytes"] - 50 * 1024) < 1e-6
+    assert abs(rec["hbm_bytes"] - (400 + 50) * 1024) < 1e-6
+    assert len(rec["source_sha256"]) == 64
