@@ -260,6 +260,11 @@ def main():
                              frac_hbm=g_bytes / t_g / 1e6 / PEAK_HBM_GBS),
                    gemm_back_to_back=dict(us=t_gk * 1e3, gbs=g_bytes / t_gk / 1e6,
                                           frac_hbm=g_bytes / t_gk / 1e6 / PEAK_HBM_GBS))
+        t_cold = dense_gemm_cold_ms(P, x_in, wq, offs, w.rows, dev)
+        res["gemm_cold_cache"] = dict(us=t_cold * 1e3, gbs=g_bytes / t_cold / 1e6,
+                                      frac_hbm=g_bytes / t_cold / 1e6 / PEAK_HBM_GBS,
+                                      note="512 MiB written between launches, so W comes "
+                                           "from HBM, not the 256 MB Infinity Cache")
         cfg = dict(workload=w.name, rows=w.rows, K=w.K, N=w.N, rac=rac, n_select_x=nsx)
 
     value = flops / (ms_step * 1e-3) / 1e12
@@ -500,6 +505,27 @@ def dense_gemm_replay_ms(P, x_in, wq, offs, rows, n=20, reps=10):
     b.synchronize()
     del outs
     return a.elapsed_time(b) / (reps * n)
+
+
+def dense_gemm_cold_ms(P, x_in, wq, offs, rows, dev, n=20):
+    """Mean duration of one decode-shaped GEMM launch with cold caches: a
+    512 MiB buffer is written before every launch (more than the 256 MB
+    Infinity Cache and the L2s), and only the launch is timed with HIP
+    events (the fill keeps the queue ahead of the host)."""
+    import torch
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for a, b in [(None, None)] * 2 + evs:
+        scrub.fill_(1)
+        if a is not None:
+            a.record()
+        P.gemm(x_in, wq, offs, rows)
+        if b is not None:
+            b.record()
+    torch.cuda.synchronize()
+    del scrub
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
 
 def measured_traffic(summary_name):
