@@ -57,7 +57,9 @@ def parse():
                          "row/column scales, bf16 out) on the dense shape of each GEMM: a "
                          "reference point for what an FP8 GEMM reaches on this chip, not a "
                          "part of the path")
-    ap.add_argument("--cpu-sample-experts", type=int, default=48)
+    ap.add_argument("--cpu-sample-experts", type=int, default=0,
+                    help="experts in the oracle's GEMM sample (0: as many as fit about "
+                         "0.6 TFLOP of work, all 128 on the default workload)")
     return ap.parse_args()
 
 
@@ -236,6 +238,13 @@ def main():
                            frac_mfma=f_d / t_d / 1e9 / PEAK_F16_TFLOPS,
                            active_kblocks=bh, kblocks=K_d // 16))
         cnt = np.diff(rt.expert_offsets.cpu().numpy())
+        # quantize + RAC of X with cold caches (X is otherwise read from the
+        # Infinity Cache after the first step)
+        t_qx_cold = cold_ms(lambda: P.quantize_input(x, nsx), dev)
+        res["quant_x_cold_cache"] = dict(
+            us=t_qx_cold * 1e3, gbs=qx_bytes / t_qx_cold / 1e6,
+            frac_hbm=qx_bytes / t_qx_cold / 1e6 / PEAK_HBM_GBS,
+            note="512 MiB written before every call, so X comes from HBM")
         res["rows_per_expert"] = dict(min=int(cnt.min()), median=float(np.median(cnt)),
                                       max=int(cnt.max()), empty=int((cnt == 0).sum()))
         cfg = dict(workload=w.name, tokens=w.T, experts=w.E, topk=w.topk, hidden=w.H,
@@ -260,7 +269,7 @@ def main():
                              frac_hbm=g_bytes / t_g / 1e6 / PEAK_HBM_GBS),
                    gemm_back_to_back=dict(us=t_gk * 1e3, gbs=g_bytes / t_gk / 1e6,
                                           frac_hbm=g_bytes / t_gk / 1e6 / PEAK_HBM_GBS))
-        t_cold = dense_gemm_cold_ms(P, x_in, wq, offs, w.rows, dev)
+        t_cold = cold_ms(lambda: P.gemm(x_in, wq, offs, w.rows), dev)
         res["gemm_cold_cache"] = dict(us=t_cold * 1e3, gbs=g_bytes / t_cold / 1e6,
                                       frac_hbm=g_bytes / t_cold / 1e6 / PEAK_HBM_GBS,
                                       note="512 MiB written between launches, so W comes "
@@ -507,11 +516,11 @@ def dense_gemm_replay_ms(P, x_in, wq, offs, rows, n=20, reps=10):
     return a.elapsed_time(b) / (reps * n)
 
 
-def dense_gemm_cold_ms(P, x_in, wq, offs, rows, dev, n=20):
-    """Mean duration of one decode-shaped GEMM launch with cold caches: a
-    512 MiB buffer is written before every launch (more than the 256 MB
-    Infinity Cache and the L2s), and only the launch is timed with HIP
-    events (the fill keeps the queue ahead of the host)."""
+def cold_ms(fn, dev, n=20):
+    """Mean duration of fn()'s GPU work with cold caches: a 512 MiB buffer
+    is written before every call (more than the 256 MB Infinity Cache and
+    the L2s), and only fn() is timed with HIP events (the fill keeps the
+    queue ahead of the host)."""
     import torch
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -520,7 +529,7 @@ def dense_gemm_cold_ms(P, x_in, wq, offs, rows, dev, n=20):
         scrub.fill_(1)
         if a is not None:
             a.record()
-        P.gemm(x_in, wq, offs, rows)
+        fn()
         if b is not None:
             b.record()
     torch.cuda.synchronize()
@@ -549,7 +558,9 @@ def measured_traffic(summary_name):
 def cpu_baseline(w, x_np, n_experts, rac):
     """The oracle, as it stands, on a bounded sample of the same workload:
     quantize + RAC of X, then the gate/up grouped GEMM (main + residual) over
-    the routed rows of the first n_experts experts."""
+    the routed rows of the first n_experts experts (0: as many experts as
+    fit about 0.6 TFLOP of GEMM work, roughly 8 s for the oracle on 16
+    threads)."""
     from nvfp4_w4a4_moe_quant_amd import datagen as D
     from oracle import oracle as O
 
@@ -558,6 +569,9 @@ def cpu_baseline(w, x_np, n_experts, rac):
     if w.kind == "moe":
         d = O.quantize_rac(x_np, w.n_select_x)
         rt = O.route(D.router_logits(w), w.topk)
+        if n_experts <= 0:
+            per = 2.0 * (w.T * w.topk / w.E) * 2 * w.I * w.H * (2 if rac else 1)
+            n_experts = max(1, int(0.6e12 // per))
         ex = list(range(min(n_experts, w.E)))
         rows = np.concatenate([rt["gather"][rt["offsets"][e]:rt["offsets"][e + 1]] for e in ex])
         offs = np.concatenate([[0], np.cumsum([rt["offsets"][e + 1] - rt["offsets"][e] for e in ex])])
