@@ -149,7 +149,8 @@ int rac_select_residual(const void* x, int dtype, int64_t rows, int64_t K, int64
  * gather_rows [T*k]: source token of each grouped row, expert-major, tokens
  *          ascending within an expert.  row_of [T, k]: grouped row of
  *          (token, slot).
- * Requires 1 <= k <= min(E, 16), E <= 1024.
+ * Requires 1 <= k <= min(E, 16), E <= 1024.  With T == 0 the per-token
+ * pointers may be NULL and expert_offsets is all zero.
  * ------------------------------------------------------------------------ */
 size_t moe_route_workspace_size(int64_t T, int64_t E, int64_t k);
 int moe_route(const float* logits, int64_t T, int64_t E, int64_t k,

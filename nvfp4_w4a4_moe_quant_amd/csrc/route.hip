@@ -12,7 +12,10 @@
 //   k_scan     one workgroup: per-expert running sums over blocks, then an
 //              exclusive scan of the expert totals for the offsets
 //   k_scatter  per 256-token block: rank of each token inside its expert via
-//              LDS bit masks, then gather_rows / row_of
+//              LDS bit masks, then gather_rows / row_of.  When blocks^2 x E
+//              is small, each block sums the counts itself (the earlier
+//              blocks' for its base, all blocks' for the offsets) and k_scan
+//              is not launched.
 #include "common.h"
 
 namespace {
@@ -20,6 +23,7 @@ namespace {
 constexpr int kTok = 256;
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 16;
+constexpr int64_t kSelfScanLoads = 1 << 20;  // nblk^2 x E bound of the fused scan
 
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
@@ -130,23 +134,79 @@ __global__ __launch_bounds__(kMaxE) void k_scan(int32_t* __restrict__ cnt, int n
   if (e == E - 1) offsets[E] = before + inc;
 }
 
+// kSelf: the block computes its own base and the expert offsets from the
+// per-block counts cnt[nblk][E] (block 0 writes offsets); otherwise base and
+// offsets come from k_scan.
+template <bool kSelf>
 __global__ __launch_bounds__(kTok) void k_scatter(const int32_t* __restrict__ ids, int64_t T,
                                                   int E, int k, const int32_t* __restrict__ base,
-                                                  const int32_t* __restrict__ offsets,
+                                                  int nblk, int32_t* __restrict__ offsets,
                                                   int32_t* __restrict__ gather,
                                                   int32_t* __restrict__ row_of) {
   __shared__ uint32_t bits[kMaxE * (kTok / 32)];
+  __shared__ int32_t sbase[kSelf ? kMaxE : 1];  // first row of expert e in this block
   for (int i = threadIdx.x; i < E * (kTok / 32); i += kTok) bits[i] = 0u;
-  __syncthreads();
   const int tl = threadIdx.x;
+  // the token's experts are loaded first, so that their latency overlaps the
+  // count sums below
   const int64_t t = (int64_t)blockIdx.x * kTok + tl;
   int32_t my[kMaxK];
-  if (t < T) {
-    for (int s = 0; s < k; ++s) {
-      my[s] = ids[t * k + s];
-      atomicOr(&bits[my[s] * (kTok / 32) + (tl >> 5)], 1u << (tl & 31));
+  if (t < T)
+    for (int s = 0; s < k; ++s) my[s] = ids[t * k + s];
+  if constexpr (kSelf) {
+    // thread tl owns experts [per tl, per tl + per): rows in earlier blocks
+    // (run) and in all blocks (tot), then a scan of the totals.  The counts
+    // of 16 blocks are loaded before any is added.
+    constexpr int kPer = kMaxE / kTok, kB = 16;
+    __shared__ int32_t wtot[kTok / 64];
+    const int per = (E + kTok - 1) / kTok;
+    int32_t run[kPer], tot[kPer], mine = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) run[j] = tot[j] = 0;
+    for (int b0 = 0; b0 < nblk; b0 += kB) {
+      int32_t c[kB][kPer];
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          const int e = tl * per + j;
+          c[u][j] = (j < per && e < E && b0 + u < nblk) ? base[(int64_t)(b0 + u) * E + e] : 0;
+        }
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          tot[j] += c[u][j];
+          run[j] += b0 + u < (int)blockIdx.x ? c[u][j] : 0;
+        }
     }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) mine += tot[j];
+    const int lane = tl & 63, w = tl >> 6;
+    int32_t inc = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t n = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += n;
+    }
+    if (lane == 63) wtot[w] = inc;
+    __syncthreads();
+    int32_t off = inc - mine;
+    for (int i = 0; i < w; ++i) off += wtot[i];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int e = tl * per + j;
+      if (j < per && e < E) {
+        sbase[e] = off + run[j];
+        if (blockIdx.x == 0) offsets[e] = off;
+      }
+      off += tot[j];
+    }
+    if (blockIdx.x == 0 && tl == kTok - 1) offsets[E] = off;  // the total
   }
+  __syncthreads();
+  if (t < T)
+    for (int s = 0; s < k; ++s) atomicOr(&bits[my[s] * (kTok / 32) + (tl >> 5)], 1u << (tl & 31));
   __syncthreads();
   if (t < T) {
     for (int s = 0; s < k; ++s) {
@@ -154,7 +214,8 @@ __global__ __launch_bounds__(kTok) void k_scatter(const int32_t* __restrict__ id
       const uint32_t* m = bits + e * (kTok / 32);
       int rank = __builtin_popcount(m[tl >> 5] & ((1u << (tl & 31)) - 1u));
       for (int w = 0; w < (tl >> 5); ++w) rank += __builtin_popcount(m[w]);
-      const int32_t pos = offsets[e] + base[(int64_t)blockIdx.x * E + e] + rank;
+      const int32_t pos =
+          (kSelf ? sbase[e] : offsets[e] + base[(int64_t)blockIdx.x * E + e]) + rank;
       gather[pos] = (int32_t)t;
       row_of[t * k + s] = pos;
     }
@@ -236,7 +297,8 @@ size_t moe_route_workspace_size(int64_t T, int64_t E, int64_t) {
 int moe_route(const float* logits, int64_t T, int64_t E, int64_t k, int32_t* topk_ids,
               float* topk_weights, int32_t* expert_offsets, int32_t* gather_rows,
               int32_t* row_of, void* ws, size_t ws_bytes, void* stream) {
-  NV_RETURN_IF(!logits || !topk_ids || !expert_offsets || !gather_rows || !row_of,
+  // per-token buffers may be NULL when T == 0 (empty tensors have no storage)
+  NV_RETURN_IF(!expert_offsets || (T > 0 && (!logits || !topk_ids || !gather_rows || !row_of)),
                NVFP4_ERR_NULL);
   NV_RETURN_IF(T < 0 || E < 1 || E > kMaxE || k < 1 || k > E || k > kMaxK ||
                    T * k > INT32_MAX,
@@ -261,10 +323,18 @@ int moe_route(const float* logits, int64_t T, int64_t E, int64_t k, int32_t* top
     hipLaunchKernelGGL(k_counts, dim3((unsigned)nblk), dim3(kTok), 0, s, topk_ids, T, (int)E,
                        (int)k, cnt);
   }
+  // Every scatter block reads all nblk x E counts when it sums them itself;
+  // beyond kSelfScanLoads in total the one-workgroup scan is cheaper.
+  if (nblk * nblk * E <= kSelfScanLoads) {
+    // at least one block: block 0 writes the offsets (all zero when T == 0)
+    hipLaunchKernelGGL(k_scatter<true>, dim3((unsigned)(nblk > 0 ? nblk : 1)), dim3(kTok), 0, s,
+                       topk_ids, T, (int)E, (int)k, cnt, (int)nblk, expert_offsets, gather_rows,
+                       row_of);
+    return nv_launch_status();
+  }
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(kMaxE), 0, s, cnt, (int)nblk, (int)E, expert_offsets);
-  if (T > 0)
-    hipLaunchKernelGGL(k_scatter, dim3((unsigned)nblk), dim3(kTok), 0, s, topk_ids, T, (int)E,
-                       (int)k, cnt, expert_offsets, gather_rows, row_of);
+  hipLaunchKernelGGL(k_scatter<false>, dim3((unsigned)nblk), dim3(kTok), 0, s, topk_ids, T,
+                     (int)E, (int)k, cnt, (int)nblk, expert_offsets, gather_rows, row_of);
   return nv_launch_status();
 }
 

@@ -91,6 +91,10 @@ def test_route_validation(lib):
     def call(T=8, E=16, k=2, ws=FAKE, wsb=1 << 20, ids=FAKE):
         return lib.moe_route(FAKE, T, E, k, ids, None, FAKE, FAKE, FAKE, ws, wsb, None)
     assert call(ids=None) == ENULL
+    assert lib.moe_route(None, 8, 16, 2, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                         None) == ENULL            # logits needed when T > 0
+    assert lib.moe_route(None, 0, 16, 2, None, None, None, None, None, FAKE, 1 << 20,
+                         None) == ENULL            # expert_offsets needed even when T == 0
     assert call(k=0) == ESHAPE
     assert call(k=17, E=32) == ESHAPE
     assert call(E=2000) == ESHAPE

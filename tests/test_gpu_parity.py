@@ -118,9 +118,12 @@ def test_quant_empty_rows(orc):
 
 
 # ------------------------------------------------------------- routing
+# the last two cases are past the fused scan's bound (blocks^2 x E > 2^20): the
+# separate one-workgroup scan of the expert counts runs there
 @pytest.mark.parametrize("T,E,k,routing", [(1, 4, 1, "normal"), (300, 8, 2, "zipf"),
                                            (1000, 128, 8, "normal"), (777, 256, 8, "normal"),
-                                           (513, 64, 6, "zipf")])
+                                           (513, 64, 6, "zipf"), (20000, 256, 8, "zipf"),
+                                           (9000, 1024, 4, "normal")])
 def test_route(orc, T, E, k, routing):
     say(f"route T={T} E={E} k={k} {routing}")
     w = D.small_moe(90 + T, T, E, k, 64, 32, routing=routing, n_empty=2 if routing == "zipf" else 0)
@@ -132,6 +135,13 @@ def test_route(orc, T, E, k, routing):
     eq(host(rt.gather_rows), d["gather"], "gather")
     eq(host(rt.row_of), d["row_of"], "row_of")
     np.testing.assert_allclose(host(rt.topk_weights), d["topk_weights"], rtol=2e-5, atol=1e-7)
+
+
+def test_route_empty():
+    say("route T=0")
+    rt = L.moe_route(torch.zeros((0, 16), dtype=torch.float32, device=DEV), 4)
+    eq(host(rt.expert_offsets), np.zeros(17, np.int32), "offsets of no tokens")
+    assert rt.gather_rows.numel() == 0 and rt.row_of.numel() == 0
 
 
 def test_route_ties(orc):
