@@ -385,22 +385,37 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
           if (full || m0 + dm < row_end) ob[(int64_t)dm * p.N + b * 32] = yval(a, b, e);
         }
   } else {
-    uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + (int64_t)m0 * I + nt * (BN / 2) +
-                   wn * (WTN / 2) + lr;
+    // Elements e and e + 1 (e even) of a lane are rows dm and dm + 1 of its
+    // column.  Lanes l and l ^ 1 hold neighbouring columns, so one swap gives
+    // the even lane both columns of row dm and the odd lane both of row
+    // dm + 1, and each stores them as one 32-bit word.  Every lane computes
+    // its values (padded rows carry finite accumulators) so the swap is
+    // uniform; only rows inside the group are stored or enter the max.
+    const bool odd = (lr & 1) != 0;
+    uint32_t* ob = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(p.out) +
+                                               (int64_t)m0 * I + nt * (BN / 2) +
+                                               wn * (WTN / 2) + (lr & ~1));
     float hmax = 0.0f;
 #pragma unroll
     for (int a = 0; a < FM; ++a)
 #pragma unroll
       for (int b = 0; b < FN; b += 2)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
+        for (int e = 0; e < 16; e += 2) {
           const int dm = a * 32 + (e >> 2) * 8 + (e & 3);
-          if (full || m0 + dm < row_end) {
-            const float g = yval(a, b, e), u = yval(a, b + 1, e);
-            const float hv = silu_mul(g, u);
-            const uint32_t hb = nv_f32_to_bf16(hv);
-            ob[(int64_t)dm * I + (b >> 1) * 32] = (uint16_t)hb;
-            hmax = __builtin_fmaxf(hmax, __builtin_fabsf(nv_bf16_to_f32(hb)));
+          const uint32_t h0 = nv_f32_to_bf16(silu_mul(yval(a, b, e), yval(a, b + 1, e)));
+          const uint32_t h1 = nv_f32_to_bf16(silu_mul(yval(a, b, e + 1), yval(a, b + 1, e + 1)));
+          const bool v0 = full || m0 + dm < row_end, v1 = full || m0 + dm + 1 < row_end;
+          if (v0) hmax = __builtin_fmaxf(hmax, __builtin_fabsf(nv_bf16_to_f32(h0)));
+          if (v1) hmax = __builtin_fmaxf(hmax, __builtin_fabsf(nv_bf16_to_f32(h1)));
+          // DPP quad_perm [1, 0, 3, 2]: lane l reads lane l ^ 1
+          const uint32_t got =
+              (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? h0 : h1), 0xB1, 0xF, 0xF, false);
+          const int64_t col = (b >> 1) * 32;  // in bf16 elements, even
+          if (!odd) {
+            if (v0) ob[((int64_t)dm * I + col) >> 1] = h0 | (got << 16);
+          } else {
+            if (v1) ob[((int64_t)(dm + 1) * I + col) >> 1] = got | (h1 << 16);
           }
         }
     if (p.out_amax) {
