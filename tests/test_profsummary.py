@@ -72,3 +72,20 @@ def test_traffic_scaling(tmp_path, capsys):
     assert abs(rec["write_bytes"] - 50 * 1024) < 1e-6
     assert abs(rec["hbm_bytes"] - (400 + 50) * 1024) < 1e-6
     assert len(rec["source_sha256"]) == 64
+
+
+def test_kernel_stats_summary(tmp_path, capsys):
+    hdr = ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs",
+           "StdDev"]
+    _write(tmp_path / "s.csv", hdr, [
+        ["void (anonymous namespace)::k_gemm<64, 256, true>((anonymous namespace)::GemmParams)",
+         13, 6020773, 463136.4, 13.6, 436500, 486853, 1.0],
+        ["(anonymous namespace)::k_amax(void const*, int, long, long, long, float*)",
+         2, 9000, 4500.0, 0.1, 4000, 5000, 1.0]])
+    S.main(str(tmp_path / "s.csv"), command="cmd x")
+    out = capsys.readouterr().out.splitlines()
+    assert out[0] == "command: cmd x"
+    # names lose the namespace, the leading "void" and the argument list
+    assert out[2].split()[:3] == ["k_gemm<64,", "256,", "true>"]
+    assert out[2].split()[-5:] == ["13", "463.14", "436.50", "486.85", "13.60"]
+    assert out[3].split() == ["k_amax", "2", "4.50", "4.00", "5.00", "0.10"]
