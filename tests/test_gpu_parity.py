@@ -122,8 +122,8 @@ def test_quant_empty_rows(orc):
 # separate one-workgroup scan of the expert counts runs there
 @pytest.mark.parametrize("T,E,k,routing", [(1, 4, 1, "normal"), (300, 8, 2, "zipf"),
                                            (1000, 128, 8, "normal"), (777, 256, 8, "normal"),
-                                           (513, 64, 6, "zipf"), (20000, 256, 8, "zipf"),
-                                           (9000, 1024, 4, "normal")])
+                                           (513, 64, 6, "zipf"), (200, 384, 8, "normal"),
+                                           (20000, 256, 8, "zipf"), (9000, 1024, 4, "normal")])
 def test_route(orc, T, E, k, routing):
     say(f"route T={T} E={E} k={k} {routing}")
     w = D.small_moe(90 + T, T, E, k, 64, 32, routing=routing, n_empty=2 if routing == "zipf" else 0)
