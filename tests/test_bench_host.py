@@ -1,5 +1,6 @@
 """Host-side checks of bench.py (no GPU): the single-GPU guard and the lookup
 of the committed HBM-traffic records."""
+import hashlib
 import json
 import os
 import subprocess
@@ -18,17 +19,15 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_traffic_record_lookup(tmp_path, monkeypatch):
-    # the committed records describe the current GEMM source
-    rec = json.load(open(os.path.join(
-        ROOT, "profiles", "gemm_gate_up_moe_ffn_e128_top8_t4096_h2048_i768_traffic.json")))
-    got = bench.measured_traffic("gemm_gate_up_moe_ffn_e128_top8_t4096_h2048_i768")
-    assert got == int(round(rec["hbm_bytes"]))
-    assert bench.measured_traffic("gemm_no_such_workload") is None
-    # a record whose source has changed since the counters were taken is not used
     (tmp_path / "profiles").mkdir()
     src = tmp_path / "k.hip"
     src.write_text("kernel v1\n")
-    stale = dict(rec, source="k.hip", source_sha256="0" * 64)
-    (tmp_path / "profiles" / "gemm_x_traffic.json").write_text(json.dumps(stale))
+    sha = hashlib.sha256(src.read_bytes()).hexdigest()
+    rec = dict(kernel="k", hbm_bytes=123456.6, source="k.hip", source_sha256=sha)
+    (tmp_path / "profiles" / "gemm_x_traffic.json").write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.measured_traffic("gemm_x") == 123457
+    assert bench.measured_traffic("gemm_no_such_workload") is None
+    # a record whose source has changed since the counters were taken is not used
+    src.write_text("kernel v2\n")
     assert bench.measured_traffic("gemm_x") is None
