@@ -902,7 +902,7 @@ int w4a4_grouped_gemm_rac(const w4a4_gemm_args_t* a, void*, size_t, void* stream
   NV_RETURN_IF(!a->a_codes || !a->a_scales || !a->out, NVFP4_ERR_NULL);
   NV_RETURN_IF(a->r_codes && (!a->r_scales || !a->r_tscale), NVFP4_ERR_NULL);
   NV_RETURN_IF(!nv_aligned16(a->a_codes) || !nv_aligned16(a->w_codes) ||
-                   (a->r_codes && !nv_aligned16(a->r_codes)) ||
+                   !nv_aligned16(a->out) || (a->r_codes && !nv_aligned16(a->r_codes)) ||
                    (reinterpret_cast<uintptr_t>(a->a_scales) & 3) ||
                    (reinterpret_cast<uintptr_t>(a->w_scales) & 3) ||
                    (a->r_scales && (reinterpret_cast<uintptr_t>(a->r_scales) & 3)) ||

@@ -119,6 +119,7 @@ def test_gemm_validation(lib):
     assert call(N=96) == ESHAPE                     # N % 128
     assert call(num_groups=0) == ESHAPE
     assert call(a_codes=FAKE_MIS) == EALIGN
+    assert call(out=FAKE_MIS) == EALIGN             # every tensor 16-byte aligned
     assert call(kblock_active=ctypes.c_void_p(0x100004), r_codes=FAKE, r_scales=FAKE,
                 r_tscale=FAKE) == EALIGN
 
