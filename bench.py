@@ -43,7 +43,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=5,
+                    help="1-5 (default 5: the large MoE FFN layer, E=256, H=7168, I=2048, "
+                         "8192 tokens, the largest workload that fits one GPU)")
     ap.add_argument("--no-rac", action="store_true", help="naive W4A4 (RAC off)")
     ap.add_argument("--cpu-baseline", type=int, default=1)
     ap.add_argument("--comparators", type=int, default=1,
@@ -59,7 +61,11 @@ def parse():
                          "part of the path")
     ap.add_argument("--cpu-sample-experts", type=int, default=0,
                     help="experts in the oracle's GEMM sample (0: as many as fit about "
-                         "0.6 TFLOP of work, all 128 on the default workload)")
+                         "0.6 TFLOP of work: the largest, median and smallest non-empty "
+                         "experts, then seeded random ones)")
+    ap.add_argument("--decode-leg", type=int, default=1,
+                    help="MoE workloads: also time the decode-shaped dense GEMM "
+                         "(16x4096x4096, NVFP4 + RAC) against HBM and the launch floor")
     return ap.parse_args()
 
 
@@ -286,6 +292,8 @@ def main():
         res.update(moe_extras(w, dev, x, lg, wgu, wd, nsx, nsh, timed, step, ms_step, NEV))
     if args.extras and w.kind == "dense":
         res["graph"] = dense_graph(w, dev, x, wq, nsx, flops)
+    if args.decode_leg and w.kind == "moe":
+        res["decode_gemm"] = decode_leg(dev, rac)
     if "bytes" in dom:  # HBM-bound (decode shape): GB/s on the bytes the GEMM must move
         ach = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "kernel": dom["name"], "achieved": round(ach, 3),
@@ -433,6 +441,75 @@ def moe_extras(w, dev, x, lg, wgu, wd, nsx, nsh, timed, step, ms_step, nev):
     return out
 
 
+def decode_leg(dev, rac):
+    """The decode-shaped dense linear (16 x 4096 x 4096, bf16 input, NVFP4 + RAC
+    of the input, pre-quantized weight): the GEMM's duration from a graph of
+    back-to-back launches and with cold caches, against the bytes it must move
+    and HBM peak; and two floors measured the same way on this machine: the
+    duration of a one-element fill kernel (launch and completion alone) and
+    of a 2 MiB device copy (one 16-byte load and store per lane over about as
+    many lanes as the GEMM's grid)."""
+    import torch
+
+    from nvfp4_w4a4_moe_quant_amd import datagen as D
+    from nvfp4_w4a4_moe_quant_amd import pipeline as P
+
+    w = D.WORKLOADS[2]
+    x = torch.from_numpy(D.bf16_bits(D.activations(w)).view(np.int16)).to(dev).view(
+        torch.bfloat16)
+    W = torch.from_numpy(D.bf16_bits(D.dense_weight(w)).view(np.int16)).to(dev).view(
+        torch.bfloat16)
+    wq = P.quantize_weights([(0, W)], 1, w.N, w.K, dev)
+    offs = torch.tensor([0, w.rows], dtype=torch.int32, device=dev)
+    nsx = w.n_select_x if rac else None
+    x_in = P.quantize_input(x, nsx)
+    torch.cuda.synchronize()
+    nv = lambda r, k: r * k // 2 + r * k // 16
+    g_bytes = nv(w.N, w.K) + (2 if rac else 1) * nv(w.rows, w.K) + 4 * w.rows * w.N
+    t_b2b = dense_gemm_replay_ms(P, x_in, wq, offs, w.rows)
+    t_cold = cold_ms(lambda: P.gemm(x_in, wq, offs, w.rows), dev)
+    one = torch.zeros(1, dtype=torch.float32, device=dev)
+    t_fill = replay_ms(lambda: one.fill_(1.0))
+    src = torch.ones(2 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    t_copy = replay_ms(lambda: dst.copy_(src))
+    gbs = lambda t: g_bytes / t / 1e6
+    return dict(workload=w.name, bytes=g_bytes,
+                back_to_back=dict(us=round(t_b2b * 1e3, 2), gbs=round(gbs(t_b2b), 1),
+                                  frac_hbm=round(gbs(t_b2b) / PEAK_HBM_GBS, 4)),
+                cold_cache=dict(us=round(t_cold * 1e3, 2), gbs=round(gbs(t_cold), 1),
+                                frac_hbm=round(gbs(t_cold) / PEAK_HBM_GBS, 4)),
+                hbm_time_us=round(g_bytes / PEAK_HBM_GBS / 1e3, 2),
+                floor_fill_kernel_us=round(t_fill * 1e3, 2),
+                floor_2mib_copy_us=round(t_copy * 1e3, 2))
+
+
+def replay_ms(fn, n=20, reps=10):
+    """Mean duration of one fn() launch: n launches captured in one HIP graph,
+    the replay timed with HIP events on the capture stream."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            fn()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    b.synchronize()
+    return a.elapsed_time(b) / (reps * n)
+
+
 def dense_graph(w, dev, x, wq, nsx, flops):
     """The dense step (quantize + RAC + GEMM) eager against a HIP-graph
     replay of the same calls: at decode sizes the eager step is bound by host
@@ -572,7 +649,7 @@ def cpu_baseline(w, x_np, n_experts, rac):
         if n_experts <= 0:
             per = 2.0 * (w.T * w.topk / w.E) * 2 * w.I * w.H * (2 if rac else 1)
             n_experts = max(1, int(0.6e12 // per))
-        ex = list(range(min(n_experts, w.E)))
+        ex = sample_experts(rt["offsets"], min(n_experts, w.E), seed=1000 + w.seed)
         rows = np.concatenate([rt["gather"][rt["offsets"][e]:rt["offsets"][e + 1]] for e in ex])
         offs = np.concatenate([[0], np.cumsum([rt["offsets"][e + 1] - rt["offsets"][e] for e in ex])])
         wq = [O.quantize(m) for _, m in D.expert_weights(w, "gate_up", ex)]
@@ -586,8 +663,9 @@ def cpu_baseline(w, x_np, n_experts, rac):
         bx = int(d["active"].sum())
         flops = 2.0 * len(rows) * 2 * w.I * (w.H + (16 * bx if rac else 0))
         sample = (f"oracle quantize+RAC of X [{w.T}x{w.H}] and routing (not in the rate), then "
-                  f"the gate/up grouped GEMM over the {len(rows)} routed rows of experts "
-                  f"0..{len(ex) - 1} (main + residual, exact int64 sums)")
+                  f"the gate/up grouped GEMM over the {len(rows)} routed rows of {len(ex)} of "
+                  f"{w.E} experts (largest, median and smallest non-empty, then seeded random: "
+                  f"{ex}; main + residual, exact int64 sums)")
     else:
         d = O.quantize_rac(x_np, w.n_select_x)
         c, s, t = O.quantize(D.dense_weight(w))
@@ -602,7 +680,34 @@ def cpu_baseline(w, x_np, n_experts, rac):
         sample = f"oracle quantize+RAC and the full dense GEMM {w.rows}x{w.K}x{w.N}"
     return {"value": round(flops / (t2 - t1) / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle", "sample": sample, "gemm_s": round(t2 - t1, 2),
-            "total_s": round(t2 - t0, 2)}
+            "total_s": round(t2 - t0, 2), "cpu_model": cpu_model(),
+            "host_cpus": os.cpu_count()}
+
+
+def sample_experts(offsets, n, seed):
+    """n experts for the oracle's sample: the largest, median and smallest
+    non-empty experts by routed rows, then seeded random non-empty ones."""
+    cnt = np.diff(np.asarray(offsets))
+    nz = np.flatnonzero(cnt)
+    order = nz[np.argsort(cnt[nz], kind="stable")]
+    pick = [int(order[-1]), int(order[len(order) // 2]), int(order[0])]
+    rest = [int(e) for e in np.random.default_rng(seed).permutation(nz) if int(e) not in pick]
+    out = []
+    for e in pick + rest:
+        if e not in out:
+            out.append(e)
+    return sorted(out[:max(1, n)])
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":

@@ -41,7 +41,8 @@
  *    the caller's next synchronization.
  *  - Not checked on the device (preconditions): finite inputs; group offsets
  *    non-decreasing with the last equal to total_rows; gather indices in
- *    range; an `amax_in` not smaller than the true max|x|.
+ *    range; an `amax_in` not smaller than the true max|x|.  The group and
+ *    gather rules can be checked on host copies with nvfp4_check_groups.
  *  - Re-entrant on distinct buffers; results are bit-reproducible (integer
  *    and max reductions only; no floating-point atomics).
  */
@@ -229,7 +230,10 @@ int moe_combine(const float* y, const int32_t* row_of, const float* topk_weights
  * h[j, i] = bf16(silu(y[j, i]) * y[j, I + i]) to out [total_rows, I] and, if
  * out_amax is given, max-combines max|h| into *out_amax (an atomic max on the
  * float bits; the caller initializes *out_amax, normally to 0, so that the
- * call launches the GEMM kernel alone).
+ * call launches the GEMM kernel alone).  With SILU_MUL, a non-NULL out_y
+ * (float [total_rows, N], 4-byte aligned) also receives the FP32 values y
+ * that enter the SiLU*mul, gate columns then up columns as in W: the same
+ * kernel and accumulation, plus these stores (for verification).
  * Requires K % 128 == 0, N % 128 == 0, all tensors 16-byte aligned.
  * ------------------------------------------------------------------------ */
 typedef struct {
@@ -253,7 +257,18 @@ typedef struct {
   void* out;                    /* float [total_rows, N] or bf16 [total_rows, N/2] */
   float* out_amax;              /* SILU_MUL only, nullable, caller-initialized */
   int64_t flags;                /* NVFP4_GEMM_* bits */
+  float* out_y;                 /* SILU_MUL only, nullable: FP32 y [total_rows, N] */
 } w4a4_gemm_args_t;
+
+/* nvfp4_check_groups -- host-side check of the grouped GEMM's preconditions
+ * that the device does not check (a violation would read out of bounds).
+ * All pointers are HOST pointers (copies of the device arrays).
+ * offsets [G+1]: offsets[0] == 0, non-decreasing, offsets[G] == total_rows.
+ * gather [total_rows] (nullable): every index in [0, src_rows).
+ * Returns NVFP4_OK, NVFP4_ERR_NULL (offsets NULL) or NVFP4_ERR_SHAPE (the
+ * first violated rule).  Reads only; no device work. */
+int nvfp4_check_groups(const int32_t* offsets, int64_t G, int64_t total_rows,
+                       const int32_t* gather, int64_t src_rows);
 
 #define NVFP4_GEMM_SKIP_INACTIVE_BLOCKS 1
 /* Per-expert RAC: a_tscale and r_tscale are [G] (group g's tensor scales) and

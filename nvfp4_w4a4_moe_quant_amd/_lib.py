@@ -37,6 +37,7 @@ class GemmArgs(ctypes.Structure):
         ("kblock_active", _P),
         ("w_codes", _P), ("w_scales", _P), ("w_tscale", _P),
         ("epilogue", _I64), ("out", _P), ("out_amax", _P), ("flags", _I64),
+        ("out_y", _P),
     ]
 
 
@@ -76,6 +77,7 @@ _SIGS = {
     "nvfp4_dequantize": (ctypes.c_int, [_P, _P, _P, _I64, _I64, ctypes.c_int, _P, _P]),
     "fp8_quantize_rows": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _P, _P, _P]),
     "fp8_grouped_gemm": (ctypes.c_int, [ctypes.POINTER(Fp8GemmArgs), _P]),
+    "nvfp4_check_groups": (ctypes.c_int, [_P, _I64, _I64, _P, _I64]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -267,10 +269,17 @@ def w4a4_grouped_gemm_rac(a: NVFP4, w: NVFP4, group_offsets: torch.Tensor, *, N:
                           out: Optional[torch.Tensor] = None,
                           out_amax: Optional[torch.Tensor] = None,
                           skip_inactive: bool = False,
-                          per_group_scales: bool = False) -> torch.Tensor:
-    """w: codes [G, N, K/2], scales [G, N, K/16], tscale [G]."""
+                          per_group_scales: bool = False,
+                          out_y: Optional[torch.Tensor] = None,
+                          validate: bool = False) -> torch.Tensor:
+    """w: codes [G, N, K/2], scales [G, N, K/16], tscale [G].  With the SiLU*mul
+    epilogue, out_y (float32 [total_rows, N]) also receives the FP32 gate/up
+    values before the SiLU.  validate=True checks the offsets and gather
+    indices on the host first (check_groups; synchronizes)."""
     dev = a.codes.device
     G = group_offsets.numel() - 1
+    if validate:
+        check_groups(group_offsets, total_rows, gather_rows, a.codes.shape[0])
     if out is None:
         if epilogue == NVFP4_EPI_F32:
             out = torch.empty((total_rows, N), dtype=torch.float32, device=dev)
@@ -285,13 +294,30 @@ def w4a4_grouped_gemm_rac(a: NVFP4, w: NVFP4, group_offsets: torch.Tensor, *, N:
         w_codes=_ptr(w.codes), w_scales=_ptr(w.scales), w_tscale=_ptr(w.tscale),
         epilogue=epilogue, out=_ptr(out), out_amax=_ptr(out_amax),
         flags=(NVFP4_GEMM_SKIP_INACTIVE_BLOCKS if skip_inactive else 0) |
-              (NVFP4_GEMM_PER_GROUP_SCALES if per_group_scales else 0))
+              (NVFP4_GEMM_PER_GROUP_SCALES if per_group_scales else 0),
+        out_y=_ptr(out_y))
     L = lib()
     nbytes = L.w4a4_grouped_gemm_rac_workspace_size(ctypes.byref(args))
     ws = _ws(nbytes, dev) if nbytes else None
     _check(L.w4a4_grouped_gemm_rac(ctypes.byref(args), _ptr(ws), 0 if ws is None else ws.numel(),
                                    _stream(dev)))
     return out
+
+
+def check_groups(group_offsets: torch.Tensor, total_rows: int,
+                 gather_rows: Optional[torch.Tensor] = None, src_rows: int = 0) -> None:
+    """Checks the grouped GEMM's offsets and gather indices on host copies
+    (nvfp4_check_groups); raises NVFP4Error on a violation.  Synchronizes with
+    the device to copy the arrays."""
+    import numpy as np
+    offs = np.ascontiguousarray(group_offsets.cpu().numpy(), np.int32)
+    gat = None if gather_rows is None else \
+        np.ascontiguousarray(gather_rows.cpu().numpy(), np.int32)
+    if gat is not None and gat.size < total_rows:
+        raise NVFP4Error(f"gather_rows has {gat.size} entries, total_rows is {total_rows}")
+    _check(lib().nvfp4_check_groups(
+        offs.ctypes.data_as(ctypes.c_void_p), offs.size - 1, total_rows,
+        None if gat is None else gat.ctypes.data_as(ctypes.c_void_p), src_rows))
 
 
 def moe_combine(y: torch.Tensor, row_of: torch.Tensor, topk_weights: torch.Tensor, *,

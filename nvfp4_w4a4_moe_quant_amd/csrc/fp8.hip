@@ -30,7 +30,6 @@
 //    copies it takes a third of the time.  Larger tiles, deeper pipelines and
 //    issuing a chunk's last MFMAs after its barrier were measured and are
 //    not faster.
-#include <stdlib.h>
 
 #include "common.h"
 
@@ -371,26 +370,10 @@ int launch_f8(F8Params& p, hipStream_t s) {
   return nv_launch_status();
 }
 
-// Tile configurations; NVFP4RAC_FP8_CFG selects another one for tuning runs.
+// 128 x 128 tiles (waves of 64 x 64), two stages, two workgroups per CU.
 template <bool SILU, bool GATHER>
 int launch_f8_cfg(F8Params& p, hipStream_t s) {
-  static const int cfg = [] {
-    const char* e = getenv("NVFP4RAC_FP8_CFG");
-    return e ? atoi(e) : 0;
-  }();
-  if (p.N % 256) return launch_f8<128, 128, 2, 2, 2, 2, SILU, GATHER>(p, s);
-  switch (cfg) {
-    case 1: return launch_f8<128, 256, 2, 2, 3, 1, SILU, GATHER>(p, s);
-    case 2: return launch_f8<128, 128, 2, 2, 3, 1, SILU, GATHER>(p, s);
-    case 3: return launch_f8<64, 256, 2, 2, 3, 1, SILU, GATHER>(p, s);
-    case 4: return launch_f8<256, 128, 4, 1, 2, 1, SILU, GATHER>(p, s);
-    case 5: return launch_f8<64, 128, 2, 2, 2, 3, SILU, GATHER>(p, s);
-    case 6: return launch_f8<256, 128, 2, 2, 2, 1, SILU, GATHER>(p, s);
-    case 7: return launch_f8<128, 256, 2, 4, 2, 1, SILU, GATHER>(p, s);
-    default:
-      // 128 x 128 tiles (waves of 64 x 64), two stages, two workgroups per CU
-      return launch_f8<128, 128, 2, 2, 2, 2, SILU, GATHER>(p, s);
-  }
+  return launch_f8<128, 128, 2, 2, 2, 2, SILU, GATHER>(p, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -27,8 +27,6 @@
 //    workgroups reading one W tile are adjacent.
 //  * Double-buffered LDS; 16-byte code pieces are XOR-swizzled per row so that
 //    the fragment reads of 8 (or 16) consecutive rows hit distinct banks.
-#include <stdlib.h>
-
 #include <type_traits>
 
 #include "common.h"
@@ -102,6 +100,7 @@ struct GemmParams {
   int n_tiles;
   int skip;     // NVFP4_GEMM_SKIP_INACTIVE_BLOCKS
   int per_group;  // NVFP4_GEMM_PER_GROUP_SCALES: a_ts, r_ts [G], kact [G, K/16]
+  float* out_y;   // SiLU*mul epilogue only, nullable: FP32 gate/up outputs [rows, N]
 };
 
 // CPB chunks are computed between two barriers; NSTAGE LDS buffers hold the
@@ -391,6 +390,20 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
     // dm + 1, and each stores them as one 32-bit word.  Every lane computes
     // its values (padded rows carry finite accumulators) so the swap is
     // uniform; only rows inside the group are stored or enter the max.
+    if (p.out_y) {  // the FP32 gate/up values before the SiLU (verification)
+#pragma unroll
+      for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+          const int64_t n = ((b & 1) ? I : 0) + nt * (BN / 2) + wn * (WTN / 2) + (b >> 1) * 32 + lr;
+          float* yb = p.out_y + (int64_t)m0 * p.N + n;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int dm = a * 32 + (e >> 2) * 8 + (e & 3);
+            if (full || m0 + dm < row_end) yb[(int64_t)dm * p.N] = yval(a, b, e);
+          }
+        }
+    }
     const bool odd = (lr & 1) != 0;
     uint32_t* ob = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(p.out) +
                                                (int64_t)m0 * I + nt * (BN / 2) +
@@ -423,239 +436,6 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
       if (lane == 0 && hmax > 0.0f)
         atomicMax(reinterpret_cast<uint32_t*>(p.out_amax), __float_as_uint(hmax));
     }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Cooperative-dequant variant.  Each 16-byte run of codes (32 k of one row,
-// two NVFP4 blocks) is fetched once per workgroup into registers, dequantized
-// once, and written to LDS as fp16 in MFMA-fragment order: for every 32-row
-// fragment F and MFMA step s, 64 lanes x 16 bytes are contiguous, lane
-// h*32 + r holding row r's 8 values of k in [32h + 8s, 32h + 8s + 8) of the
-// 64-k chunk.  Waves then read ready-made operands with one conflict-free
-// ds_read_b128 per fragment and step.  Dequantization of chunk c+1 is
-// interleaved with the MFMAs of chunk c.
-constexpr int KC3 = 64;  // k per chunk (4 MFMA steps)
-
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MINW, bool RAC, bool SILU, bool GATHER>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void k_gemm3(GemmParams p) {
-  constexpr int NT = 64 * WAVES_M * WAVES_N;
-  constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
-  constexpr int FM = WTM / 32, FN = WTN / 32;
-  static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "tile");
-  static_assert(!SILU || FN % 2 == 0, "SiLU pairs gate/up fragments");
-  constexpr int AR = RAC ? 2 * BM : BM;
-  constexpr int ROWS = AR + BN;
-  static_assert((ROWS * 2) % NT == 0, "whole units per thread");
-  constexpr int NU = ROWS * 2 / NT;      // (row, half) units per thread per chunk
-  constexpr int STAGE = ROWS * KC3 * 2;  // fp16 bytes per stage
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
-  __shared__ uint32_t kact_lds[kMaxKChunks * 2];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const int lr = lane & 31, lh = lane >> 5;
-
-  const NvTile tile = nv_find_tile(p.offsets, p.G, BM, p.m_slots, p.n_tiles);
-  const int grp = tile.grp, local = tile.local, nt = tile.nt;
-  if (grp < 0) return;
-  const int row_beg = p.offsets[grp] + local * BM;
-  const int row_end = p.offsets[grp + 1];
-  const int K2 = p.K >> 1, K16 = p.K >> 4;
-  const int I = p.N >> 1;
-
-  auto src_row = [&](int i) -> int64_t {
-    int m = row_beg + i;
-    if (m >= row_end) m = row_end - 1;
-    return GATHER ? (int64_t)p.gather[m] : (int64_t)m;
-  };
-  auto w_row = [&](int i) -> int64_t {
-    int n;
-    if constexpr (SILU) {
-      const int wv = i / WTN, f = (i % WTN) / 32, rr = i % 32;
-      n = ((f & 1) ? I : 0) + nt * (BN / 2) + wv * (WTN / 2) + (f >> 1) * 32 + rr;
-    } else {
-      n = nt * BN + i;
-    }
-    return (int64_t)grp * p.N + n;
-  };
-
-  // per-thread units: (tile row, half) with the source pointers of chunk 0
-  const uint8_t* ucode[NU];
-  const uint8_t* uscale[NU];
-  uint32_t udst[NU];  // LDS byte offset of the unit's step-0 group
-#pragma unroll
-  for (int j = 0; j < NU; ++j) {
-    const int u = tid + NT * j;
-    const int row = u >> 1, h = u & 1;
-    const uint8_t *cb, *sb;
-    int64_t r;
-    if (row < BM) { r = src_row(row); cb = p.a_codes; sb = p.a_scales; }
-    else if (RAC && row < AR) { r = src_row(row - BM); cb = p.r_codes; sb = p.r_scales; }
-    else { r = w_row(row - AR); cb = p.w_codes; sb = p.w_scales; }
-    ucode[j] = cb + r * K2 + h * 16;
-    uscale[j] = sb + r * K16 + h * 2;
-    udst[j] = (uint32_t)((((row >> 5) * 4) * 64 + h * 32 + (row & 31)) * 16);
-  }
-
-  uint4 rc[NU];
-  uint32_t rs[NU];
-  auto gload = [&](int chunk) {
-#pragma unroll
-    for (int j = 0; j < NU; ++j) {
-      rc[j] = *reinterpret_cast<const uint4*>(ucode[j] + (int64_t)chunk * (KC3 / 2));
-      rs[j] = *reinterpret_cast<const uint16_t*>(uscale[j] + (int64_t)chunk * (KC3 / 16));
-    }
-  };
-  // dequantize step group s of every unit into stage buffer `st`
-  auto dq_store = [&](int s, uint8_t* st) {
-#pragma unroll
-    for (int j = 0; j < NU; ++j) {
-      const half2v sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rs[j], 1.0f, false);
-      const half2v s2 = (s < 2) ? __builtin_shufflevector(sc, sc, 0, 0)
-                                : __builtin_shufflevector(sc, sc, 1, 1);
-      const uint32_t c = s == 0 ? rc[j].x : s == 1 ? rc[j].y : s == 2 ? rc[j].z : rc[j].w;
-      *reinterpret_cast<half8*>(st + udst[j] + s * 1024) = dequant8(c, s2);
-    }
-  };
-
-  float16v accm[FM][FN], accr[RAC ? FM : 1][RAC ? FN : 1];
-#pragma unroll
-  for (int a = 0; a < FM; ++a)
-#pragma unroll
-    for (int b = 0; b < FN; ++b)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) accm[a][b][e] = 0.0f;
-  if constexpr (RAC) {
-#pragma unroll
-    for (int a = 0; a < FM; ++a)
-#pragma unroll
-      for (int b = 0; b < FN; ++b)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) accr[a][b][e] = 0.0f;
-  }
-
-  const int nchunks = p.K / KC3;
-  if constexpr (RAC) {
-    for (int c = tid; c < nchunks; c += NT)
-      kact_lds[c] = p.kact ? *reinterpret_cast<const uint32_t*>(
-                                 p.kact + (p.per_group ? (int64_t)grp * (p.K >> 4) : 0) +
-                                 (int64_t)c * 4)
-                           : ~0u;
-  }
-  // fragment bases (in 1 KiB units) of this wave's A, R and W operands
-  const int fa0 = (wm * WTM) >> 5, fr0 = (BM + wm * WTM) >> 5, fw0 = (AR + wn * WTN) >> 5;
-
-  gload(0);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) dq_store(s, lds);
-  if (nchunks > 1) gload(1);
-  __syncthreads();
-
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const uint8_t* cur = lds + (ch & 1) * STAGE;
-    uint8_t* nxt = lds + ((ch + 1) & 1) * STAGE;
-    const bool more = ch + 1 < nchunks;
-    uint32_t act = ~0u;
-    if constexpr (RAC) act = kact_lds[ch];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      half8 av[FM], wv[FN];
-#pragma unroll
-      for (int a = 0; a < FM; ++a)
-        av[a] = *reinterpret_cast<const half8*>(cur + (((fa0 + a) * 4 + s) * 64 + lane) * 16);
-#pragma unroll
-      for (int b = 0; b < FN; ++b)
-        wv[b] = *reinterpret_cast<const half8*>(cur + (((fw0 + b) * 4 + s) * 64 + lane) * 16);
-#pragma unroll
-      for (int a = 0; a < FM; ++a)
-#pragma unroll
-        for (int b = 0; b < FN; ++b)
-          accm[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[a], wv[b], accm[a][b], 0, 0, 0);
-      if constexpr (RAC) {
-        // blocks s/2 (lanes 0-31) and 2 + s/2 (lanes 32-63) of the chunk
-        if (((act >> (8 * (s >> 1))) & 0xFFu) | ((act >> (8 * (2 + (s >> 1)))) & 0xFFu)) {
-          half8 rv[FM];
-#pragma unroll
-          for (int a = 0; a < FM; ++a)
-            rv[a] = *reinterpret_cast<const half8*>(cur + (((fr0 + a) * 4 + s) * 64 + lane) * 16);
-#pragma unroll
-          for (int a = 0; a < FM; ++a)
-#pragma unroll
-            for (int b = 0; b < FN; ++b)
-              accr[a][b] =
-                  __builtin_amdgcn_mfma_f32_32x32x16_f16(rv[a], wv[b], accr[a][b], 0, 0, 0);
-        }
-      }
-      if (more) dq_store(s, nxt);
-    }
-    if (ch + 2 < nchunks) gload(ch + 2);
-    __syncthreads();
-  }
-
-  const float s_ta = p.a_ts[p.per_group ? grp : 0];
-  const float s_tr = RAC ? p.r_ts[p.per_group ? grp : 0] : 0.0f;
-  const float s_tw = p.w_ts[grp];
-  auto yval = [&](int a, int b, int e) -> float {
-    float y = s_ta * accm[a][b][e];
-    if constexpr (RAC) y = y + s_tr * accr[a][b][e];
-    return s_tw * y;
-  };
-  if constexpr (!SILU) {
-    float* out = reinterpret_cast<float*>(p.out);
-#pragma unroll
-    for (int a = 0; a < FM; ++a)
-#pragma unroll
-      for (int b = 0; b < FN; ++b)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = row_beg + wm * WTM + a * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
-          const int n = nt * BN + wn * WTN + b * 32 + lr;
-          if (m < row_end) out[(int64_t)m * p.N + n] = yval(a, b, e);
-        }
-  } else {
-    uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
-    float hmax = 0.0f;
-#pragma unroll
-    for (int a = 0; a < FM; ++a)
-#pragma unroll
-      for (int b = 0; b < FN; b += 2)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = row_beg + wm * WTM + a * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
-          const int hc = nt * (BN / 2) + wn * (WTN / 2) + (b >> 1) * 32 + lr;
-          if (m < row_end) {
-            const float g = yval(a, b, e), u = yval(a, b + 1, e);
-            const float hv = silu_mul(g, u);
-            const uint32_t hb = nv_f32_to_bf16(hv);
-            out[(int64_t)m * I + hc] = (uint16_t)hb;
-            hmax = __builtin_fmaxf(hmax, __builtin_fabsf(nv_bf16_to_f32(hb)));
-          }
-        }
-    if (p.out_amax) {
-      hmax = nv_wave_max(hmax);
-      if (lane == 0 && hmax > 0.0f)
-        atomicMax(reinterpret_cast<uint32_t*>(p.out_amax), __float_as_uint(hmax));
-    }
-  }
-}
-
-template <int BM, int BN, int WM, int WN, int MINW, bool RAC, bool SILU, bool GATHER>
-int launch3(GemmParams& p, hipStream_t s) {
-  constexpr int rows = (RAC ? 2 * BM : BM) + BN;
-  constexpr bool ok = (rows * 2) % (64 * WM * WN) == 0 && (!SILU || (BN / WN / 32) % 2 == 0) &&
-                      2 * rows * KC3 * 2 <= 160 * 1024 - 8 * kMaxKChunks;
-  if constexpr (!ok) {
-    return launch3<128, 128, 2, 2, 1, RAC, SILU, GATHER>(p, s);
-  } else {
-    if (p.N % BN || p.K % KC3) return NVFP4_ERR_SHAPE;
-    p.m_slots = (p.total_rows + BM - 1) / BM + p.G;
-    p.n_tiles = p.N / BN;
-    const int64_t nb = (int64_t)p.m_slots * p.n_tiles;
-    if (nb > 0x7fffffff) return NVFP4_ERR_SHAPE;
-    hipLaunchKernelGGL((k_gemm3<BM, BN, WM, WN, MINW, RAC, SILU, GATHER>), dim3((unsigned)nb),
-                       dim3(64 * WM * WN), 0, s, p);
-    return nv_launch_status();
   }
 }
 
@@ -837,38 +617,18 @@ int launch_gemv(GemmParams& p, hipStream_t s) {
 
 // Tile configurations (rows x cols per workgroup, waves, LDS stages, min waves
 // per SIMD, residual step skipping).  64-row tiles waste at most 63 padded rows
-// per MoE group of ~256 rows.  64 x 128 with 2 x 2 waves of 32 x 64 fits 128
-// VGPRs and runs four waves per SIMD; 64 x 256 with waves of 32 x 128 halves
-// the W conversions per MFMA at two waves per SIMD.  NVFP4RAC_GEMM_CFG selects
-// another configuration for tuning runs.
+// per MoE group of ~256 rows.  F32 output: 64 x 128 with 2 x 2 waves of
+// 32 x 64 (142 VGPRs, three waves per SIMD).  SiLU*mul with N % 256 == 0:
+// 64 x 256 with waves of 32 x 128 (236 VGPRs, two waves per SIMD), which
+// halves the A/R conversions per MFMA; other N take the 64 x 128 tile.
+// Block skipping: 64 x 128 at two waves per SIMD (150 VGPRs).
 template <bool RAC, bool SILU, bool GATHER>
 int launch_cfg(GemmParams& p, hipStream_t s) {
-  static const int cfg = [] {
-    const char* e = getenv("NVFP4RAC_GEMM_CFG");
-    return e ? atoi(e) : 0;
-  }();
   if (RAC && p.skip) return launch_t<64, 128, 2, 2, 2, 2, RAC, SILU, GATHER, true>(p, s);
-  switch (cfg) {
-    case 1: return launch_t<128, 128, 2, 2, 2, 2, RAC, SILU, GATHER, false>(p, s);
-    case 2: return launch_t<128, 128, 2, 2, 3, 1, RAC, SILU, GATHER, false>(p, s);
-    case 3: return launch_t<64, 256, 1, 4, 2, 2, RAC, SILU, GATHER, false>(p, s);
-    case 4: return launch_t<128, 128, 4, 1, 2, 2, RAC, SILU, GATHER, false>(p, s);
-    case 5: return launch_t<64, 256, 2, 2, 2, 2, RAC, SILU, GATHER, false>(p, s);
-    case 6: return launch_t<128, 128, 4, 1, 3, 1, RAC, SILU, GATHER, false>(p, s);
-    case 7: return launch_t<64, 128, 2, 2, 4, 2, RAC, SILU, GATHER, false, 2>(p, s);
-    case 8: return launch_t<64, 256, 2, 2, 4, 1, RAC, SILU, GATHER, false, 2>(p, s);
-    case 9: return launch_t<64, 128, 2, 2, 3, 2, RAC, SILU, GATHER, false, 1>(p, s);
-    case 12: return launch_t<64, 128, 2, 2, 2, 4, RAC, SILU, GATHER, false, 1>(p, s);
-    case 13: return launch_t<64, 128, 2, 2, 2, 3, RAC, SILU, GATHER, false, 1>(p, s);
-    case 10: return launch3<128, 128, 2, 2, 1, RAC, SILU, GATHER>(p, s);
-    case 11: return launch3<128, 256, 2, 4, 1, RAC, SILU, GATHER>(p, s);
-    default:
-      // gate/up (SiLU epilogue): 64 x 256 tiles, waves of 32 x 128, two waves
-      // per SIMD, 4-5% faster on the MoE workloads; F32 output (down): 64 x
-      // 128 tiles, waves of 32 x 64, four waves per SIMD
-      if constexpr (SILU) return launch_t<64, 256, 2, 2, 2, 2, RAC, SILU, GATHER, false>(p, s);
-      else return launch_t<64, 128, 2, 2, 2, 2, RAC, SILU, GATHER, false>(p, s);
+  if constexpr (SILU) {
+    if (p.N % 256 == 0) return launch_t<64, 256, 2, 2, 2, 2, RAC, SILU, GATHER, false>(p, s);
   }
+  return launch_t<64, 128, 2, 2, 2, 2, RAC, SILU, GATHER, false>(p, s);
 }
 
 int launch(GemmParams& p, bool rac, bool silu, bool gather, hipStream_t s) {
@@ -883,6 +643,19 @@ int launch(GemmParams& p, bool rac, bool silu, bool gather, hipStream_t s) {
 }  // namespace
 
 extern "C" {
+
+int nvfp4_check_groups(const int32_t* offsets, int64_t G, int64_t total_rows,
+                       const int32_t* gather, int64_t src_rows) {
+  NV_RETURN_IF(!offsets, NVFP4_ERR_NULL);
+  NV_RETURN_IF(G < 1 || total_rows < 0 || offsets[0] != 0 || offsets[G] != total_rows,
+               NVFP4_ERR_SHAPE);
+  for (int64_t g = 0; g < G; ++g) NV_RETURN_IF(offsets[g + 1] < offsets[g], NVFP4_ERR_SHAPE);
+  if (gather) {
+    for (int64_t j = 0; j < total_rows; ++j)
+      NV_RETURN_IF(gather[j] < 0 || gather[j] >= src_rows, NVFP4_ERR_SHAPE);
+  }
+  return NVFP4_OK;
+}
 
 size_t w4a4_grouped_gemm_rac_workspace_size(const w4a4_gemm_args_t*) { return 0; }
 
@@ -903,6 +676,8 @@ int w4a4_grouped_gemm_rac(const w4a4_gemm_args_t* a, void*, size_t, void* stream
   NV_RETURN_IF(a->r_codes && (!a->r_scales || !a->r_tscale), NVFP4_ERR_NULL);
   NV_RETURN_IF(!nv_aligned16(a->a_codes) || !nv_aligned16(a->w_codes) ||
                    !nv_aligned16(a->out) || (a->r_codes && !nv_aligned16(a->r_codes)) ||
+                   (a->epilogue == NVFP4_EPI_SILU_MUL_BF16 && a->out_y &&
+                    (reinterpret_cast<uintptr_t>(a->out_y) & 3)) ||
                    (reinterpret_cast<uintptr_t>(a->a_scales) & 3) ||
                    (reinterpret_cast<uintptr_t>(a->w_scales) & 3) ||
                    (a->r_scales && (reinterpret_cast<uintptr_t>(a->r_scales) & 3)) ||
@@ -928,6 +703,7 @@ int w4a4_grouped_gemm_rac(const w4a4_gemm_args_t* a, void*, size_t, void* stream
   p.w_ts = a->w_tscale;
   p.out = a->out;
   p.out_amax = a->epilogue == NVFP4_EPI_SILU_MUL_BF16 ? a->out_amax : nullptr;
+  p.out_y = a->epilogue == NVFP4_EPI_SILU_MUL_BF16 ? a->out_y : nullptr;
   p.skip = (a->flags & NVFP4_GEMM_SKIP_INACTIVE_BLOCKS) && a->kblock_active ? 1 : 0;
   p.per_group = (a->flags & NVFP4_GEMM_PER_GROUP_SCALES) ? 1 : 0;
   const bool rac = a->r_codes != nullptr, gather = a->gather_rows != nullptr;

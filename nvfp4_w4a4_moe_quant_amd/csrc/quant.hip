@@ -16,7 +16,6 @@
 //   k_residual  r = mask * e re-quantized in the same blocks; also the
 //               residual tensor scale and the ascending selected indices
 // All reductions are max or integer sums, so results are order-independent.
-#include <stdlib.h>
 
 #include "common.h"
 
@@ -726,24 +725,14 @@ static int quantize_launch(const void* x, int dtype, int64_t rows, int64_t K, in
   // Column tiles of at most tile_max column blocks (16: 256 channels, 512 B
   // of bf16 per row), rpi rows in flight per pass.  Narrow tiles keep the
   // global atomics per workgroup few.
-  static const int tile_max = [] {
-    const char* e = getenv("NVFP4RAC_QUANT_TPR");
-    return e ? atoi(e) : 16;
-  }();
+  constexpr int tile_max = 16;
   const int64_t ntile = (CB + tile_max - 1) / tile_max;
   const int tpr = (int)((CB + ntile - 1) / ntile);
   const int rpi = kQThreads / tpr;
   // Row splits: with statistics every workgroup adds one atomic per channel
   // to the global sums, so the splits stay few (about one workgroup per CU
   // over all column tiles) and each thread takes at least two rows.
-  static const int wg_target = [] {
-    const char* e = getenv("NVFP4RAC_QUANT_WGS");
-    return e ? atoi(e) : 256;
-  }();
-  static const int min_rows = [] {
-    const char* e = getenv("NVFP4RAC_QUANT_MINROWS");
-    return e ? atoi(e) : 2;
-  }();
+  constexpr int wg_target = 256, min_rows = 2;
   int64_t splits = blocks_for(rows, (int64_t)rpi * min_rows, 65535);
   const int64_t max_splits = stats ? (wg_target / ntile > 0 ? wg_target / ntile : 1) : 65535;
   if (splits > max_splits) splits = max_splits;

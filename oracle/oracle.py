@@ -7,8 +7,13 @@ NumPy marshalling.  No arithmetic of the method happens in this file.
 
 Parity status: every function is pinned by the CPU tests in
 ``tests/test_oracle_*.py`` (closed forms, brute force, the worked example,
-invariants); nothing here is "parity unpinned" except the SiLU step, whose
-exp() is evaluated in double and is compared to the GPU within one bf16 ulp.
+invariants, and for the SiLU*mul step and the routing weights a 50-digit
+``decimal`` evaluation of exp).  The GPU's SiLU uses the hardware exp, so H
+is compared with the oracle within one bf16 ulp.
+
+``build_sanitized()`` compiles the same source with AddressSanitizer and
+UndefinedBehaviorSanitizer; setting NVFP4RAC_ORACLE_LIB to its path (with
+libasan preloaded) makes ``lib()`` load that build instead.
 """
 from __future__ import annotations
 
@@ -35,6 +40,19 @@ def build(force: bool = False) -> str:
         subprocess.run(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"], check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
+
+
+def build_sanitized() -> str:
+    """Compile oracle.c with ASan + UBSan (abort on the first report) into
+    liboracle_san.so next to it; returns the path."""
+    path = os.path.join(_HERE, "liboracle_san.so")
+    flags = [f for f in CFLAGS if f != "-O2"] + [
+        "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+        "-fno-sanitize-recover=all"]
+    tmp = path + f".tmp{os.getpid()}"
+    subprocess.run(["gcc", *flags, "-o", tmp, _SRC, "-lm"], check=True)
+    os.replace(tmp, path)
+    return path
 
 
 _P = ctypes.c_void_p
@@ -79,8 +97,10 @@ _SIGS = {
 def lib():
     global _lib
     if _lib is None:
-        build()
-        l = ctypes.CDLL(_LIB_PATH)
+        path = os.environ.get("NVFP4RAC_ORACLE_LIB")
+        if not path:
+            path = build()
+        l = ctypes.CDLL(path)
         for name, (res, args) in _SIGS.items():
             f = getattr(l, name)
             f.restype = res

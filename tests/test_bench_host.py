@@ -31,3 +31,14 @@ def test_traffic_record_lookup(tmp_path, monkeypatch):
     # a record whose source has changed since the counters were taken is not used
     src.write_text("kernel v2\n")
     assert bench.measured_traffic("gemm_x") is None
+
+
+def test_sample_experts():
+    import numpy as np
+    offs = np.concatenate([[0], np.cumsum([5, 0, 9, 2, 7, 0, 3, 4])])
+    ex = bench.sample_experts(offs, 5, seed=1)
+    assert len(ex) == 5 and ex == sorted(ex)
+    assert {2, 3} <= set(ex)                # largest (9 rows) and smallest non-empty (2)
+    assert not {1, 5} & set(ex)             # empty experts are never sampled
+    assert bench.sample_experts(offs, 99, seed=1) == [0, 2, 3, 4, 6, 7]
+    assert bench.sample_experts(offs, 5, seed=1) == bench.sample_experts(offs, 5, seed=1)

@@ -122,6 +122,36 @@ def test_gemm_validation(lib):
     assert call(out=FAKE_MIS) == EALIGN             # every tensor 16-byte aligned
     assert call(kblock_active=ctypes.c_void_p(0x100004), r_codes=FAKE, r_scales=FAKE,
                 r_tscale=FAKE) == EALIGN
+    assert call(epilogue=1, out_y=ctypes.c_void_p(0x100002)) == EALIGN   # FP32 side output
+
+
+def test_check_groups(lib):
+    """nvfp4_check_groups on host arrays: each rule, and the binding's raise."""
+    import numpy as np
+
+    def chk(offs, total, gather=None, src=0):
+        o = np.ascontiguousarray(offs, np.int32)
+        g = None if gather is None else np.ascontiguousarray(gather, np.int32)
+        return lib.nvfp4_check_groups(o.ctypes.data_as(ctypes.c_void_p), o.size - 1, total,
+                                      None if g is None else g.ctypes.data_as(ctypes.c_void_p),
+                                      src)
+    assert chk([0, 3, 3, 7], 7) == OK
+    assert chk([0, 3, 3, 7], 7, [0, 1, 2, 4, 4, 3, 0], 5) == OK
+    assert chk([0, 3, 3, 7], 7, [0, 1, 2, 5, 4, 3, 0], 5) == ESHAPE   # index == src_rows
+    assert chk([0, 3, 3, 7], 7, [0, 1, -1, 4, 4, 3, 0], 5) == ESHAPE  # negative index
+    assert chk([0, 4, 3, 7], 7) == ESHAPE            # decreasing
+    assert chk([1, 3, 3, 7], 7) == ESHAPE            # does not start at 0
+    assert chk([0, 3, 3, 6], 7) == ESHAPE            # does not end at total_rows
+    assert chk([0], 0) == ESHAPE                     # no group
+    assert lib.nvfp4_check_groups(None, 1, 0, None, 0) == ENULL
+    import torch
+    with pytest.raises(L.NVFP4Error):
+        L.check_groups(torch.tensor([0, 2, 1], dtype=torch.int32), 1)
+    with pytest.raises(L.NVFP4Error):
+        L.check_groups(torch.tensor([0, 2], dtype=torch.int32), 2,
+                       torch.tensor([0, 9], dtype=torch.int32), src_rows=4)
+    L.check_groups(torch.tensor([0, 2], dtype=torch.int32), 2,
+                   torch.tensor([0, 3], dtype=torch.int32), src_rows=4)
 
 
 def test_fp8_validation(lib):
