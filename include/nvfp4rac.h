@@ -119,10 +119,12 @@ int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ld
  * selected out [n_select] int32, ascending channel indices.
  * kblock_active out [K/16]: 1 where the 16-block holds a selected channel.
  * res_codes/res_scales out, same layout as codes/scales; res_tensor_scale out:
- *          r = e on selected channels and 0 elsewhere, quantized as its own
- *          NVFP4 tensor in the same 16-element blocks with
- *          s_tr = RN32(max over selected k of channel_max[k] / 2688)
- *          (= max|r| / 2688).
+ *          r = e on selected channels and 0 elsewhere, quantized to NVFP4 in
+ *          the same 16-element blocks with the activation's own tensor scale
+ *          s_t (the residual pass shares the main pass's tensor scale, so the
+ *          GEMM adds both passes in one accumulator): block scale
+ *          E4M3(RN32(max|r_b| / (6 s_t))), codes as nvfp4_quantize.
+ *          *res_tensor_scale receives s_t.
  * Requires K <= 16384 and the layout rules of nvfp4_quantize; ws 4-byte
  * aligned.  The result is deterministic (integer ranks, max reductions).
  * ------------------------------------------------------------------------ */
@@ -216,9 +218,13 @@ int moe_combine(const float* y, const int32_t* row_of, const float* topk_weights
  *
  * For grouped row j of group g (offsets[g] <= j < offsets[g+1]) and src =
  * gather_rows[j] (or j when gather_rows is NULL):
- *   y[j, n] = s_tw[g] * ( s_ta * sum_k A[src,k] W_g[n,k]
- *                       + s_tr * sum_{k in active blocks} R[src,k] W_g[n,k] )
- * with A, R, W the exact dequantized values g * s_b (FP32 accumulation).
+ *   y[j, n] = s_tw[g] * s_ta * ( sum_k A[src,k] W_g[n,k]
+ *                              + sum_{k in active blocks} R[src,k] W_g[n,k] )
+ * with A, R, W the exact dequantized values g * s_b, both passes accumulated
+ * in one FP32 accumulator.  The residual shares the activation's tensor
+ * scale (rac_select_residual writes *r_tscale = s_ta): the call requires
+ * *r_tscale == *a_tscale (per group with NVFP4_GEMM_PER_GROUP_SCALES) and
+ * writes NaN outputs for a group where they differ.
  * r_codes == NULL turns RAC off (naive W4A4).  kblock_active == NULL means
  * every block is active.  With NVFP4_GEMM_SKIP_INACTIVE_BLOCKS in `flags`, the
  * residual MFMAs of each 32-k step run only if one of its two 16-blocks is

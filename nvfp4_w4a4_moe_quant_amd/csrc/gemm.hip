@@ -13,9 +13,11 @@
 //    conversion and the scale multiply are packed VALU ops.
 //  * v_mfma_f32_32x32x16_f16 (gfx950) accumulates exact fp16 products in FP32.
 //    K = 16 per instruction is exactly one NVFP4 block.
-//  * Main and residual rows share every W fragment; they keep separate FP32
-//    accumulators because their tensor scales differ:
-//        y = s_tw * (s_ta * acc_main + s_tr * acc_res).
+//  * Main and residual rows share every W fragment and, since the residual is
+//    quantized with the activation's own tensor scale, one FP32 accumulator:
+//        y = s_tw * s_ta * (sum A W + sum R W).
+//    One accumulator set per fragment leaves the registers for 64 x 128 wave
+//    tiles, which dequantize half an operand fragment per MFMA.
 //  * K is consumed in chunks of 128 (8 MFMA steps).  Inside a chunk, lanes
 //    32-63 take the upper 64 k of the chunk instead of the next 8 (a fixed
 //    permutation of k applied identically to A, R and W, so the contraction is
@@ -103,15 +105,20 @@ struct GemmParams {
   float* out_y;   // SiLU*mul epilogue only, nullable: FP32 gate/up outputs [rows, N]
 };
 
-// CPB chunks are computed between two barriers; NSTAGE LDS buffers hold the
-// CPB chunks being computed and the NSTAGE - CPB chunks in flight.
+// Rows of A and R past an expert's last row (the padding of its last m-tile)
+// are read from this zero row: zero codes and zero block scales dequantize to
+// 0, so the matrix cores spend little power on them.  K <= 32768.
+__device__ uint8_t nv_zero_row[kMaxKChunks * CODE_ROW];
+
+// The grouped GEMM.  BM x BN output tile per workgroup, WAVES_M x WAVES_N
+// waves of (BM / WAVES_M) x (BN / WAVES_N), NSTAGE LDS stages of KC k.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int MINW, bool RAC, bool SILU,
-          bool GATHER, bool RSKIP = true, int CPB = 1>
+          bool GATHER, bool RSKIP>
 __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
   static_assert(WAVES_M * WAVES_N == 4, "4 waves");
   constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   constexpr int FM = WTM / 32, FN = WTN / 32;
-  static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "tile");
+  static_assert(FM >= 1 && FM <= 2 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "tile");
   static_assert(!SILU || FN % 2 == 0, "SiLU pairs gate/up fragments");
   constexpr int AR = RAC ? 2 * BM : BM;  // A rows then R rows
   constexpr int ROWS = AR + BN;          // then W rows
@@ -120,7 +127,7 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
   constexpr int NSI = ROWS * 2 / kThreads;  // 4-byte scale words per thread per chunk
   constexpr int STAGE_CODES = ROWS * CODE_ROW;
   constexpr int STAGE = STAGE_CODES + ROWS * SCALE_ROW;
-  static_assert(NSTAGE >= 2 * CPB && (NSTAGE - 2 * CPB) * (NPI + NSI) <= 63, "vmcnt range");
+  static_assert(NSTAGE >= 2 && (NSTAGE - 2) * (NPI + NSI) <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * STAGE];
   __shared__ uint64_t kact_lds[kMaxKChunks];
 
@@ -137,12 +144,7 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
   const int K2 = p.K >> 1, K16 = p.K >> 4;
   const int I = p.N >> 1;
 
-  // ---- source rows of the LDS tile rows
-  auto src_row = [&](int i) -> int64_t {  // i in [0, BM)
-    int m = row_beg + i;
-    if (m >= row_end) m = row_end - 1;
-    return GATHER ? (int64_t)p.gather[m] : (int64_t)m;
-  };
+  // ---- source rows of the LDS tile rows; rows past the group's end read zeros
   auto w_row = [&](int i) -> int64_t {  // i in [0, BN)
     int n;
     if constexpr (SILU) {
@@ -153,14 +155,19 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
     }
     return (int64_t)grp * p.N + n;
   };
+  auto act_row = [&](const uint8_t* base, int i, int per_row) -> const uint8_t* {
+    const int m = row_beg + i;
+    if (m >= row_end) return nv_zero_row;
+    return base + (GATHER ? (int64_t)p.gather[m] : (int64_t)m) * per_row;
+  };
   auto code_row_ptr = [&](int i) -> const uint8_t* {
-    if (i < BM) return p.a_codes + src_row(i) * K2;
-    if (RAC && i < AR) return p.r_codes + src_row(i - BM) * K2;
+    if (i < BM) return act_row(p.a_codes, i, K2);
+    if (RAC && i < AR) return act_row(p.r_codes, i - BM, K2);
     return p.w_codes + w_row(i - AR) * K2;
   };
   auto scale_row_ptr = [&](int i) -> const uint8_t* {
-    if (i < BM) return p.a_scales + src_row(i) * K16;
-    if (RAC && i < AR) return p.r_scales + src_row(i - BM) * K16;
+    if (i < BM) return act_row(p.a_scales, i, K16);
+    if (RAC && i < AR) return act_row(p.r_scales, i - BM, K16);
     return p.w_scales + w_row(i - AR) * K16;
   };
 
@@ -204,29 +211,25 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
     }
   };
 
-  float16v accm[FM][FN], accr[RAC ? FM : 1][RAC ? FN : 1];
+  // One FP32 accumulator per fragment: the residual shares the activation's
+  // tensor scale, so both passes add into it.
+  float16v acc[FM][FN];
 #pragma unroll
   for (int a = 0; a < FM; ++a)
 #pragma unroll
     for (int b = 0; b < FN; ++b)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) accm[a][b][e] = 0.0f;
-  if constexpr (RAC) {
-#pragma unroll
-    for (int a = 0; a < FM; ++a)
-#pragma unroll
-      for (int b = 0; b < FN; ++b)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) accr[a][b][e] = 0.0f;
-  }
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
 
   const int arow0 = wm * WTM + lr;       // + a*32 (A), + BM (R)
-  const bool wave_live = row_beg + wm * WTM < row_end;  // wave-uniform
   const int wrow0 = AR + wn * WTN + lr;  // + b*32
+  // live 32-row fragments of this wave: rows past the group's end are padding
+  const int wave_rows = row_end - (row_beg + wm * WTM);  // wave-uniform
+  const int fm_live = wave_rows <= 0 ? 0 : (wave_rows <= 32 ? 1 : FM);
 
   const int nchunks = p.K / KC;
   // residual block activity, 8 blocks (one chunk) per 64-bit word
-  if constexpr (RAC) {
+  if constexpr (RAC && RSKIP) {
     for (int c = tid; c < nchunks; c += kThreads)
       kact_lds[c] = p.kact ? *reinterpret_cast<const uint64_t*>(
                                  p.kact + (p.per_group ? (int64_t)grp * (p.K >> 4) : 0) +
@@ -234,13 +237,13 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
                            : ~0ull;
   }
 
-  // One chunk (8 MFMA steps).  With RSKIP, the residual MFMAs of a step run
-  // only when one of its two blocks holds a selected channel; inactive blocks
-  // carry all-zero residual codes, so running them is exact as well.
-  auto compute = [&](int ch, const uint8_t* base) {
-    constexpr bool RES = RAC;
-    // activity of the chunk's 8 blocks as a wave-uniform 8-bit mask (SGPR)
-    uint32_t act = 0xFFu;
+  // One chunk (8 MFMA steps) over the first FMX fragments of the wave.  With
+  // RSKIP, the residual MFMAs of a step run only when one of its two blocks
+  // holds a selected channel; inactive blocks carry all-zero residual codes,
+  // so running them is exact as well.
+  auto compute = [&](auto fmx_c, int ch, const uint8_t* base) {
+    constexpr int FMX = decltype(fmx_c)::value;
+    uint32_t act = 0xFFu;  // activity of the chunk's 8 blocks (SGPR)
     if constexpr (RAC && RSKIP) {
       const uint64_t w = kact_lds[ch];
       uint32_t m = 0;
@@ -248,15 +251,14 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
       for (int b = 0; b < 8; ++b) m |= ((w >> (8 * b)) & 0xFFull) ? (1u << b) : 0u;
       act = __builtin_amdgcn_readfirstlane(m);
     }
-
     // scales of the lane's 4 blocks for every fragment row
-    half2v sa01[FM], sa23[FM], sr01[RES ? FM : 1], sr23[RES ? FM : 1], sw01[FN], sw23[FN];
+    half2v sa01[FMX], sa23[FMX], sr01[RAC ? FMX : 1], sr23[RAC ? FMX : 1], sw01[FN], sw23[FN];
 #pragma unroll
-    for (int a = 0; a < FM; ++a) {
+    for (int a = 0; a < FMX; ++a) {
       const int i = arow0 + a * 32;
       scales4(*reinterpret_cast<const uint32_t*>(base + STAGE_CODES + i * SCALE_ROW + lh * 4),
               sa01[a], sa23[a]);
-      if constexpr (RES)
+      if constexpr (RAC)
         scales4(*reinterpret_cast<const uint32_t*>(base + STAGE_CODES + (i + BM) * SCALE_ROW +
                                                    lh * 4),
                 sr01[a], sr23[a]);
@@ -267,16 +269,15 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
       scales4(*reinterpret_cast<const uint32_t*>(base + STAGE_CODES + i * SCALE_ROW + lh * 4),
               sw01[b], sw23[b]);
     }
-
 #pragma unroll
     for (int hp = 0; hp < 2; ++hp) {
       const uint32_t pc = 2 * lh + hp;
-      uint4 ca[FM], cr[RES ? FM : 1], cw[FN];
+      uint4 ca[FMX], cr[RAC ? FMX : 1], cw[FN];
 #pragma unroll
-      for (int a = 0; a < FM; ++a) {
+      for (int a = 0; a < FMX; ++a) {
         const uint32_t i = arow0 + a * 32;
         ca[a] = *reinterpret_cast<const uint4*>(base + i * CODE_ROW + ((pc ^ swz(i)) << 4));
-        if constexpr (RES) {
+        if constexpr (RAC) {
           const uint32_t ir = i + BM;
           cr[a] = *reinterpret_cast<const uint4*>(base + ir * CODE_ROW + ((pc ^ swz(ir)) << 4));
         }
@@ -288,85 +289,79 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
       }
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
-        const int s = hp * 4 + s4;  // MFMA step in the chunk
-        const int blk = s >> 1;     // block among the lane's four
-        half8 av[FM], wv[FN];
+        const int blk = (hp * 4 + s4) >> 1;  // block among the lane's four
+        half8 av[FMX], wv[FN];
 #pragma unroll
         for (int b = 0; b < FN; ++b) {
           const uint32_t c = s4 == 0 ? cw[b].x : s4 == 1 ? cw[b].y : s4 == 2 ? cw[b].z : cw[b].w;
           wv[b] = dequant8(c, pick_scale(sw01[b], sw23[b], blk));
         }
 #pragma unroll
-        for (int a = 0; a < FM; ++a) {
+        for (int a = 0; a < FMX; ++a) {
           const uint32_t c = s4 == 0 ? ca[a].x : s4 == 1 ? ca[a].y : s4 == 2 ? ca[a].z : ca[a].w;
           av[a] = dequant8(c, pick_scale(sa01[a], sa23[a], blk));
         }
 #pragma unroll
-        for (int a = 0; a < FM; ++a)
+        for (int a = 0; a < FMX; ++a)
 #pragma unroll
           for (int b = 0; b < FN; ++b)
-            accm[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[a], wv[b], accm[a][b], 0, 0, 0);
-        if (RES && (!RSKIP || (act & ((1u << blk) | (1u << (4 + blk)))))) {
-          half8 rv[FM];
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[a], wv[b], acc[a][b], 0, 0, 0);
+        if (RAC && (!RSKIP || (act & ((1u << blk) | (1u << (4 + blk)))))) {
+          half8 rv[RAC ? FMX : 1];
 #pragma unroll
-          for (int a = 0; a < FM; ++a) {
+          for (int a = 0; a < FMX; ++a) {
             const uint32_t c = s4 == 0 ? cr[a].x : s4 == 1 ? cr[a].y : s4 == 2 ? cr[a].z : cr[a].w;
             rv[a] = dequant8(c, pick_scale(sr01[a], sr23[a], blk));
           }
 #pragma unroll
-          for (int a = 0; a < FM; ++a)
+          for (int a = 0; a < FMX; ++a)
 #pragma unroll
             for (int b = 0; b < FN; ++b)
-              accr[a][b] =
-                  __builtin_amdgcn_mfma_f32_32x32x16_f16(rv[a], wv[b], accr[a][b], 0, 0, 0);
+              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rv[a], wv[b], acc[a][b], 0, 0, 0);
         }
       }
     }
   };
 
-  // NSTAGE-deep pipeline, CPB chunks per barrier: chunks ch .. ch+CPB-1 are
-  // computed while chunks up to ch + NSTAGE - 1 are in flight; before the
-  // barrier that ends the iteration, chunks ch+CPB .. ch+2CPB-1 must have
-  // landed, i.e. at most the DMA of the later chunks may be outstanding.
+  // Two-deep pipeline: chunk ch is computed while chunk ch + NSTAGE - 1 is in
+  // flight; before the barrier that ends the iteration, chunk ch + 1 must have
+  // landed.  Waves without live rows (the padded part of an expert's last
+  // tile) still load and synchronize.
   constexpr int PER_CHUNK = NPI + NSI;
-  constexpr int AHEAD = NSTAGE - CPB;  // chunks in flight while CPB are computed
+  constexpr int AHEAD = NSTAGE - 1;
+  auto run = [&](auto fmx_c) {
 #pragma unroll
-  for (int c = 0; c < AHEAD; ++c)
-    if (c < nchunks) issue(c, c);
-  if (nchunks > CPB && NSTAGE > 2 * CPB)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NSTAGE - 2 * CPB) * PER_CHUNK) : "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int ch = 0; ch < nchunks; ch += CPB) {
-#pragma unroll
-    for (int u = 0; u < CPB; ++u) {
-      const int nxt = ch + AHEAD + u;
-      if (nxt < nchunks) issue(nxt, nxt % NSTAGE);
-    }
-    // A wave whose rows all lie past the group's end (the padded half of an
-    // expert's last tile) has nothing to compute; it still loads and syncs.
-    if (wave_live) {
-#pragma unroll
-      for (int u = 0; u < CPB; ++u)
-        if (ch + u < nchunks) compute(ch + u, lds + ((ch + u) % NSTAGE) * STAGE);
-    }
-    if (ch + AHEAD + CPB - 1 < nchunks && NSTAGE > 2 * CPB)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NSTAGE - 2 * CPB) * PER_CHUNK) : "memory");
+    for (int c = 0; c < AHEAD; ++c)
+      if (c < nchunks) issue(c, c);
+    if (nchunks > 1 && NSTAGE > 2)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NSTAGE - 2) * PER_CHUNK) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-  }
-
-  // ---- epilogue
-  const float s_ta = p.a_ts[p.per_group ? grp : 0];
-  const float s_tr = RAC ? p.r_ts[p.per_group ? grp : 0] : 0.0f;
-  const float s_tw = p.w_ts[grp];
-  auto yval = [&](int a, int b, int e) -> float {
-    float y = s_ta * accm[a][b][e];
-    if constexpr (RAC) y = y + s_tr * accr[a][b][e];
-    return s_tw * y;
+    for (int ch = 0; ch < nchunks; ++ch) {
+      const int nxt = ch + AHEAD;
+      if (nxt < nchunks) issue(nxt, nxt % NSTAGE);
+      if constexpr (decltype(fmx_c)::value > 0) compute(fmx_c, ch, lds + (ch % NSTAGE) * STAGE);
+      if (ch + AHEAD < nchunks && NSTAGE > 2)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NSTAGE - 2) * PER_CHUNK) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
   };
+  if (fm_live == FM) run(std::integral_constant<int, FM>{});
+  else if (fm_live == 1) run(std::integral_constant<int, 1>{});
+  else run(std::integral_constant<int, 0>{});
+
+  // ---- epilogue: y = s_tw * s_ta * acc.  The residual pass assumed the
+  // activation's tensor scale; a residual tensor scale that differs makes the
+  // group's outputs NaN rather than silently wrong.
+  const float s_ta = p.a_ts[p.per_group ? grp : 0];
+  float scale = p.w_ts[grp] * s_ta;
+  if constexpr (RAC) {
+    if (p.r_ts[p.per_group ? grp : 0] != s_ta) scale = __builtin_nanf("");
+  }
+  auto yval = [&](int a, int b, int e) -> float { return scale * acc[a][b][e]; };
   // Element e of fragment (a, b) sits at row m0 + a*32 + (e>>2)*8 + (e&3) of
   // the lane's column; the base pointer is formed once, and a wave whose 32
   // x FM rows all lie inside the group stores without per-element checks.
@@ -440,18 +435,17 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
 }
 
 template <int BM, int BN, int WM, int WN, int NS, int MINW, bool RAC, bool SILU, bool GATHER,
-          bool RSKIP = true, int CPB = 1>
+          bool RSKIP>
 int launch_t(GemmParams& p, hipStream_t s) {
   constexpr int rows = (RAC ? 2 * BM : BM) + BN;
-  if constexpr (rows % 128 != 0) {
-    return launch_t<128, 128, 2, 2, 2, 2, RAC, SILU, GATHER, RSKIP>(p, s);
-  } else {
+  static_assert(rows % 128 == 0, "whole wave-loads of codes and scales");
+  {
     if (p.N % BN) return NVFP4_ERR_SHAPE;
     p.m_slots = (p.total_rows + BM - 1) / BM + p.G;
     p.n_tiles = p.N / BN;
     const int64_t nb = (int64_t)p.m_slots * p.n_tiles;
     if (nb > 0x7fffffff) return NVFP4_ERR_SHAPE;
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, NS, MINW, RAC, SILU, GATHER, RSKIP, CPB>), dim3((unsigned)nb),
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, NS, MINW, RAC, SILU, GATHER, RSKIP>), dim3((unsigned)nb),
                        dim3(kThreads), 0, s, p);
     return nv_launch_status();
   }
@@ -482,7 +476,7 @@ constexpr int kGvMaxRows = 64;    // rows up to which the decode kernel is used
 template <int WAVES, int GRP, bool RAC, bool GATHER>
 __global__ __launch_bounds__(64 * WAVES) void k_gemv16(GemmParams p) {
   constexpr int NCG = 1;  // 16-column groups per workgroup (2 measured slower)
-  __shared__ float4v red[WAVES][2][NCG][64];
+  __shared__ float4v red[WAVES][NCG][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // K slice of this wave, rotated by the workgroup id so that the workgroups
   // (which all read the same A and R rows) spread over different lines
@@ -491,8 +485,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv16(GemmParams p) {
   const int K = p.K;
   const int kw = K / WAVES;  // k per wave
   const float s_ta = p.a_ts[0];  // one group
-  const float s_tr = RAC ? p.r_ts[0] : 0.0f;
-  const float s_tw = p.w_ts[0];
+  float scale = p.w_ts[0] * s_ta;
+  if constexpr (RAC) {
+    if (p.r_ts[0] != s_ta) scale = __builtin_nanf("");  // the residual shares s_ta
+  }
   const int m = (int)blockIdx.y * 16 + c;  // A row fed by this lane
   const bool mv = m < p.total_rows;
   // W rows fed by this lane: one per 16-column group of the workgroup
@@ -501,9 +497,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv16(GemmParams p) {
   const uint8_t* wsc = p.w_scales + n0 * (K >> 4);
   const int64_t cgc = (int64_t)16 * (K >> 1), cgs = (int64_t)16 * (K >> 4);  // next group
 
-  float4v accm[NCG], accr[NCG];
+  float4v accm[NCG];  // main and residual passes (one tensor scale)
 #pragma unroll
-  for (int j = 0; j < NCG; ++j) accm[j] = accr[j] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < NCG; ++j) accm[j] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
   const int64_t src = mv ? (GATHER ? (int64_t)p.gather[m] : (int64_t)m) : 0;
   const uint8_t* ac = p.a_codes + src * (K >> 1);
   const uint8_t* asc = p.a_scales + src * (K >> 4);
@@ -571,37 +567,27 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv16(GemmParams p) {
           const half8 bw = dequant8(ww, s_w);
           accm[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ba, bw, accm[j], 0, 0, 0);
           if constexpr (RAC)
-            accr[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(br, bw, accr[j], 0, 0, 0);
+            accm[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(br, bw, accm[j], 0, 0, 0);
         }
       }
     }
   }
 
 #pragma unroll
-  for (int j = 0; j < NCG; ++j) {
-    red[w][0][j][lane] = accm[j];
-    red[w][1][j][lane] = accr[j];
-  }
+  for (int j = 0; j < NCG; ++j) red[w][j][lane] = accm[j];
   __syncthreads();
   // wave j adds the K slices of column group j in slice order
   if (wave >= NCG) return;
   const int j = wave;
-  float4v sm = red[0][0][j][lane], sr = red[0][1][j][lane];
+  float4v sm = red[0][j][lane];
 #pragma unroll
-  for (int i = 1; i < WAVES; ++i) {
-    sm += red[i][0][j][lane];
-    sr += red[i][1][j][lane];
-  }
+  for (int i = 1; i < WAVES; ++i) sm += red[i][j][lane];
   float* out = reinterpret_cast<float*>(p.out);
   const int64_t n = n0 + 16 * j;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = (int)blockIdx.y * 16 + 4 * q + i;  // D row of element i
-    if (row < p.total_rows) {
-      float y = s_ta * sm[i];
-      if constexpr (RAC) y = y + s_tr * sr[i];
-      out[(int64_t)row * p.N + n] = s_tw * y;
-    }
+    if (row < p.total_rows) out[(int64_t)row * p.N + n] = scale * sm[i];
   }
 }
 
@@ -616,19 +602,24 @@ int launch_gemv(GemmParams& p, hipStream_t s) {
 }
 
 // Tile configurations (rows x cols per workgroup, waves, LDS stages, min waves
-// per SIMD, residual step skipping).  64-row tiles waste at most 63 padded rows
-// per MoE group of ~256 rows.  F32 output: 64 x 128 with 2 x 2 waves of
-// 32 x 64 (142 VGPRs, three waves per SIMD).  SiLU*mul with N % 256 == 0:
-// 64 x 256 with waves of 32 x 128 (236 VGPRs, two waves per SIMD), which
-// halves the A/R conversions per MFMA; other N take the 64 x 128 tile.
-// Block skipping: 64 x 128 at two waves per SIMD (150 VGPRs).
+// per SIMD, residual step skipping).  N % 256 == 0: 128 x 256 tiles, 2 x 2
+// waves of 64 x 128 (two 32-row fragments per wave; a wave whose second
+// fragment is all padding skips it), two workgroups per CU.  Other N, and
+// residual block skipping: with RAC, 64 x 128 tiles (waves of 32 x 64); RAC
+// off, 128 x 128 (waves of 64 x 64), so that the staged rows fill whole
+// wave-loads.
 template <bool RAC, bool SILU, bool GATHER>
 int launch_cfg(GemmParams& p, hipStream_t s) {
-  if (RAC && p.skip) return launch_t<64, 128, 2, 2, 2, 2, RAC, SILU, GATHER, true>(p, s);
-  if constexpr (SILU) {
-    if (p.N % 256 == 0) return launch_t<64, 256, 2, 2, 2, 2, RAC, SILU, GATHER, false>(p, s);
+  // block skipping needs registers for its activity mask: 64 x 128 tiles
+  if constexpr (RAC) {
+    if (p.skip) return launch_t<64, 128, 2, 2, 2, 2, RAC, SILU, GATHER, true>(p, s);
   }
-  return launch_t<64, 128, 2, 2, 2, 2, RAC, SILU, GATHER, false>(p, s);
+  if (p.N % 256 == 0) return launch_t<128, 256, 2, 2, 2, 2, RAC, SILU, GATHER, false>(p, s);
+  if constexpr (RAC) {
+    return launch_t<64, 128, 2, 2, 2, 2, RAC, SILU, GATHER, false>(p, s);
+  } else {
+    return launch_t<128, 128, 2, 2, 2, 2, RAC, SILU, GATHER, false>(p, s);
+  }
 }
 
 int launch(GemmParams& p, bool rac, bool silu, bool gather, hipStream_t s) {

@@ -13,8 +13,8 @@
 //               per-channel error statistics (score = sum q^2, max |e|)
 //   k_rank      rank of every channel by (score desc, index asc); the
 //               first n are selected; block masks and activity flags
-//   k_residual  r = mask * e re-quantized in the same blocks; also the
-//               residual tensor scale and the ascending selected indices
+//   k_residual  r = mask * e re-quantized in the same blocks with the
+//               activation's tensor scale; the ascending selected indices
 // All reductions are max or integer sums, so results are order-independent.
 
 #include "common.h"
@@ -542,10 +542,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select_group(
 // r = mask * e in every block with a selected channel, e = x - deq(q(x)).
 // The main codes are recomputed from x, the block scale and the tensor scale
 // (the same operations as k_quant, so the same codes) rather than read back:
-// that saves a quarter of this pass's reads.  Every workgroup first reduces
-// k_rank's per-workgroup maxima to the residual tensor scale; workgroup 0
-// also writes it and lists the selected channels in ascending order (a prefix
-// sum of the block masks' popcounts).
+// that saves a quarter of this pass's reads.  The residual is quantized with
+// the activation's tensor scale s_t (the residual pass of the GEMM shares
+// it), so its block scales are E4M3(max|r_b| / (6 s_t)); |r| <= max|x| keeps
+// them within E4M3's range.  Workgroup 0 writes the residual tensor scale
+// (= s_t) and lists the selected channels in ascending order (a prefix sum of
+// the block masks' popcounts).
 __global__ __launch_bounds__(kThreads) void k_residual(
     const void* __restrict__ x, int bf16, int64_t rows, int64_t K, int64_t ldx,
     const uint8_t* __restrict__ scales, const float* __restrict__ tscale,
@@ -570,20 +572,11 @@ __global__ __launch_bounds__(kThreads) void k_residual(
     if (selected) selected += (int64_t)g * n_sel;
   }
   __shared__ uint16_t lmask[kMaxSelectK / 16];  // block masks, so x loads wait on nothing
-  float a = 0.0f;
-  for (int i = threadIdx.x; i < nparts; i += kThreads) {  // nparts = K / 16 blocks
-    a = __builtin_fmaxf(a, __uint_as_float(part_max[i]));
-    lmask[i] = mask16[i];
-  }
-  a = nv_wave_max(a);
-  if ((threadIdx.x & 63) == 0) wred[threadIdx.x >> 6] = __float_as_uint(a);
+  (void)part_max;
+  for (int i = threadIdx.x; i < nparts; i += kThreads) lmask[i] = mask16[i];  // K / 16 blocks
   __syncthreads();
-  float m_all = 0.0f;
-#pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) m_all = __builtin_fmaxf(m_all, __uint_as_float(wred[w]));
-  const float s_tr = nv_tensor_scale(m_all);
+  const float s_tr = *tscale;  // the residual pass shares the activation's tensor scale
   if (blockIdx.x == 0) {
-    __syncthreads();  // wred is reused by the scan
     if (threadIdx.x == 0) *res_ts = s_tr;
     // thread t lists the selected channels of blocks [t*pb, t*pb + pb)
     constexpr int kPb = (kMaxSelectK / 16 + kThreads - 1) / kThreads;

@@ -94,13 +94,17 @@ def e2m1_nearest(a: Fr) -> int:
 
 
 # --- quantizer ---------------------------------------------------------------
-def quantize(x, amax=None):
+def quantize(x, amax=None, s_t=None):
     """x: list of rows of Fractions (FP32 values).  Returns (codes, scale bytes,
-    s_t) with codes as a list of rows of 4-bit ints (unpacked)."""
+    s_t) with codes as a list of rows of 4-bit ints (unpacked).  s_t, when
+    given, is the tensor scale to use (the residual pass uses the main pass's);
+    otherwise s_t = RN32(amax / 2688) with amax = max|x| by default."""
     rows, K = len(x), len(x[0])
-    if amax is None:
-        amax = max((abs(v) for row in x for v in row), default=Fr(0))
-    s_t = rn32(Fr(amax) / 2688)
+    if s_t is None:
+        if amax is None:
+            amax = max((abs(v) for row in x for v in row), default=Fr(0))
+        s_t = rn32(Fr(amax) / 2688)
+    s_t = Fr(s_t)
     codes, scales = [], []
     for row in x:
         crow, srow = [], []

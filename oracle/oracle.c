@@ -147,6 +147,23 @@ static int quantize_block(const float* x, float s_t, uint8_t* elem_codes) {
   return sc;
 }
 
+/* Block-quantize every row of x[rows, K] (row stride ldx) with the tensor
+ * scale s_t: per 16-block scale byte and E2M1 codes, packed. */
+static void quantize_rows(const float* x, int64_t rows, int64_t K, int64_t ldx, float s_t,
+                          uint8_t* codes, uint8_t* scales) {
+  int64_t r;
+#pragma omp parallel for schedule(static)
+  for (r = 0; r < rows; r++) {
+    uint8_t ec[16];
+    for (int64_t b = 0; b < K / 16; b++) {
+      int sc = quantize_block(x + r * ldx + b * 16, s_t, ec);
+      scales[r * (K / 16) + b] = (uint8_t)sc;
+      for (int i = 0; i < 16; i += 2)
+        codes[r * (K / 2) + b * 8 + i / 2] = (uint8_t)(ec[i] | (ec[i + 1] << 4));
+    }
+  }
+}
+
 /* NVFP4-quantize x[rows, K] (row stride ldx floats).
  * codes[rows, K/2]: element 2j in the low nibble of byte j, 2j+1 in the high.
  * scales[rows, K/16]: E4M3 bytes.  *tscale_out = s_t.
@@ -157,6 +174,7 @@ int or_quantize(const float* x, int64_t rows, int64_t K, int64_t ldx,
   float amax = 0.0f, s_t;
   int64_t r;
   if (K % 16 != 0) return 2;
+  (void)r;
   if (amax_in) {
     amax = *amax_in;
   } else {
@@ -168,16 +186,7 @@ int or_quantize(const float* x, int64_t rows, int64_t K, int64_t ldx,
   }
   s_t = or_tensor_scale(amax);
   *tscale_out = s_t;
-#pragma omp parallel for schedule(static)
-  for (r = 0; r < rows; r++) {
-    uint8_t ec[16];
-    for (int64_t b = 0; b < K / 16; b++) {
-      int sc = quantize_block(x + r * ldx + b * 16, s_t, ec);
-      scales[r * (K / 16) + b] = (uint8_t)sc;
-      for (int i = 0; i < 16; i += 2)
-        codes[r * (K / 2) + b * 8 + i / 2] = (uint8_t)(ec[i] | (ec[i + 1] << 4));
-    }
-  }
+  quantize_rows(x, rows, K, ldx, s_t, codes, scales);
   return 0;
 }
 
@@ -270,11 +279,11 @@ static int int_cmp(const void* a, const void* b) {
 /* Select the n_sel channels with the largest score, ties toward the lower
  * channel index [FIX: "roughly top-50%"; n_sel = K/2 exactly in the
  * workloads].  Outputs: selected[n_sel] ascending, mask[K], active[K/16]
- * (block holds a selected channel), and the residual tensor scale
- * s_tr = RN32(max_{k selected} chmax[k] / 2688). */
+ * (block holds a selected channel), and res_amax = max over the selected
+ * channels of chmax[k], which is max|r| of the residual. */
 void or_rac_select(const int64_t* score, const float* chmax, int64_t K,
                    int64_t n_sel, int32_t* selected, uint8_t* mask,
-                   uint8_t* active, float* res_tscale) {
+                   uint8_t* active, float* res_amax) {
   key_t_* keys = (key_t_*)malloc(sizeof(key_t_) * (size_t)(K > 0 ? K : 1));
   float amax_r = 0.0f;
   int64_t i;
@@ -292,15 +301,17 @@ void or_rac_select(const int64_t* score, const float* chmax, int64_t K,
     for (int j = 0; j < 16; j++) any |= mask[i * 16 + j];
     active[i] = (uint8_t)any;
   }
-  *res_tscale = or_tensor_scale(amax_r);
+  *res_amax = amax_r;
   free(keys);
 }
 
 /* Masked residual r = mask * e, re-quantized to NVFP4 in the same 16-element
- * blocks with its own tensor scale [FIX: the selected channels' residual gets
- * its own 4-bit pass].  The residual tensor amax is max|r| computed here
- * directly from r; it is also returned so tests can check it against the
- * selection's s_tr. */
+ * blocks [FIX: the selected channels' residual goes through a second 4-bit
+ * pass inside the same kernels].  Reading: the residual pass uses the main
+ * pass's tensor scale s_t -- its block scales are E4M3(RN32(max|r_b| /
+ * (6 s_t))) and its codes follow N2-N4 with that s_t -- so that both passes of
+ * the GEMM share the activation's tensor scale.  *res_tscale_out = s_t.
+ * Every residual block scale stays within E4M3's range: |r| <= max|x|. */
 void or_rac_residual(const float* x, int64_t rows, int64_t K, int64_t ldx,
                      const uint8_t* codes, const uint8_t* scales, float s_t,
                      const uint8_t* mask, uint8_t* res_codes,
@@ -311,7 +322,8 @@ void or_rac_residual(const float* x, int64_t rows, int64_t K, int64_t ldx,
   for (i = 0; i < rows; i++)
     for (k = 0; k < K; k++)
       r[i * K + k] = mask[k] ? quant_error(x, ldx, codes, scales, s_t, K, i, k) : 0.0f;
-  or_quantize(r, rows, K, K, NULL, res_codes, res_scales, res_tscale_out);
+  quantize_rows(r, rows, K, K, s_t, res_codes, res_scales);
+  *res_tscale_out = s_t;
   if (res_out) memcpy(res_out, r, sizeof(float) * (size_t)(rows * K));
   free(r);
 }
@@ -700,9 +712,8 @@ void or_moe_combine(const float* y, const int32_t* row_of, const float* w, int64
  * the per-tensor oracle above applied to that tensor.  Outputs are in
  * grouped row order (codes [rows, K/2], scales [rows, K/16], residual codes
  * and scales likewise); per-group arrays: s_t[G], score[G, K], chmax[G, K],
- * selected[G, n_sel], active[G, K/16], s_tr[G] (the selection's residual
- * scale, max over the selected channels' max|e| / 2688).  score == NULL
- * quantizes only (no RAC). */
+ * selected[G, n_sel], active[G, K/16], s_tr[G] (the residual's tensor scale,
+ * which is the group's s_t).  score == NULL quantizes only (no RAC). */
 void or_quantize_rac_grouped(const float* x, int64_t K, const int32_t* offsets, int64_t G,
                              const int32_t* gather, int64_t n_sel, uint8_t* codes,
                              uint8_t* scales, float* s_t, int64_t* score, float* chmax,
@@ -713,7 +724,7 @@ void or_quantize_rac_grouped(const float* x, int64_t K, const int32_t* offsets, 
   for (g = 0; g < G; g++) {
     const int64_t j0 = offsets[g], rows = offsets[g + 1] - offsets[g];
     float* sub = (float*)malloc(sizeof(float) * (size_t)(rows * K > 0 ? rows * K : 1));
-    float s_tr_res;
+    float amax_r;
     for (i = 0; i < rows; i++) {
       const int64_t src = gather ? gather[j0 + i] : j0 + i;
       memcpy(sub + i * K, x + src * K, sizeof(float) * (size_t)K);
@@ -723,9 +734,9 @@ void or_quantize_rac_grouped(const float* x, int64_t K, const int32_t* offsets, 
       or_channel_stats(sub, rows, K, K, codes + j0 * (K / 2), scales + j0 * (K / 16), s_t[g],
                        score + g * K, chmax + g * K);
       or_rac_select(score + g * K, chmax + g * K, K, n_sel, selected + g * n_sel, mask,
-                    active + g * (K / 16), &s_tr[g]);
+                    active + g * (K / 16), &amax_r);
       or_rac_residual(sub, rows, K, K, codes + j0 * (K / 2), scales + j0 * (K / 16), s_t[g],
-                      mask, res_codes + j0 * (K / 2), res_scales + j0 * (K / 16), &s_tr_res,
+                      mask, res_codes + j0 * (K / 2), res_scales + j0 * (K / 16), &s_tr[g],
                       NULL);
     }
     free(sub);

@@ -191,14 +191,15 @@ def rac_select(score, chmax, n_select):
     sel = np.zeros(max(n_select, 0), np.int32)
     mask = np.zeros(K, np.uint8)
     active = np.zeros(K // 16, np.uint8)
-    ts = np.zeros(1, np.float32)
+    am = np.zeros(1, np.float32)
     lib().or_rac_select(_p(score), _p(chmax), K, n_select, _p(sel), _p(mask),
-                        _p(active), _p(ts))
-    return sel, mask, active, float(ts[0])
+                        _p(active), _p(am))
+    return sel, mask, active, float(am[0])
 
 
 def rac_residual(x, codes, scales, s_t, mask):
-    """-> (res_codes, res_scales, s_tr computed from max|r|, r float32)."""
+    """-> (res_codes, res_scales, s_tr (the residual's tensor scale, = s_t),
+    r float32)."""
     x = _c(x, np.float32)
     rows, K = x.shape
     rc = np.zeros((rows, K // 2), np.uint8)
@@ -396,8 +397,8 @@ def quantize_rac(x, n_select, amax=None):
     """Quantize + RAC for one GEMM input; returns a dict of every stage."""
     codes, scales, s_t = quantize(x, amax)
     score, chmax = channel_stats(x, codes, scales, s_t)
-    sel, mask, active, s_tr = rac_select(score, chmax, n_select)
-    rc, rs, s_tr_direct, r = rac_residual(x, codes, scales, s_t, mask)
+    sel, mask, active, amax_r = rac_select(score, chmax, n_select)
+    rc, rs, s_tr, r = rac_residual(x, codes, scales, s_t, mask)
     return dict(codes=codes, scales=scales, s_t=s_t, score=score, chmax=chmax,
-                selected=sel, mask=mask, active=active, s_tr=s_tr,
-                s_tr_direct=s_tr_direct, res_codes=rc, res_scales=rs, r=r)
+                selected=sel, mask=mask, active=active, s_tr=s_tr, amax_r=amax_r,
+                res_codes=rc, res_scales=rs, r=r)

@@ -85,16 +85,17 @@ def test_select_crafted_scores(orc, K, n_sel, kind):
         score = np.zeros(K, np.int64)
     else:
         score = np.full(K, 123456789, np.int64)
-    chmax = host(qo.channel_max)
     qo2 = L.QuantOut(qo.q, torch.from_numpy(score).to(DEV), qo.channel_max)
     rac = L.rac_select_residual(xd, qo2, n_sel)
-    sel, mask, active, s_tr = orc.rac_select(score, chmax, n_sel)
+    # the oracle's own quantization and channel maxima, the crafted scores
+    c, sc, t = orc.quantize(x)
+    _, chmax = orc.channel_stats(x, c, sc, t)
+    sel, mask, active, _ = orc.rac_select(score, chmax, n_sel)
     eq(host(rac.selected), sel, "selected")
     eq(host(rac.kblock_active), active, "kblock_active")
+    rc, rs, s_tr, _ = orc.rac_residual(x, c, sc, t, mask)
+    assert np.float32(s_tr) == np.float32(t)
     eq(host(rac.r.tscale)[0], np.float32(s_tr), "residual tensor scale")
-    rc, rs, s_tr_r, _ = orc.rac_residual(x, host(qo.q.codes), host(qo.q.scales),
-                                         float(host(qo.q.tscale)[0]), mask)
-    assert np.float32(s_tr_r) == np.float32(s_tr)
     eq(host(rac.r.scales), rs, "residual scales")
     eq(host(rac.r.codes), rc, "residual codes")
 

@@ -150,18 +150,21 @@ def test_grouped_select_crafted_scores(orc, K, n_sel):
     score[2] = 0
     score[3] = 123456789
     score[4] = rng.integers(0, 2 ** 40, K)
-    chmax = host(qo.channel_max)
     qo2 = L.QuantOut(qo.q, _t(score), qo.channel_max)
     rac = L.rac_select_residual_grouped(xd, qo2, od, total, n_sel)
     sel_g, act_g = host(rac.selected), host(rac.kblock_active)
     s_tr_g = host(rac.r.tscale)
-    codes, scales, s_t = host(qo.q.codes), host(qo.q.scales), host(qo.q.tscale)
+    # the oracle's own per-group quantization and channel maxima
+    q = orc.quantize_rac_grouped(x, off, None, None)
+    codes, scales, s_t = q["codes"], q["scales"], q["s_t"]
     for g in range(G):
-        sel, mask, active, s_tr = orc.rac_select(score[g], chmax[g], n_sel)
+        j0, j1 = off[g], off[g + 1]
+        _, chmax = orc.channel_stats(x[j0:j1], codes[j0:j1], scales[j0:j1], float(s_t[g]))
+        sel, mask, active, _ = orc.rac_select(score[g], chmax, n_sel)
         eq(sel_g[g], sel, f"selected group {g}")
         eq(act_g[g], active, f"kblock_active group {g}")
+        rc, rs, s_tr, _ = orc.rac_residual(x[j0:j1], codes[j0:j1], scales[j0:j1], float(s_t[g]),
+                                           mask)
         eq(s_tr_g[g], np.float32(s_tr), f"residual tensor scale group {g}")
-        j0, j1 = off[g], off[g + 1]
-        rc, rs, _, _ = orc.rac_residual(x[j0:j1], codes[j0:j1], scales[j0:j1], float(s_t[g]), mask)
         eq(host(rac.r.codes)[j0:j1], rc, f"residual codes group {g}")
         eq(host(rac.r.scales)[j0:j1], rs, f"residual scales group {g}")

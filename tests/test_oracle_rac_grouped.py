@@ -36,7 +36,7 @@ def _brute_group(sub, n_sel):
     score, chmax = brute.channel_scores(e, s_t)
     sel = brute.select(score, n_sel)
     r = [[e[i][k] if k in sel else Fr(0) for k in range(len(sub[0]))] for i in range(len(sub))]
-    rc, rs, s_tr = brute.quantize(r)
+    rc, rs, s_tr = brute.quantize(r, s_t=s_t)        # the residual pass uses the group's s_t
     return dict(codes=codes, scales=scales, s_t=s_t, score=score, chmax=chmax, sel=sel,
                 res_codes=rc, res_scales=rs, s_tr=s_tr)
 
@@ -66,7 +66,7 @@ def test_groups_with_gather_vs_brute(orc):
         assert d["score"][g].tolist() == b["score"]
         assert [Fr(float(v)) for v in d["chmax"][g]] == b["chmax"]
         assert d["selected"][g].tolist() == b["sel"]
-        assert Fr(float(d["s_tr"][g])) == b["s_tr"]
+        assert Fr(float(d["s_tr"][g])) == b["s_tr"] == b["s_t"]
         assert _unpack(d["res_codes"][j0:j1]).tolist() == b["res_codes"]
         assert d["res_scales"][j0:j1].tolist() == b["res_scales"]
 
