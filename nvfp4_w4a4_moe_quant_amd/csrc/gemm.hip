@@ -114,17 +114,18 @@ __device__ uint8_t nv_zero_row[kMaxKChunks * CODE_ROW];
 // waves of (BM / WAVES_M) x (BN / WAVES_N), NSTAGE LDS stages of KC k.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int MINW, bool RAC, bool SILU,
           bool GATHER, bool RSKIP>
-__global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
-  static_assert(WAVES_M * WAVES_N == 4, "4 waves");
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void k_gemm(GemmParams p) {
+  constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(FM >= 1 && FM <= 2 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "tile");
   static_assert(!SILU || FN % 2 == 0, "SiLU pairs gate/up fragments");
   constexpr int AR = RAC ? 2 * BM : BM;  // A rows then R rows
   constexpr int ROWS = AR + BN;          // then W rows
-  static_assert(ROWS % 128 == 0, "whole wave-loads of codes and scales");
-  constexpr int NPI = ROWS * 4 / kThreads;  // 16-byte code pieces per thread per chunk
-  constexpr int NSI = ROWS * 2 / kThreads;  // 4-byte scale words per thread per chunk
+  static_assert((ROWS * 2) % NT == 0, "whole wave-loads of codes and scales");
+  constexpr int NPI = ROWS * 4 / NT;  // 16-byte code pieces per thread per chunk
+  constexpr int NSI = ROWS * 2 / NT;  // 4-byte scale words per thread per chunk
   constexpr int STAGE_CODES = ROWS * CODE_ROW;
   constexpr int STAGE = STAGE_CODES + ROWS * SCALE_ROW;
   static_assert(NSTAGE >= 2 && (NSTAGE - 2) * (NPI + NSI) <= 63, "vmcnt range");
@@ -178,14 +179,14 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
   const uint8_t* gscale[NSI];
 #pragma unroll
   for (int j = 0; j < NPI; ++j) {
-    const int slot = (j * 4 + wave) * 64 + lane;
+    const int slot = (j * NW + wave) * 64 + lane;
     const int row = slot >> 2;
     const uint32_t piece = (uint32_t)(slot & 3) ^ swz((uint32_t)row);
     gcode[j] = code_row_ptr(row) + piece * 16;
   }
 #pragma unroll
   for (int j = 0; j < NSI; ++j) {
-    const int slot = (j * 4 + wave) * 64 + lane;
+    const int slot = (j * NW + wave) * 64 + lane;
     gscale[j] = scale_row_ptr(slot >> 1) + (slot & 1) * 4;
   }
   // The DMA is issued through inline asm: the compiler cannot tell that the
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
     const uint32_t st = (uint32_t)(uintptr_t)(lds_ptr_t)(lds + buf * STAGE);
 #pragma unroll
     for (int j = 0; j < NPI; ++j) {
-      const uint32_t m0 = __builtin_amdgcn_readfirstlane(st + (j * 4 + wave) * 1024);
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(st + (j * NW + wave) * 1024);
       const uint8_t* g = gcode[j] + (int64_t)chunk * CODE_ROW;
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                    :: "s"(m0), "v"(g) : "memory", "m0");
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < NSI; ++j) {
       const uint32_t m0 =
-          __builtin_amdgcn_readfirstlane(st + STAGE_CODES + (j * 4 + wave) * 256);
+          __builtin_amdgcn_readfirstlane(st + STAGE_CODES + (j * NW + wave) * 256);
       const uint8_t* g = gscale[j] + (int64_t)chunk * SCALE_ROW;
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
                    :: "s"(m0), "v"(g) : "memory", "m0");
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(kThreads, MINW) void k_gemm(GemmParams p) {
   const int nchunks = p.K / KC;
   // residual block activity, 8 blocks (one chunk) per 64-bit word
   if constexpr (RAC && RSKIP) {
-    for (int c = tid; c < nchunks; c += kThreads)
+    for (int c = tid; c < nchunks; c += NT)
       kact_lds[c] = p.kact ? *reinterpret_cast<const uint64_t*>(
                                  p.kact + (p.per_group ? (int64_t)grp * (p.K >> 4) : 0) +
                                  (int64_t)c * 8)
@@ -438,7 +439,7 @@ template <int BM, int BN, int WM, int WN, int NS, int MINW, bool RAC, bool SILU,
           bool RSKIP>
 int launch_t(GemmParams& p, hipStream_t s) {
   constexpr int rows = (RAC ? 2 * BM : BM) + BN;
-  static_assert(rows % 128 == 0, "whole wave-loads of codes and scales");
+  static_assert((rows * 2) % (64 * WM * WN) == 0, "whole wave-loads of codes and scales");
   {
     if (p.N % BN) return NVFP4_ERR_SHAPE;
     p.m_slots = (p.total_rows + BM - 1) / BM + p.G;
@@ -446,7 +447,7 @@ int launch_t(GemmParams& p, hipStream_t s) {
     const int64_t nb = (int64_t)p.m_slots * p.n_tiles;
     if (nb > 0x7fffffff) return NVFP4_ERR_SHAPE;
     hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, NS, MINW, RAC, SILU, GATHER, RSKIP>), dim3((unsigned)nb),
-                       dim3(kThreads), 0, s, p);
+                       dim3(64 * WM * WN), 0, s, p);
     return nv_launch_status();
   }
 }
@@ -602,9 +603,12 @@ int launch_gemv(GemmParams& p, hipStream_t s) {
 }
 
 // Tile configurations (rows x cols per workgroup, waves, LDS stages, min waves
-// per SIMD, residual step skipping).  N % 256 == 0: 128 x 256 tiles, 2 x 2
-// waves of 64 x 128 (two 32-row fragments per wave; a wave whose second
-// fragment is all padding skips it), two workgroups per CU.  Other N, and
+// per SIMD, residual step skipping).  Waves compute 64 x 128 (two 32-row
+// fragments; a wave whose second fragment is all padding skips it).  With
+// RAC and N % 512 == 0: 128 x 512 tiles of 2 x 4 waves, one workgroup (two
+// waves per SIMD) per CU -- each staged byte feeds a third more MFMAs than
+// in a 128 x 256 tile, which the copy into LDS dominates.  N % 256 == 0:
+// 128 x 256 tiles of 2 x 2 waves, two workgroups per CU.  Other N, and
 // residual block skipping: with RAC, 64 x 128 tiles (waves of 32 x 64); RAC
 // off, 128 x 128 (waves of 64 x 64), so that the staged rows fill whole
 // wave-loads.
@@ -613,6 +617,9 @@ int launch_cfg(GemmParams& p, hipStream_t s) {
   // block skipping needs registers for its activity mask: 64 x 128 tiles
   if constexpr (RAC) {
     if (p.skip) return launch_t<64, 128, 2, 2, 2, 2, RAC, SILU, GATHER, true>(p, s);
+  }
+  if constexpr (RAC) {
+    if (p.N % 512 == 0) return launch_t<128, 512, 2, 4, 2, 1, RAC, SILU, GATHER, false>(p, s);
   }
   if (p.N % 256 == 0) return launch_t<128, 256, 2, 2, 2, 2, RAC, SILU, GATHER, false>(p, s);
   if constexpr (RAC) {
