@@ -110,9 +110,10 @@ int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ld
  * their quantized residual).
  *
  * Inputs: the same x, scales, tensor_scale that nvfp4_quantize used and
- * wrote, and its channel_score / channel_max.  codes is not read and may be
- * NULL: the main codes are a function of x, scales and tensor_scale, and the
- * residual pass recomputes them, which costs less than reading them back.
+ * wrote, and its channel_score.  codes is not read and may be NULL: the main
+ * codes are a function of x, scales and tensor_scale, and the residual pass
+ * recomputes them, which costs less than reading them back.  channel_max is
+ * not read either (the selection ranks the scores) and may be NULL.
  * n_select (0 <= n_select <= K; K/2 in the workloads): the channels with the
  *          largest channel_score are selected, ties toward the lower channel
  *          index.

@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant(
 // holds channel 16b + l % 16 and counts over part 4w + l / 16 of the 64
 // parts of the j range, reading the scores from LDS tiles; the 64 partial
 // counts of a channel are summed in LDS.  The workgroup also writes the
-// block's mask, its activity flag and the max |e| over its selected channels.
+// block's mask and its activity flag.
 constexpr int kRankWaves = 16;
 constexpr int kRankParts = 4 * kRankWaves;  // j parts per channel
 constexpr int kRankTile = 4096;             // scores staged in LDS per pass (32 KiB)
@@ -341,17 +341,15 @@ constexpr int kSelThreads = 1024;
 constexpr int kMaxSelectK = 16384;
 
 __global__ __launch_bounds__(64 * kRankWaves) void k_rank(
-    const int64_t* __restrict__ score_in, const uint32_t* __restrict__ chmax, int K, int n_sel,
-    uint16_t* __restrict__ mask16, uint8_t* __restrict__ kact, uint32_t* __restrict__ part_max) {
+    const int64_t* __restrict__ score_in, int K, int n_sel, uint16_t* __restrict__ mask16,
+    uint8_t* __restrict__ kact) {
   __shared__ uint64_t tile[kRankTile];
   __shared__ uint32_t cnt[kRankParts][16];
   {  // group blockIdx.y (per-expert RAC): its statistics and outputs
     const int64_t g = blockIdx.y;
     score_in += g * K;
-    chmax += g * K;
     mask16 += g * (K >> 4);
     kact += g * (K >> 4);
-    part_max += g * (K >> 4);
   }
   const uint64_t* score = reinterpret_cast<const uint64_t*>(score_in);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -402,8 +400,6 @@ __global__ __launch_bounds__(64 * kRankWaves) void k_rank(
       mask16[blockIdx.x] = (uint16_t)bits;
       kact[blockIdx.x] = bits ? 1 : 0;
     }
-    const float a = nv_wave_max(sel ? __uint_as_float(chmax[k]) : 0.0f);
-    if (lane == 0) part_max[blockIdx.x] = __float_as_uint(a);
   }
 }
 
@@ -444,18 +440,16 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* t
 constexpr int kGroupSelectMaxK = 8192;  // scores staged in LDS (64 KiB)
 
 __global__ __launch_bounds__(kSelThreads) void k_select_group(
-    const int64_t* __restrict__ score_in, const uint32_t* __restrict__ chmax, int K, int n_sel,
-    uint16_t* __restrict__ mask16, uint8_t* __restrict__ kact, uint32_t* __restrict__ part_max) {
+    const int64_t* __restrict__ score_in, int K, int n_sel, uint16_t* __restrict__ mask16,
+    uint8_t* __restrict__ kact) {
   __shared__ uint64_t sc[kGroupSelectMaxK];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t wsum[kSelThreads / 64];
   __shared__ uint32_t res_digit, res_above;
   const int64_t g = blockIdx.x;
   const uint64_t* score = reinterpret_cast<const uint64_t*>(score_in + g * K);
-  chmax += g * K;
   mask16 += g * (K >> 4);
   kact += g * (K >> 4);
-  part_max += g * (K >> 4);
   const int tid = threadIdx.x, lane = tid & 63;
   for (int i = tid; i < K; i += kSelThreads) sc[i] = score[i];
 
@@ -520,9 +514,6 @@ __global__ __launch_bounds__(kSelThreads) void k_select_group(
   uint32_t total;
   const uint32_t before = block_exclusive_scan<kSelThreads>((uint32_t)__builtin_popcount(eqbits), wsum, &total);
   if (tid < nb) {
-    uint32_t cm[16];  // all 16 loads issued before the first use
-#pragma unroll
-    for (int i = 0; i < 16; ++i) cm[i] = chmax[tid * 16 + i];
     uint32_t bits = gtbits, rank = before;
     for (uint32_t m = eqbits; m; m &= m - 1) {
       if (rank < remaining) bits |= m & (~m + 1u);
@@ -530,11 +521,6 @@ __global__ __launch_bounds__(kSelThreads) void k_select_group(
     }
     mask16[tid] = (uint16_t)bits;
     kact[tid] = bits ? 1 : 0;
-    float a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if ((bits >> i) & 1u) a = __builtin_fmaxf(a, __uint_as_float(cm[i]));
-    part_max[tid] = __float_as_uint(a);
   }
 }
 
@@ -551,7 +537,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_group(
 __global__ __launch_bounds__(kThreads) void k_residual(
     const void* __restrict__ x, int bf16, int64_t rows, int64_t K, int64_t ldx,
     const uint8_t* __restrict__ scales, const float* __restrict__ tscale,
-    const uint16_t* __restrict__ mask16, const uint32_t* __restrict__ part_max, int nparts,
+    const uint16_t* __restrict__ mask16, int nparts,
     int32_t* __restrict__ selected,
     float* __restrict__ res_ts, uint8_t* __restrict__ res_codes,
     uint8_t* __restrict__ res_scales, const int32_t* __restrict__ goff,
@@ -566,13 +552,11 @@ __global__ __launch_bounds__(kThreads) void k_residual(
     row0 = goff[g];
     rows = goff[g + 1] - row0;
     mask16 += (int64_t)g * nparts;
-    part_max += (int64_t)g * nparts;
     tscale += g;
     res_ts += g;
     if (selected) selected += (int64_t)g * n_sel;
   }
   __shared__ uint16_t lmask[kMaxSelectK / 16];  // block masks, so x loads wait on nothing
-  (void)part_max;
   for (int i = threadIdx.x; i < nparts; i += kThreads) lmask[i] = mask16[i];  // K / 16 blocks
   __syncthreads();
   const float s_tr = *tscale;  // the residual pass shares the activation's tensor scale
@@ -830,21 +814,33 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* t
   return nv_launch_status();
 }
 
-// Workspace of rac_select_residual: block masks [K/16] u16, then the
-// per-block max |e| of the selected channels [K/16] u32.
-struct RacWs {
-  size_t mask_off, max_off, total;
-};
-static RacWs rac_ws_layout(int64_t K) {
-  RacWs w;
-  const size_t k = (size_t)(K > 0 ? K : 0);
-  w.mask_off = 0;
-  w.max_off = nv_round256(sizeof(uint16_t) * (k / 16));
-  w.total = w.max_off + nv_round256(sizeof(uint32_t) * (k / 16));
-  return w;
+// The RAC launches of one tensor (after validation): the rank count writes the
+// block masks into mask16 [K/16] and kblock_active; the residual pass writes
+// the residual, its tensor scale and the selected list.
+static int rac_launch(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx,
+                      const uint8_t* scales, const float* tensor_scale,
+                      const int64_t* channel_score, int64_t n_select, int32_t* selected,
+                      uint8_t* kblock_active, uint8_t* res_codes, uint8_t* res_scales,
+                      float* res_tensor_scale, uint16_t* mask16, hipStream_t s) {
+  const int nrank = (int)(K / 16);
+  hipLaunchKernelGGL(k_rank, dim3(nrank), dim3(64 * kRankWaves), 0, s, channel_score, (int)K,
+                     (int)n_select, mask16, kblock_active);
+  int st = nv_launch_status();
+  if (st) return st;
+  // at least one workgroup: it also writes selected[] and the tensor scale
+  const int64_t nblk = rows * (K / 16);
+  hipLaunchKernelGGL(k_residual, dim3((unsigned)blocks_for(nblk, 2 * kThreads, 2048)), dim3(kThreads),
+                     0, s, x, dtype == NVFP4_IN_BF16, rows, K, ldx, scales, tensor_scale, mask16,
+                     nrank, selected, res_tensor_scale, res_codes, res_scales, nullptr, nullptr, 0);
+  return nv_launch_status();
 }
 
-size_t rac_select_residual_workspace_size(int64_t, int64_t K) { return rac_ws_layout(K).total; }
+// Workspace of rac_select_residual: the selection's block masks [K/16] u16.
+static size_t rac_ws_bytes(int64_t K) {
+  return nv_round256(sizeof(uint16_t) * (size_t)(K > 0 ? K / 16 : 0));
+}
+
+size_t rac_select_residual_workspace_size(int64_t, int64_t K) { return rac_ws_bytes(K); }
 
 int rac_select_residual(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx,
                         const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
@@ -855,36 +851,20 @@ int rac_select_residual(const void* x, int dtype, int64_t rows, int64_t K, int64
   int st = check_x(x, dtype, rows, K, ldx);
   if (st) return st;
   (void)codes;  // recomputed from x, scales and tensor_scale
-  NV_RETURN_IF(!tensor_scale || !channel_score || !channel_max || !kblock_active ||
-                   !res_tensor_scale,
+  (void)channel_max;  // the selection needs the scores only
+  NV_RETURN_IF(!tensor_scale || !channel_score || !kblock_active || !res_tensor_scale,
                NVFP4_ERR_NULL);
   NV_RETURN_IF(rows > 0 && (!scales || !res_codes || !res_scales), NVFP4_ERR_NULL);
   NV_RETURN_IF(n_select < 0 || n_select > K || K > kMaxSelectK, NVFP4_ERR_SHAPE);
   NV_RETURN_IF(n_select > 0 && !selected, NVFP4_ERR_NULL);
-  NV_RETURN_IF(!nv_aligned16(res_codes) || (reinterpret_cast<uintptr_t>(channel_score) & 7) ||
-                   (reinterpret_cast<uintptr_t>(channel_max) & 3),
+  NV_RETURN_IF(!nv_aligned16(res_codes) || (reinterpret_cast<uintptr_t>(channel_score) & 7),
                NVFP4_ERR_ALIGN);
   NV_RETURN_IF(!ws || ws_bytes < rac_select_residual_workspace_size(rows, K) ||
                    (reinterpret_cast<uintptr_t>(ws) & 3),
                NVFP4_ERR_WORKSPACE);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const RacWs L = rac_ws_layout(K);
-  unsigned char* base = reinterpret_cast<unsigned char*>(ws);
-  uint16_t* mask16 = reinterpret_cast<uint16_t*>(base + L.mask_off);
-  uint32_t* part_max = reinterpret_cast<uint32_t*>(base + L.max_off);
-  const int nrank = (int)(K / 16);
-  hipLaunchKernelGGL(k_rank, dim3(nrank), dim3(64 * kRankWaves), 0, s, channel_score,
-                     reinterpret_cast<const uint32_t*>(channel_max), (int)K, (int)n_select,
-                     mask16, kblock_active, part_max);
-  st = nv_launch_status();
-  if (st) return st;
-  // at least one workgroup: it also writes selected[] and the tensor scale
-  const int64_t nblk = rows * (K / 16);
-  hipLaunchKernelGGL(k_residual, dim3((unsigned)blocks_for(nblk, 2 * kThreads, 2048)), dim3(kThreads),
-                     0, s, x, dtype == NVFP4_IN_BF16, rows, K, ldx, scales, tensor_scale, mask16,
-                     part_max, nrank, selected, res_tensor_scale, res_codes, res_scales, nullptr,
-                     nullptr, 0);
-  return nv_launch_status();
+  return rac_launch(x, dtype, rows, K, ldx, scales, tensor_scale, channel_score, n_select,
+                    selected, kblock_active, res_codes, res_scales, res_tensor_scale,
+                    reinterpret_cast<uint16_t*>(ws), reinterpret_cast<hipStream_t>(stream));
 }
 
 // ------------------------------------------------------- per-expert RAC
@@ -952,7 +932,7 @@ int nvfp4_quantize_grouped(const void* x, int dtype, int64_t K, int64_t ldx,
 }
 
 size_t rac_select_residual_grouped_workspace_size(int64_t G, int64_t K) {
-  return rac_ws_layout((G > 0 ? G : 0) * K).total;
+  return rac_ws_bytes((G > 0 ? G : 0) * K);
 }
 
 int rac_select_residual_grouped(const void* x, int dtype, int64_t K, int64_t ldx,
@@ -965,33 +945,27 @@ int rac_select_residual_grouped(const void* x, int dtype, int64_t K, int64_t ldx
                                 void* stream) {
   int st = check_grouped(x, dtype, K, ldx, group_offsets, G, total_rows);
   if (st) return st;
-  NV_RETURN_IF(!tensor_scales || !channel_score || !channel_max || !kblock_active ||
-                   !res_tensor_scales,
+  (void)channel_max;  // the selection needs the scores only
+  NV_RETURN_IF(!tensor_scales || !channel_score || !kblock_active || !res_tensor_scales,
                NVFP4_ERR_NULL);
   NV_RETURN_IF(total_rows > 0 && (!scales || !res_codes || !res_scales), NVFP4_ERR_NULL);
   NV_RETURN_IF(n_select < 0 || n_select > K || K > kMaxSelectK, NVFP4_ERR_SHAPE);
   NV_RETURN_IF(n_select > 0 && !selected, NVFP4_ERR_NULL);
-  NV_RETURN_IF(!nv_aligned16(res_codes) || (reinterpret_cast<uintptr_t>(channel_score) & 7) ||
-                   (reinterpret_cast<uintptr_t>(channel_max) & 3),
+  NV_RETURN_IF(!nv_aligned16(res_codes) || (reinterpret_cast<uintptr_t>(channel_score) & 7),
                NVFP4_ERR_ALIGN);
   NV_RETURN_IF(!ws || ws_bytes < rac_select_residual_grouped_workspace_size(G, K) ||
                    (reinterpret_cast<uintptr_t>(ws) & 3),
                NVFP4_ERR_WORKSPACE);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const RacWs L = rac_ws_layout(G * K);
-  unsigned char* base = reinterpret_cast<unsigned char*>(ws);
-  uint16_t* mask16 = reinterpret_cast<uint16_t*>(base + L.mask_off);
-  uint32_t* part_max = reinterpret_cast<uint32_t*>(base + L.max_off);
+  uint16_t* mask16 = reinterpret_cast<uint16_t*>(ws);
   const int nrank = (int)(K / 16);
   // many groups: a radix select per group; very long rows: the rank count
   if (K <= kGroupSelectMaxK)
     hipLaunchKernelGGL(k_select_group, dim3((unsigned)G), dim3(kSelThreads), 0, s, channel_score,
-                       reinterpret_cast<const uint32_t*>(channel_max), (int)K, (int)n_select,
-                       mask16, kblock_active, part_max);
+                       (int)K, (int)n_select, mask16, kblock_active);
   else
     hipLaunchKernelGGL(k_rank, dim3(nrank, (unsigned)G), dim3(64 * kRankWaves), 0, s,
-                       channel_score, reinterpret_cast<const uint32_t*>(channel_max), (int)K,
-                       (int)n_select, mask16, kblock_active, part_max);
+                       channel_score, (int)K, (int)n_select, mask16, kblock_active);
   st = nv_launch_status();
   if (st) return st;
   // at least one workgroup per group: it writes the group's selected[] and
@@ -999,7 +973,7 @@ int rac_select_residual_grouped(const void* x, int dtype, int64_t K, int64_t ldx
   const int64_t per_group = ((total_rows + G - 1) / G) * (K / 16);
   hipLaunchKernelGGL(k_residual, dim3((unsigned)blocks_for(per_group, 2 * kThreads, 256), (unsigned)G),
                      dim3(kThreads), 0, s, x, dtype == NVFP4_IN_BF16, total_rows, K, ldx, scales,
-                     tensor_scales, mask16, part_max, nrank, selected, res_tensor_scales,
+                     tensor_scales, mask16, nrank, selected, res_tensor_scales,
                      res_codes, res_scales, group_offsets, gather_rows, (int)n_select);
   return nv_launch_status();
 }
