@@ -140,6 +140,28 @@ int rac_select_residual(const void* x, int dtype, int64_t rows, int64_t K, int64
                         void* stream);
 
 /* ------------------------------------------------------------------------
+ * nvfp4_quantize_rac_static -- nvfp4_quantize (with statistics) followed by
+ * rac_select_residual, in one call that allocates nothing and takes no
+ * workspace: for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Arguments and
+ * results are those of the two calls (channel_score and channel_max are
+ * required).  Scratch (6 KiB: amax partials and block masks) lives in a
+ * device array of the library, one per GPU, held until the process ends; its
+ * address is looked up on the first call on each device (which must be the
+ * current device, the stream's device).  Every call on a GPU shares that
+ * GPU's array: calls that overlap on one GPU race (serialize them on one
+ * stream).  Nothing in it needs to start at zero.  Limit: K <= 16384
+ * (NVFP4_ERR_SHAPE beyond); otherwise the rules of nvfp4_quantize and
+ * rac_select_residual.  NVFP4_ERR_HIP if the array's address cannot be found.
+ * ------------------------------------------------------------------------ */
+int nvfp4_quantize_rac_static(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx,
+                              const float* amax_in, uint8_t* codes, uint8_t* scales,
+                              float* tensor_scale, int64_t* channel_score, float* channel_max,
+                              int64_t n_select, int32_t* selected, uint8_t* kblock_active,
+                              uint8_t* res_codes, uint8_t* res_scales, float* res_tensor_scale,
+                              void* stream);
+
+/* ------------------------------------------------------------------------
  * moe_route -- top-k routing of T tokens over E experts and the gather map
  * for the grouped GEMM (the MoE layer of the rollout model; the pages give no
  * routing details, so this is the plain reading).

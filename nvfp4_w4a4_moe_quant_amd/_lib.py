@@ -78,6 +78,8 @@ _SIGS = {
     "fp8_quantize_rows": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _P, _P, _P]),
     "fp8_grouped_gemm": (ctypes.c_int, [ctypes.POINTER(Fp8GemmArgs), _P]),
     "nvfp4_check_groups": (ctypes.c_int, [_P, _I64, _I64, _P, _I64]),
+    "nvfp4_quantize_rac_static": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, _P,
+                                                 _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -197,6 +199,32 @@ def rac_select_residual(x: torch.Tensor, qo: QuantOut, n_select: int) -> RacOut:
                                  _ptr(rc), _ptr(rs), _ptr(rts), _ptr(ws), ws.numel(),
                                  _stream(dev)))
     return RacOut(NVFP4(rc, rs, rts), sel, kact)
+
+
+def nvfp4_quantize_rac_static(x: torch.Tensor, n_select: int, *,
+                              amax_in: Optional[torch.Tensor] = None):
+    """nvfp4_quantize (with statistics) + rac_select_residual in one call that
+    takes no workspace (the library's per-device scratch).  Returns
+    (QuantOut, RacOut)."""
+    assert x.dim() == 2 and x.stride(1) == 1
+    rows, K = x.shape
+    dev = x.device
+    codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((rows, K // 16), dtype=torch.uint8, device=dev)
+    ts = torch.empty(1, dtype=torch.float32, device=dev)
+    score = torch.empty(K, dtype=torch.int64, device=dev)
+    chmax = torch.empty(K, dtype=torch.float32, device=dev)
+    sel = torch.empty(max(n_select, 1), dtype=torch.int32, device=dev)[:n_select]
+    kact = torch.empty(K // 16, dtype=torch.uint8, device=dev)
+    rc = torch.empty((rows, K // 2), dtype=torch.uint8, device=dev)
+    rs = torch.empty((rows, K // 16), dtype=torch.uint8, device=dev)
+    rts = torch.empty(1, dtype=torch.float32, device=dev)
+    _check(lib().nvfp4_quantize_rac_static(
+        _ptr(x), _dtype_code(x), rows, K, x.stride(0), _ptr(amax_in), _ptr(codes), _ptr(scales),
+        _ptr(ts), _ptr(score), _ptr(chmax), n_select, _ptr(sel), _ptr(kact), _ptr(rc), _ptr(rs),
+        _ptr(rts), _stream(dev)))
+    return (QuantOut(NVFP4(codes, scales, ts), score, chmax),
+            RacOut(NVFP4(rc, rs, rts), sel, kact))
 
 
 def nvfp4_quantize_grouped(x: torch.Tensor, group_offsets: torch.Tensor, total_rows: int, *,

@@ -17,6 +17,8 @@
 //               activation's tensor scale; the ascending selected indices
 // All reductions are max or integer sums, so results are order-independent.
 
+#include <mutex>
+
 #include "common.h"
 
 namespace {
@@ -865,6 +867,62 @@ int rac_select_residual(const void* x, int dtype, int64_t rows, int64_t K, int64
   return rac_launch(x, dtype, rows, K, ldx, scales, tensor_scale, channel_score, n_select,
                     selected, kblock_active, res_codes, res_scales, res_tensor_scale,
                     reinterpret_cast<uint16_t*>(ws), reinterpret_cast<hipStream_t>(stream));
+}
+
+// --------------------------------------------- allocation-free quantize + RAC
+// Scratch of nvfp4_quantize_rac_static on each device: the tensor-amax
+// partials (kMaxParts floats) at offset 0, then the selection's block masks
+// (kMaxSelectK / 16 u16).  Every byte is written by a kernel of the call before
+// any kernel of the call reads it, so nothing needs clearing between calls.
+constexpr size_t kStaticMaskOff = sizeof(float) * kMaxParts;             // 4096, 256-aligned
+constexpr size_t kScratchBytes = kStaticMaskOff + sizeof(uint16_t) * (kMaxSelectK / 16);
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static void* g_scratch[kMaxDevices];
+static std::once_flag g_scratch_once[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up once per
+// device with that device current (the array's name is a host-side handle,
+// not a device address).
+static int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return NVFP4_ERR_HIP;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess) g_scratch[dev] = ptr;
+  });
+  if (!g_scratch[dev]) return NVFP4_ERR_HIP;
+  *out = g_scratch[dev];
+  return NVFP4_OK;
+}
+
+extern "C" int nvfp4_quantize_rac_static(
+    const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx, const float* amax_in,
+    uint8_t* codes, uint8_t* scales, float* tensor_scale, int64_t* channel_score,
+    float* channel_max, int64_t n_select, int32_t* selected, uint8_t* kblock_active,
+    uint8_t* res_codes, uint8_t* res_scales, float* res_tensor_scale, void* stream) {
+  int st = check_x(x, dtype, rows, K, ldx);
+  if (st) return st;
+  NV_RETURN_IF(K > kMaxSelectK || n_select < 0 || n_select > K, NVFP4_ERR_SHAPE);
+  NV_RETURN_IF(!tensor_scale || !channel_score || !channel_max || !kblock_active ||
+                   !res_tensor_scale || (n_select > 0 && !selected),
+               NVFP4_ERR_NULL);
+  NV_RETURN_IF(rows > 0 && (!codes || !scales || !res_codes || !res_scales), NVFP4_ERR_NULL);
+  NV_RETURN_IF(!nv_aligned16(codes) || !nv_aligned16(res_codes) ||
+                   (reinterpret_cast<uintptr_t>(channel_score) & 7) ||
+                   (reinterpret_cast<uintptr_t>(channel_max) & 3),
+               NVFP4_ERR_ALIGN);
+  void* base = nullptr;
+  st = scratch_on_current_device(&base);
+  if (st) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = quantize_launch(x, dtype, rows, K, ldx, amax_in, codes, scales, tensor_scale,
+                       channel_score, channel_max, base, 0, nullptr, s);
+  if (st) return st;
+  return rac_launch(x, dtype, rows, K, ldx, scales, tensor_scale, channel_score, n_select,
+                    selected, kblock_active, res_codes, res_scales, res_tensor_scale,
+                    reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(base) + kStaticMaskOff), s);
 }
 
 // ------------------------------------------------------- per-expert RAC

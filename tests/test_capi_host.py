@@ -87,6 +87,31 @@ def test_rac_validation(lib):
     assert call(wsb=64) == EWS
 
 
+def test_static_quant_rac_validation(lib):
+    """nvfp4_quantize_rac_static rejects bad arguments before touching the
+    device (no scratch lookup, nothing enqueued)."""
+    def call(**kw):
+        a = dict(x=FAKE, dtype=1, rows=4, K=32, ldx=32, amax=None, codes=FAKE, scales=FAKE,
+                 ts=FAKE, score=FAKE, chmax=FAKE, nsel=16, sel=FAKE, kact=FAKE, rc=FAKE, rs=FAKE,
+                 rts=FAKE)
+        a.update(kw)
+        return lib.nvfp4_quantize_rac_static(
+            a["x"], a["dtype"], a["rows"], a["K"], a["ldx"], a["amax"], a["codes"], a["scales"],
+            a["ts"], a["score"], a["chmax"], a["nsel"], a["sel"], a["kact"], a["rc"], a["rs"],
+            a["rts"], None)
+    assert call(K=16384 + 16, ldx=16384 + 16) == ESHAPE   # beyond the scratch's limit
+    assert call(nsel=33) == ESHAPE
+    assert call(chmax=None) == ENULL
+    assert call(score=None) == ENULL
+    assert call(sel=None) == ENULL
+    assert call(rc=None) == ENULL
+    assert call(x=None) == ENULL
+    assert call(dtype=9) == EDTYPE
+    assert call(K=24, ldx=32) == ESHAPE
+    assert call(codes=FAKE_MIS) == EALIGN
+    assert call(rc=FAKE_MIS) == EALIGN
+
+
 def test_route_validation(lib):
     def call(T=8, E=16, k=2, ws=FAKE, wsb=1 << 20, ids=FAKE):
         return lib.moe_route(FAKE, T, E, k, ids, None, FAKE, FAKE, FAKE, ws, wsb, None)
