@@ -25,11 +25,9 @@
 //    16-byte pieces are XOR-swizzled per row so that fragment reads hit
 //    distinct banks.
 //  * Measured on MI355X (MoE gate/up shape, 32768 x 1536 x 2048 grouped over
-//    128 experts): the kernel is bound by its global->LDS copies (about 1.8 GB
-//    per call for 128 x 128 tiles), not by the matrix cores: without the
-//    copies it takes a third of the time.  Larger tiles, deeper pipelines and
-//    issuing a chunk's last MFMAs after its barrier were measured and are
-//    not faster.
+//    128 experts): with 128 x 128 tiles the kernel was bound by its
+//    global->LDS copies (about 1.8 GB per call), not by the matrix cores;
+//    256 x 256 tiles of eight waves halve the copies per MFMA.
 
 #include "common.h"
 
@@ -169,20 +167,28 @@ struct F8Params {
   int m_slots, n_tiles;
 };
 
-constexpr int KB = 128;  // k (= bytes) per row per chunk
+constexpr int KB = 128;  // largest k (= bytes) per row per chunk; K % KB == 0
 
-// Position of logical 16-byte piece lp of a 128-byte row is lp ^ f8_swz(row):
-// the 8 (or 16) rows one ds_read_b128 phase touches land on distinct banks
-// whether a phase covers 8 lanes of a 32-bank or 16 lanes of a 64-bank LDS.
-__device__ __forceinline__ uint32_t f8_swz(uint32_t row) { return (row ^ (row >> 3)) & 7u; }
+// Position of logical 16-byte piece lp of a row of PPR pieces is
+// lp ^ f8_swz<PPR>(row): the rows one ds_read_b128 phase touches land on
+// distinct banks.  128-byte rows (8 pieces): 8 rows of a 32-bank or 16 of a
+// 64-bank LDS phase; 64-byte rows (4 pieces): 16 rows of a 64-bank phase
+// (row % 4 picks the bank quarter, the swizzle spreads row / 4 over it).
+template <int PPR>
+__device__ __forceinline__ uint32_t f8_swz(uint32_t row) {
+  return PPR == 8 ? ((row ^ (row >> 3)) & 7u) : ((row >> 2) & 3u);
+}
 
 // silu(g) * u in FP32 with the hardware exp and reciprocal.
 __device__ __forceinline__ float f8_silu_mul(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int MINW, bool SILU, bool GATHER>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int MINW, bool SILU, bool GATHER,
+          int KC = KB>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void k_fp8_gemm(F8Params p) {
+  static_assert(KC == 64 || KC == 128, "64- or 128-byte chunks");
+  constexpr int PPR = KC / 16;  // 16-byte pieces per row per chunk
   constexpr int NW = WAVES_M * WAVES_N;  // waves per workgroup
   constexpr int NT = 64 * NW;
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
@@ -191,10 +197,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void k_fp8_gemm(F8Par
   static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "tile");
   static_assert(!SILU || FN % 2 == 0, "SiLU pairs gate/up fragments");
   constexpr int ROWS = BM + BN;  // A rows, then W rows
-  constexpr int PIECES = ROWS * (KB / 16);
+  constexpr int PIECES = ROWS * PPR;
   static_assert(PIECES % NT == 0, "whole wave-loads");
   constexpr int NPI = PIECES / NT;  // 16-byte pieces per thread per chunk
-  constexpr int STAGE = ROWS * KB;
+  constexpr int STAGE = ROWS * KC;
   static_assert(NSTAGE >= 2 && (NSTAGE - 2) * NPI <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * STAGE];
   __shared__ float sc_lds[ROWS];
@@ -235,8 +241,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void k_fp8_gemm(F8Par
 #pragma unroll
   for (int j = 0; j < NPI; ++j) {
     const int slot = (j * NW + wave) * 64 + lane;
-    const int row = slot >> 3;
-    const uint32_t piece = (uint32_t)(slot & 7) ^ f8_swz((uint32_t)row);
+    const int row = slot / PPR;
+    const uint32_t piece = (uint32_t)(slot % PPR) ^ f8_swz<PPR>((uint32_t)row);
     const uint8_t* base = row < BM ? p.a_codes + src_row(row) * K : p.w_codes + w_row(row - BM) * K;
     gsrc[j] = base + piece * 16;
   }
@@ -245,7 +251,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void k_fp8_gemm(F8Par
 #pragma unroll
     for (int j = 0; j < NPI; ++j) {
       const uint32_t m0 = __builtin_amdgcn_readfirstlane(st + (j * NW + wave) * 1024);
-      const uint8_t* g = gsrc[j] + (int64_t)chunk * KB;
+      const uint8_t* g = gsrc[j] + (int64_t)chunk * KC;
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                    :: "s"(m0), "v"(g) : "memory", "m0");
     }
@@ -262,15 +268,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void k_fp8_gemm(F8Par
   const bool wave_live = row_beg + wm * WTM < row_end;  // wave-uniform
   // 32 contiguous k of row i starting at logical piece lp (two pieces)
   auto frag = [&](const uint8_t* base, uint32_t i, uint32_t lp) -> int8v {
-    const uint8_t* rp = base + i * KB;
-    const uint4 x = *reinterpret_cast<const uint4*>(rp + ((lp ^ f8_swz(i)) << 4));
-    const uint4 y = *reinterpret_cast<const uint4*>(rp + (((lp + 1) ^ f8_swz(i)) << 4));
+    const uint8_t* rp = base + i * KC;
+    const uint4 x = *reinterpret_cast<const uint4*>(rp + ((lp ^ f8_swz<PPR>(i)) << 4));
+    const uint4 y = *reinterpret_cast<const uint4*>(rp + (((lp + 1) ^ f8_swz<PPR>(i)) << 4));
     int8v v;
     v[0] = (int)x.x; v[1] = (int)x.y; v[2] = (int)x.z; v[3] = (int)x.w;
     v[4] = (int)y.x; v[5] = (int)y.y; v[6] = (int)y.z; v[7] = (int)y.w;
     return v;
   };
-  constexpr int STEPS = KB / 64;
+  constexpr int STEPS = KC / 64;
   // operands of one 64-k step; lanes 32-63 take the upper 32 k of the step
   auto load_step = [&](const uint8_t* base, int s, int8v* av, int8v* wv) {
     const uint32_t lp = 4 * s + 2 * lh;
@@ -288,7 +294,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void k_fp8_gemm(F8Par
                                                                     0, 0, 0, 127, 0, 127);
   };
 
-  const int nchunks = K / KB;
+  const int nchunks = K / KC;
 #pragma unroll
   for (int c = 0; c < NSTAGE - 1; ++c)
     if (c < nchunks) issue(c, c);
@@ -358,21 +364,25 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void k_fp8_gemm(F8Par
   }
 }
 
-template <int BM, int BN, int WM, int WN, int NS, int MINW, bool SILU, bool GATHER>
+template <int BM, int BN, int WM, int WN, int NS, int MINW, bool SILU, bool GATHER, int KC = KB>
 int launch_f8(F8Params& p, hipStream_t s) {
   if (p.N % BN) return NVFP4_ERR_SHAPE;
   p.m_slots = (p.total_rows + BM - 1) / BM + p.G;
   p.n_tiles = p.N / BN;
   const int64_t nb = (int64_t)p.m_slots * p.n_tiles;
   if (nb > 0x7fffffff) return NVFP4_ERR_SHAPE;
-  hipLaunchKernelGGL((k_fp8_gemm<BM, BN, WM, WN, NS, MINW, SILU, GATHER>), dim3((unsigned)nb),
+  hipLaunchKernelGGL((k_fp8_gemm<BM, BN, WM, WN, NS, MINW, SILU, GATHER, KC>), dim3((unsigned)nb),
                      dim3(64 * WM * WN), 0, s, p);
   return nv_launch_status();
 }
 
-// 128 x 128 tiles (waves of 64 x 64), two stages, two workgroups per CU.
+// N % 256 == 0: 256 x 256 tiles of eight 64 x 128 waves, two stages, one
+// workgroup per CU (twice the MFMAs per staged byte and per LDS fragment read
+// of 128 x 128 tiles with 64 x 64 waves, which were bound by the copies into
+// LDS).  Other N: 128 x 128 tiles (waves of 64 x 64), two workgroups per CU.
 template <bool SILU, bool GATHER>
 int launch_f8_cfg(F8Params& p, hipStream_t s) {
+  if (p.N % 256 == 0) return launch_f8<256, 256, 4, 2, 2, 1, SILU, GATHER>(p, s);
   return launch_f8<128, 128, 2, 2, 2, 2, SILU, GATHER>(p, s);
 }
 
