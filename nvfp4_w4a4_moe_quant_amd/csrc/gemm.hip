@@ -453,152 +453,182 @@ int launch_t(GemmParams& p, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode-shaped GEMM: one group and few rows (a 16 x 4096 x 4096 linear layer
-// is the model case).  There the 64 x 128 prefill tiles would make only N/128
-// workgroups, and those few CUs would have to stream all of W.  Here a
-// workgroup owns 16 output columns and one 16-row tile over the whole of K:
-// N/16 workgroups stream W exactly once, and every lane issues all of its
-// loads for a pass before the first use, so each workgroup pays about one
-// memory latency.  v_mfma_f32_16x16x32_f16 matches the 16-row shape.  The
-// four waves split K and add their accumulators through LDS in a fixed
-// order.  A and R (a few KiB per row) are read by every workgroup from L2.
-//
-// k layout: a 128-k group is split into four 32-k quarters, one per 16-lane
-// quarter of the wave; the quarter's 32 contiguous k (16 code bytes, two
-// scale blocks) feed four MFMA steps of 8 k each.  The same permutation of k
-// is applied to A, R and W, so the contraction is unchanged.
+// Decode-shaped GEMM: one group and at most 64 rows (a 16 x 4096 x 4096
+// linear layer is the model case), K % 1024 == 0, K <= 16384.  A workgroup
+// owns 16 output columns (16 W rows) and one 16-row tile of A over the whole
+// of K, so N/16 workgroups stream W exactly once.
+//  * Every operand goes through LDS by coalesced DMA: each wave-instruction
+//    fetches 1 KiB of whole 128-byte lines (two rows' 512-byte chunk pieces).
+//    Fetching the MFMA fragments straight from global memory would make every
+//    load instruction touch 16 rows, and the A and R rows that every
+//    workgroup re-reads from L2 then cost more than streaming W.
+//  * K is consumed in chunks of 1024 k (128 per wave) through a ring of four
+//    LDS chunk buffers; the block scales of the whole K are fetched first.
+//    Chunk c is computed as soon as its DMA has landed while up to three
+//    later chunks are in flight.
+//  * v_mfma_f32_16x16x32_f16 matches the 16-row shape.  Inside a 128-k group,
+//    lane quarter q takes k = 32q .. 32q + 31 (16 contiguous code bytes) for
+//    four MFMA steps of 8 k: a fixed permutation of k applied to A, R and W
+//    alike, so the contraction is unchanged.  The eight waves split each chunk
+//    and add their accumulators through LDS in wave order.
+//  * Code pieces (16 bytes) are XOR-swizzled by row within 16-piece groups,
+//    scale pieces likewise, so the fragment reads of 16 rows hit distinct
+//    banks.
+// Rows of the tile past total_rows read the zero row.  The workgroup is
+// bound by dequantization VALU (A, R and W each once per element: A and R
+// are dequantized again by every workgroup) rather than by HBM.
 typedef float float4v __attribute__((ext_vector_type(4)));
-constexpr int kGvGroups = 8;      // 128-k groups per wave per load pass
-constexpr int kGvMaxRows = 64;    // rows up to which the decode kernel is used
+constexpr int kGvMaxRows = 64;      // rows up to which the decode kernel is used
+constexpr int kGvWaves = 8;
+constexpr int kGvKC = 128 * kGvWaves;  // k per chunk
+constexpr int kGvCRow = kGvKC / 2;     // code bytes per row per chunk
+constexpr int kGvBufs = 4;             // chunk buffers
+constexpr int kGvMaxK = 16384;
 
-// WAVES waves split K (K % (128 * WAVES) == 0).  The only device values the
-// loads wait for are the gather indices; the group spans rows [0, total_rows)
-// (offsets[0] == 0, offsets[1] == total_rows).
-template <int WAVES, int GRP, bool RAC, bool GATHER>
-__global__ __launch_bounds__(64 * WAVES) void k_gemv16(GemmParams p) {
-  constexpr int NCG = 1;  // 16-column groups per workgroup (2 measured slower)
-  __shared__ float4v red[WAVES][NCG][64];
+template <bool RAC, bool GATHER>
+__global__ __launch_bounds__(64 * kGvWaves) void k_gemv16(GemmParams p) {
+  constexpr int ROWS = RAC ? 48 : 32;  // LDS rows: A 16 | R 16 (RAC) | W 16
+  constexpr int WROW = ROWS - 16;      // first W row
+  constexpr int CHUNK = ROWS * kGvCRow;
+  constexpr int NCI = CHUNK / 1024 / kGvWaves;  // code DMA instructions per wave per chunk
+  static_assert(CHUNK % (1024 * kGvWaves) == 0 && 3 * NCI <= 63, "DMA split, vmcnt range");
+  constexpr int SCODES = kGvBufs * CHUNK;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[SCODES + ROWS * (kGvMaxK / 16)];
+  __shared__ float4v red[kGvWaves][64];
+
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // K slice of this wave, rotated by the workgroup id so that the workgroups
-  // (which all read the same A and R rows) spread over different lines
-  const int w = (wave + (int)blockIdx.x) % WAVES;
+  const int K = p.K, K2 = K >> 1, K16 = K >> 4;
+  const int nch = K / kGvKC;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;  // first output column (W row)
+  const int m0 = (int)blockIdx.y * 16;          // first output row
+  auto act = [&](const uint8_t* base, int i, int per_row) -> const uint8_t* {
+    const int m = m0 + i;
+    if (m >= p.total_rows) return nv_zero_row;
+    return base + (GATHER ? (int64_t)p.gather[m] : (int64_t)m) * per_row;
+  };
+  auto code_row = [&](int r) -> const uint8_t* {
+    if (r < 16) return act(p.a_codes, r, K2);
+    if (RAC && r < 32) return act(p.r_codes, r - 16, K2);
+    return p.w_codes + (n0 + r - WROW) * K2;
+  };
+  auto scale_row = [&](int r) -> const uint8_t* {
+    if (r < 16) return act(p.a_scales, r, K16);
+    if (RAC && r < 32) return act(p.r_scales, r - 16, K16);
+    return p.w_scales + (n0 + r - WROW) * K16;
+  };
+  const uint32_t lbase = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
+
+  // block scales of the whole K: ROWS rows of K/16 bytes, in 16-byte pieces
+  // swizzled within groups of smask + 1 pieces
+  const int spr = K16 >> 4;  // pieces per scale row (a multiple of 4)
+  const int smask = (spr & 15) == 0 ? 15 : (spr & 7) == 0 ? 7 : 3;
+  const int nsi = ROWS * spr / 64;
+  for (int j = wave; j < nsi; j += kGvWaves) {
+    const int slot = j * 64 + lane, r = slot / spr, pc = (slot % spr) ^ (r & smask);
+    const uint8_t* g = scale_row(r) + pc * 16;
+    const uint32_t m0r = __builtin_amdgcn_readfirstlane(lbase + SCODES + j * 1024);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(m0r), "v"(g) : "memory", "m0");
+  }
+  // code pieces: slot -> (row, piece), 32 pieces per row per chunk
+  const uint8_t* gcode[NCI];
+#pragma unroll
+  for (int j = 0; j < NCI; ++j) {
+    const int slot = (j * kGvWaves + wave) * 64 + lane, r = slot >> 5;
+    gcode[j] = code_row(r) + (((slot & 31) ^ (r & 15)) << 4);
+  }
+  auto issue = [&](int ch) {
+    const uint32_t st = lbase + (ch % kGvBufs) * CHUNK;
+#pragma unroll
+    for (int j = 0; j < NCI; ++j) {
+      const uint32_t m0r = __builtin_amdgcn_readfirstlane(st + (j * kGvWaves + wave) * 1024);
+      const uint8_t* g = gcode[j] + (int64_t)ch * kGvCRow;
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                   :: "s"(m0r), "v"(g) : "memory", "m0");
+    }
+  };
+  for (int ch = 0; ch < kGvBufs && ch < nch; ++ch) issue(ch);
+
   const int c = lane & 15, q = lane >> 4;
-  const int K = p.K;
-  const int kw = K / WAVES;  // k per wave
-  const float s_ta = p.a_ts[0];  // one group
+  auto code16 = [&](const uint8_t* buf, int r, int kl) -> uint4 {
+    return *reinterpret_cast<const uint4*>(buf + r * kGvCRow + (((kl >> 5) ^ (r & 15)) << 4));
+  };
+  auto scale2 = [&](int r, int k) -> half2v {  // the two block scales of k .. k + 31
+    const int b = k >> 4, pc = (b >> 4) ^ (r & smask);
+    const uint32_t v =
+        *reinterpret_cast<const uint16_t*>(lds + SCODES + r * K16 + pc * 16 + (b & 15));
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, false);
+  };
+  float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};  // main and residual passes (one tensor scale)
+  for (int ch = 0; ch < nch; ++ch) {
+    // chunks issued after ch whose DMA may still be in flight
+    const int pend = nch - 1 - ch < kGvBufs - 1 ? nch - 1 - ch : kGvBufs - 1;
+    if (pend >= 3)
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(3 * NCI) : "memory");
+    else if (pend == 2)
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * NCI) : "memory");
+    else if (pend == 1)
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NCI) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const uint8_t* buf = lds + (ch % kGvBufs) * CHUNK;
+    const int kl = wave * 128 + q * 32;  // this lane's 32 k within the chunk
+    const int k = ch * kGvKC + kl;
+    const uint4 av = code16(buf, c, kl), wv = code16(buf, WROW + c, kl);
+    const half2v sa = scale2(c, k), sw = scale2(WROW + c, k);
+    uint4 rv = av;
+    half2v sr = sa;
+    if constexpr (RAC) {
+      rv = code16(buf, 16 + c, kl);
+      sr = scale2(16 + c, k);
+    }
+    const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, rw[4] = {rv.x, rv.y, rv.z, rv.w},
+                   ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int hi = st >> 1;  // steps 0-1: first block of the 32 k, 2-3: second
+      const half2v s_w = hi ? __builtin_shufflevector(sw, sw, 1, 1)
+                            : __builtin_shufflevector(sw, sw, 0, 0);
+      const half2v s_a = hi ? __builtin_shufflevector(sa, sa, 1, 1)
+                            : __builtin_shufflevector(sa, sa, 0, 0);
+      const half8 bw = dequant8(ww[st], s_w);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8(aw[st], s_a), bw, acc, 0, 0, 0);
+      if constexpr (RAC) {
+        const half2v s_r = hi ? __builtin_shufflevector(sr, sr, 1, 1)
+                              : __builtin_shufflevector(sr, sr, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8(rw[st], s_r), bw, acc, 0, 0, 0);
+      }
+    }
+    if (ch + kGvBufs < nch) {
+      __syncthreads();  // every wave is done with this buffer
+      issue(ch + kGvBufs);
+    }
+  }
+
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  float4v sm = red[0][lane];
+#pragma unroll
+  for (int i = 1; i < kGvWaves; ++i) sm += red[i][lane];
+  const float s_ta = p.a_ts[0];
   float scale = p.w_ts[0] * s_ta;
   if constexpr (RAC) {
     if (p.r_ts[0] != s_ta) scale = __builtin_nanf("");  // the residual shares s_ta
   }
-  const int m = (int)blockIdx.y * 16 + c;  // A row fed by this lane
-  const bool mv = m < p.total_rows;
-  // W rows fed by this lane: one per 16-column group of the workgroup
-  const int64_t n0 = (int64_t)blockIdx.x * 16 * NCG + c;
-  const uint8_t* wc = p.w_codes + n0 * (K >> 1);
-  const uint8_t* wsc = p.w_scales + n0 * (K >> 4);
-  const int64_t cgc = (int64_t)16 * (K >> 1), cgs = (int64_t)16 * (K >> 4);  // next group
-
-  float4v accm[NCG];  // main and residual passes (one tensor scale)
-#pragma unroll
-  for (int j = 0; j < NCG; ++j) accm[j] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-  const int64_t src = mv ? (GATHER ? (int64_t)p.gather[m] : (int64_t)m) : 0;
-  const uint8_t* ac = p.a_codes + src * (K >> 1);
-  const uint8_t* asc = p.a_scales + src * (K >> 4);
-  const uint8_t* rc = RAC ? p.r_codes + src * (K >> 1) : nullptr;
-  const uint8_t* rsc = RAC ? p.r_scales + src * (K >> 4) : nullptr;
-  for (int g0 = 0; g0 < kw; g0 += 128 * GRP) {
-    const int ng = (kw - g0) / 128 < GRP ? (kw - g0) / 128 : GRP;
-    uint4 wv[GRP][NCG], av[GRP], rv[GRP];
-    uint32_t wsv[GRP][NCG], asv[GRP], rsv[GRP];
-    // loads in group order (A, R, then the W rows), so that group g can be
-    // computed once its own loads have landed
-#pragma unroll
-    for (int g = 0; g < GRP; ++g) {
-      const int kb = w * kw + g0 + g * 128 + q * 32;
-      av[g] = rv[g] = make_uint4(0u, 0u, 0u, 0u);
-      asv[g] = rsv[g] = 0u;
-      if (g < ng && mv) {
-        av[g] = *reinterpret_cast<const uint4*>(ac + (kb >> 1));
-        asv[g] = *reinterpret_cast<const uint16_t*>(asc + (kb >> 4));
-        if constexpr (RAC) {
-          rv[g] = *reinterpret_cast<const uint4*>(rc + (kb >> 1));
-          rsv[g] = *reinterpret_cast<const uint16_t*>(rsc + (kb >> 4));
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < NCG; ++j) {
-        wv[g][j] = make_uint4(0u, 0u, 0u, 0u);
-        wsv[g][j] = 0u;
-        if (g < ng) {
-          wv[g][j] = *reinterpret_cast<const uint4*>(wc + j * cgc + (kb >> 1));
-          wsv[g][j] = *reinterpret_cast<const uint16_t*>(wsc + j * cgs + (kb >> 4));
-        }
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < GRP; ++g) {
-      if (g >= ng) break;
-      const half2v sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(asv[g], 1.0f, false);
-      half2v sr = sa;
-      if constexpr (RAC) sr = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rsv[g], 1.0f, false);
-      half2v sw[NCG];
-#pragma unroll
-      for (int j = 0; j < NCG; ++j)
-        sw[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wsv[g][j], 1.0f, false);
-      const uint32_t aword[4] = {av[g].x, av[g].y, av[g].z, av[g].w};
-      const uint32_t rword[4] = {rv[g].x, rv[g].y, rv[g].z, rv[g].w};
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const int hi = st >> 1;  // steps 0-1: first block, 2-3: second
-        const half2v s_a = hi ? __builtin_shufflevector(sa, sa, 1, 1)
-                              : __builtin_shufflevector(sa, sa, 0, 0);
-        const half8 ba = dequant8(aword[st], s_a);
-        half8 br;
-        if constexpr (RAC) {
-          const half2v s_r = hi ? __builtin_shufflevector(sr, sr, 1, 1)
-                                : __builtin_shufflevector(sr, sr, 0, 0);
-          br = dequant8(rword[st], s_r);
-        }
-#pragma unroll
-        for (int j = 0; j < NCG; ++j) {
-          const uint32_t ww = st == 0 ? wv[g][j].x : st == 1 ? wv[g][j].y
-                            : st == 2 ? wv[g][j].z : wv[g][j].w;
-          const half2v s_w = hi ? __builtin_shufflevector(sw[j], sw[j], 1, 1)
-                                : __builtin_shufflevector(sw[j], sw[j], 0, 0);
-          const half8 bw = dequant8(ww, s_w);
-          accm[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ba, bw, accm[j], 0, 0, 0);
-          if constexpr (RAC)
-            accm[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(br, bw, accm[j], 0, 0, 0);
-        }
-      }
-    }
-  }
-
-#pragma unroll
-  for (int j = 0; j < NCG; ++j) red[w][j][lane] = accm[j];
-  __syncthreads();
-  // wave j adds the K slices of column group j in slice order
-  if (wave >= NCG) return;
-  const int j = wave;
-  float4v sm = red[0][j][lane];
-#pragma unroll
-  for (int i = 1; i < WAVES; ++i) sm += red[i][j][lane];
   float* out = reinterpret_cast<float*>(p.out);
-  const int64_t n = n0 + 16 * j;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int row = (int)blockIdx.y * 16 + 4 * q + i;  // D row of element i
-    if (row < p.total_rows) out[(int64_t)row * p.N + n] = scale * sm[i];
+    const int row = m0 + 4 * q + i;  // D row of element i
+    if (row < p.total_rows) out[(int64_t)row * p.N + n0 + c] = scale * sm[i];
   }
 }
 
 template <bool RAC, bool GATHER>
 int launch_gemv(GemmParams& p, hipStream_t s) {
   const dim3 grid((unsigned)(p.N / 16), (unsigned)((p.total_rows + 15) / 16));
-  if (p.K % 1024 == 0)
-    hipLaunchKernelGGL((k_gemv16<8, kGvGroups, RAC, GATHER>), grid, dim3(512), 0, s, p);
-  else
-    hipLaunchKernelGGL((k_gemv16<4, kGvGroups, RAC, GATHER>), grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((k_gemv16<RAC, GATHER>), grid, dim3(64 * kGvWaves), 0, s, p);
   return nv_launch_status();
 }
 
@@ -705,7 +735,7 @@ int w4a4_grouped_gemm_rac(const w4a4_gemm_args_t* a, void*, size_t, void* stream
   p.skip = (a->flags & NVFP4_GEMM_SKIP_INACTIVE_BLOCKS) && a->kblock_active ? 1 : 0;
   p.per_group = (a->flags & NVFP4_GEMM_PER_GROUP_SCALES) ? 1 : 0;
   const bool rac = a->r_codes != nullptr, gather = a->gather_rows != nullptr;
-  if (p.G == 1 && p.total_rows <= kGvMaxRows && p.K % 512 == 0 &&
+  if (p.G == 1 && p.total_rows <= kGvMaxRows && p.K % kGvKC == 0 && p.K <= kGvMaxK &&
       a->epilogue == NVFP4_EPI_F32) {
     if (rac) return gather ? launch_gemv<true, true>(p, s) : launch_gemv<true, false>(p, s);
     return gather ? launch_gemv<false, true>(p, s) : launch_gemv<false, false>(p, s);

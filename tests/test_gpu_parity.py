@@ -222,11 +222,14 @@ def _nv(orc_triple):
 @pytest.mark.parametrize("rows,K,N,rac,gather", [
     (16, 4096, 256, True, False), (1, 512, 128, True, False), (5, 1536, 128, False, False),
     (33, 1024, 256, True, True), (64, 2048, 384, True, False), (17, 512, 128, False, True),
-    (65, 512, 128, True, False)])
+    (65, 512, 128, True, False), (16, 16384, 128, True, True), (3, 3072, 256, True, False),
+    (64, 1024, 128, False, True), (9, 7168, 384, True, False), (16, 8192, 256, False, False)])
 def test_decode_shaped_gemm(orc, rows, K, N, rac, gather):
-    """One group with few rows (the decode kernel below 65 rows when K % 512
-    == 0; 65 rows takes the prefill kernel), with and without RAC and a row
-    gather, against the oracle GEMM on oracle-quantized operands."""
+    """One group with few rows (the decode kernel below 65 rows when K % 1024
+    == 0 and K <= 16384: one to sixteen chunks of 1024 k, so the LDS chunk
+    ring wraps up to four times, and scale rows of 4 to 64 pieces; other
+    shapes take the prefill kernel), with and without RAC and a row gather,
+    against the oracle GEMM on oracle-quantized operands."""
     say(f"decode gemm {rows}x{K}x{N} rac={rac} gather={gather}")
     rng = np.random.default_rng(rows * 31 + K + N)
     src = rows + 3 if gather else rows
