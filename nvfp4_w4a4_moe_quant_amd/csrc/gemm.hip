@@ -453,183 +453,510 @@ int launch_t(GemmParams& p, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode-shaped GEMM: one group and at most 64 rows (a 16 x 4096 x 4096
-// linear layer is the model case), K % 1024 == 0, K <= 16384.  A workgroup
-// owns 16 output columns (16 W rows) and one 16-row tile of A over the whole
-// of K, so N/16 workgroups stream W exactly once.
+// Decode-shaped GEMM: few rows per group -- one group with at most 64 rows
+// (a 16 x 4096 x 4096 linear layer), or many groups averaging at most four
+// rows (the experts of a decode step) -- with K % 1024 == 0, K <= 16384.  A
+// workgroup owns one 16-column slab of W (with the SiLU*mul epilogue two:
+// gate columns j .. j+15 and the up columns I + j ..) over the whole of K, and
+// the 16-row tiles of one group: N/16 workgroups per group stream W once.
 //  * Every operand goes through LDS by coalesced DMA: each wave-instruction
-//    fetches 1 KiB of whole 128-byte lines (two rows' 512-byte chunk pieces).
-//    Fetching the MFMA fragments straight from global memory would make every
-//    load instruction touch 16 rows, and the A and R rows that every
+//    fetches 1 KiB of whole 128-byte lines (two rows' 512-byte pieces of a
+//    chunk).  Fetching MFMA fragments straight from global memory would make
+//    every load instruction touch 16 rows, and the A and R rows that every
 //    workgroup re-reads from L2 then cost more than streaming W.
-//  * K is consumed in chunks of 1024 k (128 per wave) through a ring of four
-//    LDS chunk buffers; the block scales of the whole K are fetched first.
-//    Chunk c is computed as soon as its DMA has landed while up to three
-//    later chunks are in flight.
-//  * v_mfma_f32_16x16x32_f16 matches the 16-row shape.  Inside a 128-k group,
+//  * K is consumed in chunks of 1024 k (128 per wave) through a ring of LDS
+//    chunk buffers; the block scales of the whole K land first.  Chunk c is
+//    computed as soon as its DMA has landed while later chunks are in flight.
+//  * v_mfma_f32_16x16x32_f16 matches the 16-row tile.  Inside a 128-k group,
 //    lane quarter q takes k = 32q .. 32q + 31 (16 contiguous code bytes) for
 //    four MFMA steps of 8 k: a fixed permutation of k applied to A, R and W
-//    alike, so the contraction is unchanged.  The eight waves split each chunk
-//    and add their accumulators through LDS in wave order.
+//    alike, so the contraction is unchanged.  The eight waves split each
+//    chunk and add their accumulators through LDS in wave order.
 //  * Code pieces (16 bytes) are XOR-swizzled by row within 16-piece groups,
 //    scale pieces likewise, so the fragment reads of 16 rows hit distinct
 //    banks.
-// Rows of the tile past total_rows read the zero row.  The workgroup is
-// bound by dequantization VALU (A, R and W each once per element: A and R
-// are dequantized again by every workgroup) rather than by HBM.
+// Rows of a tile past the group's end read the zero row.  The kernel is
+// bound by dequantization VALU (A, R and W each once per element; every
+// workgroup dequantizes its A and R rows again) and DMA latency, not MFMA.
 typedef float float4v __attribute__((ext_vector_type(4)));
-constexpr int kGvMaxRows = 64;      // rows up to which the decode kernel is used
+constexpr int kGvMaxRows = 64;      // one group: rows up to which this kernel is used
+constexpr int kGvAvgRows = 4;       // many groups: average rows per group
 constexpr int kGvWaves = 8;
 constexpr int kGvKC = 128 * kGvWaves;  // k per chunk
 constexpr int kGvCRow = kGvKC / 2;     // code bytes per row per chunk
-constexpr int kGvBufs = 4;             // chunk buffers
-constexpr int kGvMaxK = 16384;
+constexpr int kGvMaxK = 16384;      // 12288 with the SiLU*mul epilogue (two W slabs)
 
-template <bool RAC, bool GATHER>
-__global__ __launch_bounds__(64 * kGvWaves) void k_gemv16(GemmParams p) {
-  constexpr int ROWS = RAC ? 48 : 32;  // LDS rows: A 16 | R 16 (RAC) | W 16
-  constexpr int WROW = ROWS - 16;      // first W row
+template <bool RAC, bool SILU, bool GATHER>
+__global__ __launch_bounds__(64 * kGvWaves) void k_gemv(GemmParams p) {
+  constexpr int NS = SILU ? 2 : 1;           // 16-column W slabs per workgroup
+  constexpr int AROWS = RAC ? 32 : 16;       // A 16 | R 16
+  constexpr int ROWS = AROWS + 16 * NS;      // then the W slabs
   constexpr int CHUNK = ROWS * kGvCRow;
+  constexpr int NBUF = ROWS <= 48 ? 4 : 3;   // chunk buffers
   constexpr int NCI = CHUNK / 1024 / kGvWaves;  // code DMA instructions per wave per chunk
-  static_assert(CHUNK % (1024 * kGvWaves) == 0 && 3 * NCI <= 63, "DMA split, vmcnt range");
-  constexpr int SCODES = kGvBufs * CHUNK;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[SCODES + ROWS * (kGvMaxK / 16)];
-  __shared__ float4v red[kGvWaves][64];
+  static_assert(CHUNK % (1024 * kGvWaves) == 0 && (NBUF - 1) * NCI <= 63, "DMA, vmcnt");
+  constexpr int SCODES = NBUF * CHUNK;
+  constexpr int MAXK = SILU ? 12288 : kGvMaxK;
+  static_assert(kGvWaves * NS * 64 * 16 <= CHUNK, "reduction fits in a chunk buffer");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[SCODES + ROWS * (MAXK / 16)];
+  float4v* red = reinterpret_cast<float4v*>(lds);  // [wave][slab][lane], after the last chunk
+
+  const int grp = blockIdx.z;
+  const int row_beg = p.offsets[grp], row_end = p.offsets[grp + 1];
+  const int nrows = row_end - row_beg;
+  if ((int)blockIdx.y * 16 >= nrows) return;  // workgroup-uniform
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int K = p.K, K2 = K >> 1, K16 = K >> 4;
   const int nch = K / kGvKC;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;  // first output column (W row)
-  const int m0 = (int)blockIdx.y * 16;          // first output row
-  auto act = [&](const uint8_t* base, int i, int per_row) -> const uint8_t* {
-    const int m = m0 + i;
-    if (m >= p.total_rows) return nv_zero_row;
-    return base + (GATHER ? (int64_t)p.gather[m] : (int64_t)m) * per_row;
+  const int I = p.N >> 1;
+  const int j0 = (int)blockIdx.x * 16;  // first column of slab 0
+  auto w_row = [&](int i) -> int64_t {  // W row of LDS W row i (0 .. 16 NS - 1)
+    const int n = SILU ? ((i >> 4) ? I : 0) + j0 + (i & 15) : j0 + i;
+    return (int64_t)grp * p.N + n;
   };
-  auto code_row = [&](int r) -> const uint8_t* {
-    if (r < 16) return act(p.a_codes, r, K2);
-    if (RAC && r < 32) return act(p.r_codes, r - 16, K2);
-    return p.w_codes + (n0 + r - WROW) * K2;
-  };
-  auto scale_row = [&](int r) -> const uint8_t* {
-    if (r < 16) return act(p.a_scales, r, K16);
-    if (RAC && r < 32) return act(p.r_scales, r - 16, K16);
-    return p.w_scales + (n0 + r - WROW) * K16;
-  };
+  const float s_ta = p.a_ts[p.per_group ? grp : 0];
+  float scale = p.w_ts[grp] * s_ta;
+  if constexpr (RAC) {
+    if (p.r_ts[p.per_group ? grp : 0] != s_ta) scale = __builtin_nanf("");  // shares s_ta
+  }
   const uint32_t lbase = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
-
-  // block scales of the whole K: ROWS rows of K/16 bytes, in 16-byte pieces
-  // swizzled within groups of smask + 1 pieces
-  const int spr = K16 >> 4;  // pieces per scale row (a multiple of 4)
+  const int spr = K16 >> 4;  // 16-byte pieces per scale row (a multiple of 4)
   const int smask = (spr & 15) == 0 ? 15 : (spr & 7) == 0 ? 7 : 3;
-  const int nsi = ROWS * spr / 64;
-  for (int j = wave; j < nsi; j += kGvWaves) {
-    const int slot = j * 64 + lane, r = slot / spr, pc = (slot % spr) ^ (r & smask);
-    const uint8_t* g = scale_row(r) + pc * 16;
-    const uint32_t m0r = __builtin_amdgcn_readfirstlane(lbase + SCODES + j * 1024);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :: "s"(m0r), "v"(g) : "memory", "m0");
-  }
-  // code pieces: slot -> (row, piece), 32 pieces per row per chunk
-  const uint8_t* gcode[NCI];
-#pragma unroll
-  for (int j = 0; j < NCI; ++j) {
-    const int slot = (j * kGvWaves + wave) * 64 + lane, r = slot >> 5;
-    gcode[j] = code_row(r) + (((slot & 31) ^ (r & 15)) << 4);
-  }
-  auto issue = [&](int ch) {
-    const uint32_t st = lbase + (ch % kGvBufs) * CHUNK;
-#pragma unroll
-    for (int j = 0; j < NCI; ++j) {
-      const uint32_t m0r = __builtin_amdgcn_readfirstlane(st + (j * kGvWaves + wave) * 1024);
-      const uint8_t* g = gcode[j] + (int64_t)ch * kGvCRow;
+  const int nsi = ROWS * spr / 64;  // scale DMA instructions (whole K)
+  const int c = lane & 15, q = lane >> 4;
+  float hmax = 0.0f;
+
+  for (int tile = blockIdx.y; tile * 16 < nrows; tile += gridDim.y) {
+    const int m0 = row_beg + tile * 16;
+    auto act = [&](const uint8_t* base, int i, int per_row) -> const uint8_t* {
+      const int m = m0 + i;
+      if (m >= row_end) return nv_zero_row;
+      return base + (GATHER ? (int64_t)p.gather[m] : (int64_t)m) * per_row;
+    };
+    auto code_row = [&](int r) -> const uint8_t* {
+      if (r < 16) return act(p.a_codes, r, K2);
+      if (RAC && r < 32) return act(p.r_codes, r - 16, K2);
+      return p.w_codes + w_row(r - AROWS) * K2;
+    };
+    auto scale_row = [&](int r) -> const uint8_t* {
+      if (r < 16) return act(p.a_scales, r, K16);
+      if (RAC && r < 32) return act(p.r_scales, r - 16, K16);
+      return p.w_scales + w_row(r - AROWS) * K16;
+    };
+    __syncthreads();  // the previous tile's reduction has been read
+    // block scales of the whole K: ROWS rows of K/16 bytes in 16-byte pieces,
+    // swizzled within groups of smask + 1 pieces
+    for (int j = wave; j < nsi; j += kGvWaves) {
+      const int slot = j * 64 + lane, r = slot / spr, pc = (slot % spr) ^ (r & smask);
+      const uint8_t* g = scale_row(r) + pc * 16;
+      const uint32_t m0r = __builtin_amdgcn_readfirstlane(lbase + SCODES + j * 1024);
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                    :: "s"(m0r), "v"(g) : "memory", "m0");
     }
-  };
-  for (int ch = 0; ch < kGvBufs && ch < nch; ++ch) issue(ch);
-
-  const int c = lane & 15, q = lane >> 4;
-  auto code16 = [&](const uint8_t* buf, int r, int kl) -> uint4 {
-    return *reinterpret_cast<const uint4*>(buf + r * kGvCRow + (((kl >> 5) ^ (r & 15)) << 4));
-  };
-  auto scale2 = [&](int r, int k) -> half2v {  // the two block scales of k .. k + 31
-    const int b = k >> 4, pc = (b >> 4) ^ (r & smask);
-    const uint32_t v =
-        *reinterpret_cast<const uint16_t*>(lds + SCODES + r * K16 + pc * 16 + (b & 15));
-    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, false);
-  };
-  float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};  // main and residual passes (one tensor scale)
-  for (int ch = 0; ch < nch; ++ch) {
-    // chunks issued after ch whose DMA may still be in flight
-    const int pend = nch - 1 - ch < kGvBufs - 1 ? nch - 1 - ch : kGvBufs - 1;
-    if (pend >= 3)
-      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(3 * NCI) : "memory");
-    else if (pend == 2)
-      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * NCI) : "memory");
-    else if (pend == 1)
-      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NCI) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const uint8_t* buf = lds + (ch % kGvBufs) * CHUNK;
-    const int kl = wave * 128 + q * 32;  // this lane's 32 k within the chunk
-    const int k = ch * kGvKC + kl;
-    const uint4 av = code16(buf, c, kl), wv = code16(buf, WROW + c, kl);
-    const half2v sa = scale2(c, k), sw = scale2(WROW + c, k);
-    uint4 rv = av;
-    half2v sr = sa;
-    if constexpr (RAC) {
-      rv = code16(buf, 16 + c, kl);
-      sr = scale2(16 + c, k);
-    }
-    const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, rw[4] = {rv.x, rv.y, rv.z, rv.w},
-                   ww[4] = {wv.x, wv.y, wv.z, wv.w};
+    // code pieces: slot -> (row, piece), 32 pieces per row per chunk
+    const uint8_t* gcode[NCI];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int hi = st >> 1;  // steps 0-1: first block of the 32 k, 2-3: second
-      const half2v s_w = hi ? __builtin_shufflevector(sw, sw, 1, 1)
-                            : __builtin_shufflevector(sw, sw, 0, 0);
-      const half2v s_a = hi ? __builtin_shufflevector(sa, sa, 1, 1)
-                            : __builtin_shufflevector(sa, sa, 0, 0);
-      const half8 bw = dequant8(ww[st], s_w);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8(aw[st], s_a), bw, acc, 0, 0, 0);
+    for (int j = 0; j < NCI; ++j) {
+      const int slot = (j * kGvWaves + wave) * 64 + lane, r = slot >> 5;
+      gcode[j] = code_row(r) + (((slot & 31) ^ (r & 15)) << 4);
+    }
+    auto issue = [&](int ch) {
+      const uint32_t st = lbase + (ch % NBUF) * CHUNK;
+#pragma unroll
+      for (int j = 0; j < NCI; ++j) {
+        const uint32_t m0r = __builtin_amdgcn_readfirstlane(st + (j * kGvWaves + wave) * 1024);
+        const uint8_t* g = gcode[j] + (int64_t)ch * kGvCRow;
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :: "s"(m0r), "v"(g) : "memory", "m0");
+      }
+    };
+    for (int ch = 0; ch < NBUF && ch < nch; ++ch) issue(ch);
+
+    auto code16 = [&](const uint8_t* buf, int r, int kl) -> uint4 {
+      return *reinterpret_cast<const uint4*>(buf + r * kGvCRow + (((kl >> 5) ^ (r & 15)) << 4));
+    };
+    auto scale2 = [&](int r, int k) -> half2v {  // the two block scales of k .. k + 31
+      const int b = k >> 4, pc = (b >> 4) ^ (r & smask);
+      const uint32_t v =
+          *reinterpret_cast<const uint16_t*>(lds + SCODES + r * K16 + pc * 16 + (b & 15));
+      return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, false);
+    };
+    float4v acc[NS];  // main and residual passes (one tensor scale)
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) acc[sl] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int ch = 0; ch < nch; ++ch) {
+      // chunks issued after ch whose DMA may still be in flight
+      const int pend = nch - 1 - ch < NBUF - 1 ? nch - 1 - ch : NBUF - 1;
+      if (pend >= 3)
+        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(3 * NCI) : "memory");
+      else if (pend == 2)
+        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * NCI) : "memory");
+      else if (pend == 1)
+        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NCI) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      const uint8_t* buf = lds + (ch % NBUF) * CHUNK;
+      const int kl = wave * 128 + q * 32;  // this lane's 32 k within the chunk
+      const int k = ch * kGvKC + kl;
+      const uint4 av = code16(buf, c, kl);
+      const half2v sa = scale2(c, k);
+      uint4 rv = av;
+      half2v sr = sa;
       if constexpr (RAC) {
-        const half2v s_r = hi ? __builtin_shufflevector(sr, sr, 1, 1)
-                              : __builtin_shufflevector(sr, sr, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8(rw[st], s_r), bw, acc, 0, 0, 0);
+        rv = code16(buf, 16 + c, kl);
+        sr = scale2(16 + c, k);
+      }
+      uint4 wv[NS];
+      half2v sw[NS];
+#pragma unroll
+      for (int sl = 0; sl < NS; ++sl) {
+        wv[sl] = code16(buf, AROWS + 16 * sl + c, kl);
+        sw[sl] = scale2(AROWS + 16 * sl + c, k);
+      }
+      const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, rw[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int hi = st >> 1;  // steps 0-1: first block of the 32 k, 2-3: second
+        const half2v s_a = hi ? __builtin_shufflevector(sa, sa, 1, 1)
+                              : __builtin_shufflevector(sa, sa, 0, 0);
+        const half8 ba = dequant8(aw[st], s_a);
+        half8 br;
+        if constexpr (RAC) {
+          const half2v s_r = hi ? __builtin_shufflevector(sr, sr, 1, 1)
+                                : __builtin_shufflevector(sr, sr, 0, 0);
+          br = dequant8(rw[st], s_r);
+        }
+#pragma unroll
+        for (int sl = 0; sl < NS; ++sl) {
+          const uint32_t ww = st == 0 ? wv[sl].x : st == 1 ? wv[sl].y : st == 2 ? wv[sl].z
+                                                                              : wv[sl].w;
+          const half2v s_w = hi ? __builtin_shufflevector(sw[sl], sw[sl], 1, 1)
+                                : __builtin_shufflevector(sw[sl], sw[sl], 0, 0);
+          const half8 bw = dequant8(ww, s_w);
+          acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ba, bw, acc[sl], 0, 0, 0);
+          if constexpr (RAC)
+            acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(br, bw, acc[sl], 0, 0, 0);
+        }
+      }
+      if (ch + NBUF < nch) {
+        __syncthreads();  // every wave is done with this buffer
+        issue(ch + NBUF);
       }
     }
-    if (ch + kGvBufs < nch) {
-      __syncthreads();  // every wave is done with this buffer
-      issue(ch + kGvBufs);
+
+    __syncthreads();  // every wave is done with the last chunk: its buffer holds the sums
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) red[(wave * NS + sl) * 64 + lane] = acc[sl];
+    __syncthreads();
+    if (wave == 0) {
+      float4v sm[NS];
+#pragma unroll
+      for (int sl = 0; sl < NS; ++sl) {
+        sm[sl] = red[sl * 64 + lane];
+#pragma unroll
+        for (int i = 1; i < kGvWaves; ++i) sm[sl] += red[(i * NS + sl) * 64 + lane];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m0 + 4 * q + i;  // D row of element i
+        if (row >= row_end) continue;
+        if constexpr (!SILU) {
+          float* out = reinterpret_cast<float*>(p.out);
+          out[(int64_t)row * p.N + j0 + c] = scale * sm[0][i];
+        } else {
+          const float g = scale * sm[0][i], u = scale * sm[1][i];
+          if (p.out_y) {
+            p.out_y[(int64_t)row * p.N + j0 + c] = g;
+            p.out_y[(int64_t)row * p.N + I + j0 + c] = u;
+          }
+          const uint32_t h = nv_f32_to_bf16(silu_mul(g, u));
+          reinterpret_cast<uint16_t*>(p.out)[(int64_t)row * I + j0 + c] = (uint16_t)h;
+          hmax = __builtin_fmaxf(hmax, __builtin_fabsf(nv_bf16_to_f32(h)));
+        }
+      }
     }
   }
-
-  red[wave][lane] = acc;
-  __syncthreads();
-  if (wave != 0) return;
-  float4v sm = red[0][lane];
-#pragma unroll
-  for (int i = 1; i < kGvWaves; ++i) sm += red[i][lane];
-  const float s_ta = p.a_ts[0];
-  float scale = p.w_ts[0] * s_ta;
-  if constexpr (RAC) {
-    if (p.r_ts[0] != s_ta) scale = __builtin_nanf("");  // the residual shares s_ta
-  }
-  float* out = reinterpret_cast<float*>(p.out);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = m0 + 4 * q + i;  // D row of element i
-    if (row < p.total_rows) out[(int64_t)row * p.N + n0 + c] = scale * sm[i];
+  if constexpr (SILU) {
+    if (wave == 0 && p.out_amax) {
+      hmax = nv_wave_max(hmax);
+      if (lane == 0 && hmax > 0.0f)
+        atomicMax(reinterpret_cast<uint32_t*>(p.out_amax), __float_as_uint(hmax));
+    }
   }
 }
 
-template <bool RAC, bool GATHER>
-int launch_gemv(GemmParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)(p.N / 16), (unsigned)((p.total_rows + 15) / 16));
-  hipLaunchKernelGGL((k_gemv16<RAC, GATHER>), grid, dim3(64 * kGvWaves), 0, s, p);
+// Many groups with few rows each (the experts of a decode step): there is
+// parallelism to spare across groups, so a workgroup owns 128 columns (eight
+// 16-column slabs; with SiLU*mul four gate and the four matching up slabs)
+// and one group.  A wave dequantizes its A and R fragments once for four
+// slabs, which keeps the VALU work per streamed W byte low.  K goes in
+// 256-k chunks (codes, then the chunk's block scales, of 160 LDS rows) through
+// a three-deep ring of 23 KiB buffers: two chunks stay in flight while the
+// third is computed, and two workgroups fit on a CU, so one streams while
+// the other starts or finishes.  Wave w takes k-slice w % 2 (128 k) of every
+// chunk for slabs 4 (w / 2) .. 4 (w / 2) + 3; the two slices of a slab are
+// added in slice order.
+constexpr int kGwWaves = 4;
+constexpr int kGwSlices = 2;               // 128-k slices per chunk
+constexpr int kGwKC = 128 * kGwSlices;     // k per chunk
+constexpr int kGwSlabs = 8;                // 16-column W slabs per workgroup
+constexpr int kGwWaveSlabs = kGwSlabs * kGwSlices / kGwWaves;  // slabs per wave
+constexpr int kGwBufs = 3;
+
+template <bool RAC, bool SILU, bool GATHER>
+__global__ __launch_bounds__(64 * kGwWaves) void k_gemv_wide(GemmParams p) {
+  constexpr int ROWS = 32 + 16 * kGwSlabs;   // A 16 | R 16 (zero rows without RAC) | W
+  constexpr int CROW = kGwKC / 2;            // code bytes per row per chunk (8 pieces)
+  constexpr int SROW = kGwKC / 16;           // scale bytes per row per chunk
+  constexpr int CODES = ROWS * CROW;
+  constexpr int NCI = CODES / 1024 / kGwWaves;  // code DMA (16 B per lane) per wave
+  // scale DMA (4 B per lane), rounded up to whole instructions per wave: the
+  // extra lanes fetch zero-row words into padding past the scales
+  constexpr int NSI = (ROWS * SROW + 256 * kGwWaves - 1) / (256 * kGwWaves);
+  constexpr int SCALE_WORDS = ROWS * SROW / 4;
+  constexpr int CHUNK = CODES + NSI * kGwWaves * 256;
+  constexpr int PER = NCI + NSI;             // DMA instructions per wave per chunk
+  static_assert(CODES % (1024 * kGwWaves) == 0 && (kGwBufs - 1) * PER <= 63, "DMA, vmcnt");
+  static_assert(kGwWaves * kGwWaveSlabs * 64 * 16 <= CHUNK, "reduction fits in a chunk buffer");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kGwBufs * CHUNK];
+  float4v* red = reinterpret_cast<float4v*>(lds);  // [wave][wave slab][lane], after the last chunk
+
+  const int grp = blockIdx.z;
+  const int row_beg = p.offsets[grp], row_end = p.offsets[grp + 1];
+  const int nrows = row_end - row_beg;
+  if ((int)blockIdx.y * 16 >= nrows) return;  // workgroup-uniform
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ks = wave % kGwSlices, sh = wave / kGwSlices;  // k-slice, slab group
+  const int K = p.K, K2 = K >> 1, K16 = K >> 4;
+  const int nch = K / kGwKC;
+  const int I = p.N >> 1;
+  constexpr int HS = SILU ? kGwSlabs / 2 : kGwSlabs;  // slabs per half (gate, up)
+  const int j0 = (int)blockIdx.x * 16 * HS;           // first column of slab 0
+  auto w_row = [&](int i) -> int64_t {  // W row of LDS W row i
+    const int sl = i >> 4;
+    const int n = SILU ? (sl >= HS ? I : 0) + j0 + (sl % HS) * 16 + (i & 15) : j0 + i;
+    return (int64_t)grp * p.N + n;
+  };
+  const float s_ta = p.a_ts[p.per_group ? grp : 0];
+  float scale = p.w_ts[grp] * s_ta;
+  if constexpr (RAC) {
+    if (p.r_ts[p.per_group ? grp : 0] != s_ta) scale = __builtin_nanf("");  // shares s_ta
+  }
+  const uint32_t lbase = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
+  const int c = lane & 15, q = lane >> 4;
+  float hmax = 0.0f;
+
+  for (int tile = blockIdx.y; tile * 16 < nrows; tile += gridDim.y) {
+    const int m0 = row_beg + tile * 16;
+    auto act = [&](const uint8_t* base, int i, int per_row) -> const uint8_t* {
+      const int m = m0 + i;
+      if (m >= row_end) return nv_zero_row;
+      return base + (GATHER ? (int64_t)p.gather[m] : (int64_t)m) * per_row;
+    };
+    auto code_row = [&](int r) -> const uint8_t* {
+      if (r < 16) return act(p.a_codes, r, K2);
+      if (r < 32) return RAC ? act(p.r_codes, r - 16, K2) : nv_zero_row;
+      return p.w_codes + w_row(r - 32) * K2;
+    };
+    auto scale_row = [&](int r) -> const uint8_t* {
+      if (r < 16) return act(p.a_scales, r, K16);
+      if (r < 32) return RAC ? act(p.r_scales, r - 16, K16) : nv_zero_row;
+      return p.w_scales + w_row(r - 32) * K16;
+    };
+    // per-lane sources: code pieces (8 per row per chunk, XOR-swizzled by
+    // row) and scale words (4 per row per chunk); chunk ch adds ch * CROW
+    // or ch * SROW (the zero row is long enough for every chunk)
+    const uint8_t* gcode[NCI];
+    const uint8_t* gscale[NSI];
+#pragma unroll
+    for (int j = 0; j < NCI; ++j) {
+      const int slot = (j * kGwWaves + wave) * 64 + lane, r = slot >> 3;
+      gcode[j] = code_row(r) + (((slot & 7) ^ (r & 7)) << 4);
+    }
+#pragma unroll
+    for (int j = 0; j < NSI; ++j) {
+      const int slot = (j * kGwWaves + wave) * 64 + lane;
+      gscale[j] = slot < SCALE_WORDS ? scale_row(slot >> 2) + (slot & 3) * 4 : nv_zero_row;
+    }
+    auto issue = [&](int ch) {
+      const uint32_t st = lbase + (ch % kGwBufs) * CHUNK;
+#pragma unroll
+      for (int j = 0; j < NCI; ++j) {
+        const uint32_t m0r = __builtin_amdgcn_readfirstlane(st + (j * kGwWaves + wave) * 1024);
+        const uint8_t* g = gcode[j] + (int64_t)ch * CROW;
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :: "s"(m0r), "v"(g) : "memory", "m0");
+      }
+#pragma unroll
+      for (int j = 0; j < NSI; ++j) {
+        const uint32_t m0r =
+            __builtin_amdgcn_readfirstlane(st + CODES + (j * kGwWaves + wave) * 256);
+        const uint8_t* g = gscale[j] + (int64_t)ch * SROW;
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                     :: "s"(m0r), "v"(g) : "memory", "m0");
+      }
+    };
+    __syncthreads();  // the previous tile's reduction has been read
+    for (int ch = 0; ch < kGwBufs - 1 && ch < nch; ++ch) issue(ch);
+
+    auto code16 = [&](const uint8_t* buf, int r, int kl) -> uint4 {
+      return *reinterpret_cast<const uint4*>(buf + r * CROW + (((kl >> 5) ^ (r & 7)) << 4));
+    };
+    auto scale2 = [&](const uint8_t* buf, int r, int kl) -> half2v {  // blocks of kl .. kl+31
+      const uint32_t v = *reinterpret_cast<const uint16_t*>(buf + CODES + r * SROW + (kl >> 4));
+      return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, false);
+    };
+    float4v acc[kGwWaveSlabs];  // main and residual passes (one tensor scale)
+#pragma unroll
+    for (int t = 0; t < kGwWaveSlabs; ++t) acc[t] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int ch = 0; ch < nch; ++ch) {
+      // issue chunk ch + 2 into the buffer computed two iterations ago (the
+      // barrier at the end of the previous iteration ended its reads), then
+      // wait for chunk ch: the chunks issued after it may stay in flight
+      if (ch + kGwBufs - 1 < nch) issue(ch + kGwBufs - 1);
+      const int pend = nch - 1 - ch < kGwBufs - 1 ? nch - 1 - ch : kGwBufs - 1;
+      if (pend >= 2)
+        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * PER) : "memory");
+      else if (pend == 1)
+        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(PER) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      const uint8_t* buf = lds + (ch % kGwBufs) * CHUNK;
+      const int kl = ks * 128 + q * 32;  // this lane's 32 k within the chunk
+      const uint4 av = code16(buf, c, kl);
+      const half2v sa = scale2(buf, c, kl);
+      uint4 rv = av;
+      half2v sr = sa;
+      if constexpr (RAC) {
+        rv = code16(buf, 16 + c, kl);
+        sr = scale2(buf, 16 + c, kl);
+      }
+      const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, rw[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {  // the two 16-k blocks of the lane's 32 k
+        const half2v s_a = hi ? __builtin_shufflevector(sa, sa, 1, 1)
+                              : __builtin_shufflevector(sa, sa, 0, 0);
+        const half2v s_r = hi ? __builtin_shufflevector(sr, sr, 1, 1)
+                              : __builtin_shufflevector(sr, sr, 0, 0);
+        const half8 ba0 = dequant8(aw[2 * hi], s_a), ba1 = dequant8(aw[2 * hi + 1], s_a);
+        half8 br0, br1;
+        if constexpr (RAC) {
+          br0 = dequant8(rw[2 * hi], s_r);
+          br1 = dequant8(rw[2 * hi + 1], s_r);
+        }
+#pragma unroll
+        for (int t = 0; t < kGwWaveSlabs; ++t) {
+          const int r = 32 + 16 * (sh * kGwWaveSlabs + t) + c;
+          const uint4 wv = code16(buf, r, kl);
+          const half2v sw = scale2(buf, r, kl);
+          const half2v s_w = hi ? __builtin_shufflevector(sw, sw, 1, 1)
+                                : __builtin_shufflevector(sw, sw, 0, 0);
+          const half8 bw0 = dequant8(hi ? wv.z : wv.x, s_w), bw1 = dequant8(hi ? wv.w : wv.y, s_w);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ba0, bw0, acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ba1, bw1, acc[t], 0, 0, 0);
+          if constexpr (RAC) {
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(br0, bw0, acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(br1, bw1, acc[t], 0, 0, 0);
+          }
+        }
+      }
+      __syncthreads();  // every wave is done with this buffer
+    }
+
+#pragma unroll
+    for (int t = 0; t < kGwWaveSlabs; ++t) red[(wave * kGwWaveSlabs + t) * 64 + lane] = acc[t];
+    __syncthreads();
+    // wave w finishes slabs w and w + 4 (with SiLU: gate slab w, up slab w + 4);
+    // slab sl's two k-slices sit with the waves of slab group sl / 4
+    constexpr int PERW = kGwSlabs / kGwWaves;
+    float4v sm[PERW];
+#pragma unroll
+    for (int t = 0; t < PERW; ++t) {
+      const int sl = wave + t * kGwWaves;
+      const int g = sl / kGwWaveSlabs, u = sl % kGwWaveSlabs;
+      sm[t] = red[((g * kGwSlices + 0) * kGwWaveSlabs + u) * 64 + lane];
+#pragma unroll
+      for (int i = 1; i < kGwSlices; ++i)
+        sm[t] += red[((g * kGwSlices + i) * kGwWaveSlabs + u) * 64 + lane];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = m0 + 4 * q + i;  // D row of element i
+      if (row >= row_end) continue;
+      if constexpr (!SILU) {
+        float* out = reinterpret_cast<float*>(p.out);
+#pragma unroll
+        for (int t = 0; t < PERW; ++t)
+          out[(int64_t)row * p.N + j0 + (wave + t * kGwWaves) * 16 + c] = scale * sm[t][i];
+      } else {
+        static_assert(!SILU || (PERW == 2 && HS == kGwWaves), "gate slab w, up slab w + HS");
+        const int j = j0 + wave * 16 + c;
+        const float g = scale * sm[0][i], u = scale * sm[1][i];
+        if (p.out_y) {
+          p.out_y[(int64_t)row * p.N + j] = g;
+          p.out_y[(int64_t)row * p.N + I + j] = u;
+        }
+        const uint32_t h = nv_f32_to_bf16(silu_mul(g, u));
+        reinterpret_cast<uint16_t*>(p.out)[(int64_t)row * I + j] = (uint16_t)h;
+        hmax = __builtin_fmaxf(hmax, __builtin_fabsf(nv_bf16_to_f32(h)));
+      }
+    }
+  }
+  if constexpr (SILU) {
+    if (p.out_amax) {
+      hmax = nv_wave_max(hmax);
+      if (lane == 0 && hmax > 0.0f)
+        atomicMax(reinterpret_cast<uint32_t*>(p.out_amax), __float_as_uint(hmax));
+    }
+  }
+}
+
+template <bool RAC, bool SILU, bool GATHER>
+int launch_gemv_wide(GemmParams& p, hipStream_t s) {
+  const int cols = 16 * kGwSlabs;  // output columns (SiLU: gate + up columns) per workgroup
+  const dim3 grid((unsigned)(p.N / cols), 1u, (unsigned)p.G);
+  hipLaunchKernelGGL((k_gemv_wide<RAC, SILU, GATHER>), grid, dim3(64 * kGwWaves), 0, s, p);
   return nv_launch_status();
+}
+
+template <bool RAC, bool SILU, bool GATHER>
+int launch_gemv(GemmParams& p, hipStream_t s) {
+  const int slabs = SILU ? p.N / 32 : p.N / 16;
+  const int ytiles = p.G == 1 ? (p.total_rows + 15) / 16 : 1;
+  const dim3 grid((unsigned)slabs, (unsigned)ytiles, (unsigned)p.G);
+  hipLaunchKernelGGL((k_gemv<RAC, SILU, GATHER>), grid, dim3(64 * kGvWaves), 0, s, p);
+  return nv_launch_status();
+}
+
+// 0: tile kernel; 1: decode kernel (one group); 2: wide decode kernel (groups)
+int gemv_kind(const GemmParams& p, bool silu) {
+  if (p.G == 1)
+    return p.total_rows <= kGvMaxRows && p.K % kGvKC == 0 &&
+                   p.K <= (silu ? 12288 : kGvMaxK) && p.N / 16 <= 65535
+               ? 1 : 0;
+  return p.total_rows <= (int64_t)kGvAvgRows * p.G && p.K % kGwKC == 0 && p.G <= 65535 ? 2 : 0;
+}
+
+int launch_gemv_wide_any(GemmParams& p, bool rac, bool silu, bool gather, hipStream_t s) {
+  if (rac) {
+    if (silu) return gather ? launch_gemv_wide<true, true, true>(p, s) : launch_gemv_wide<true, true, false>(p, s);
+    return gather ? launch_gemv_wide<true, false, true>(p, s) : launch_gemv_wide<true, false, false>(p, s);
+  }
+  if (silu) return gather ? launch_gemv_wide<false, true, true>(p, s) : launch_gemv_wide<false, true, false>(p, s);
+  return gather ? launch_gemv_wide<false, false, true>(p, s) : launch_gemv_wide<false, false, false>(p, s);
+}
+
+int launch_gemv_any(GemmParams& p, bool rac, bool silu, bool gather, hipStream_t s) {
+  if (rac) {
+    if (silu) return gather ? launch_gemv<true, true, true>(p, s) : launch_gemv<true, true, false>(p, s);
+    return gather ? launch_gemv<true, false, true>(p, s) : launch_gemv<true, false, false>(p, s);
+  }
+  if (silu) return gather ? launch_gemv<false, true, true>(p, s) : launch_gemv<false, true, false>(p, s);
+  return gather ? launch_gemv<false, false, true>(p, s) : launch_gemv<false, false, false>(p, s);
 }
 
 // Tile configurations (rows x cols per workgroup, waves, LDS stages, min waves
@@ -735,12 +1062,11 @@ int w4a4_grouped_gemm_rac(const w4a4_gemm_args_t* a, void*, size_t, void* stream
   p.skip = (a->flags & NVFP4_GEMM_SKIP_INACTIVE_BLOCKS) && a->kblock_active ? 1 : 0;
   p.per_group = (a->flags & NVFP4_GEMM_PER_GROUP_SCALES) ? 1 : 0;
   const bool rac = a->r_codes != nullptr, gather = a->gather_rows != nullptr;
-  if (p.G == 1 && p.total_rows <= kGvMaxRows && p.K % kGvKC == 0 && p.K <= kGvMaxK &&
-      a->epilogue == NVFP4_EPI_F32) {
-    if (rac) return gather ? launch_gemv<true, true>(p, s) : launch_gemv<true, false>(p, s);
-    return gather ? launch_gemv<false, true>(p, s) : launch_gemv<false, false>(p, s);
-  }
-  return launch(p, rac, a->epilogue == NVFP4_EPI_SILU_MUL_BF16, gather, s);
+  const bool silu = a->epilogue == NVFP4_EPI_SILU_MUL_BF16;
+  const int kind = gemv_kind(p, silu);
+  if (kind == 1) return launch_gemv_any(p, rac, silu, gather, s);
+  if (kind == 2) return launch_gemv_wide_any(p, rac, silu, gather, s);
+  return launch(p, rac, silu, gather, s);
 }
 
 }  // extern "C"
