@@ -85,10 +85,13 @@ __device__ __forceinline__ int nv_score_shift(float s_t) {
   return (s_t == 0.0f) ? 8 : 8 - __builtin_amdgcn_frexp_expf(s_t);
 }
 
-// Fixed-point magnitude q = min(floor(|e| 2^shift), 2^17 - 1), as float.
-__device__ __forceinline__ float nv_score_q(float e, int shift) {
-  const float q = __builtin_floorf(__builtin_ldexpf(__builtin_fabsf(e), shift));
-  return __builtin_fminf(q, 131071.0f);
+// Fixed-point magnitude q = min(floor(|e| 2^shift), 2^17 - 1).  The clamp
+// comes first and the conversion truncates, which is the floor of a
+// non-negative value (2^17 - 1 is an integer, so clamping and flooring
+// commute).
+__device__ __forceinline__ uint32_t nv_score_qi(float e, int shift) {
+  const float t = __builtin_fminf(__builtin_ldexpf(__builtin_fabsf(e), shift), 131071.0f);
+  return (uint32_t)t;
 }
 
 // bf16 bits -> float.

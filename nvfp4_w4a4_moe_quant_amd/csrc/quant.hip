@@ -135,8 +135,9 @@ __device__ float workgroup_amax(const float* __restrict__ partials, int nparts,
 // grid.x: column tiles of `tpr` column blocks; grid.y: row splits.  Thread t
 // handles column block (blockIdx.x * tpr + t % tpr) for rows
 // start + t / tpr, start + t / tpr + rpi, ...  With statistics, per-channel
-// partial sums are accumulated in registers (FP64, exact integers below 2^53),
-// combined in LDS, then added to the global int64 sums.  That costs one
+// partial sums of q^2 (q < 2^17) are accumulated in 64-bit integer registers
+// (one v_mad_u64_u32 per element), combined in LDS, then added to the global
+// int64 sums.  That costs one
 // global atomic pair per channel and workgroup, and atomics on one address
 // are serialized, so the host keeps the row splits few and the workgroups
 // large (16 waves).
@@ -240,11 +241,11 @@ __global__ __launch_bounds__(kQThreads) void k_quant(
   const int64_t r1 = r0 + rows_per_split < row0 + rows ? r0 + rows_per_split : row0 + rows;
   const int shift = nv_score_shift(s_t);
 
-  double acc[16];
+  uint64_t acc[16];
   float emax[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    acc[i] = 0.0;
+    acc[i] = 0u;
     emax[i] = 0.0f;
   }
 
@@ -265,8 +266,8 @@ __global__ __launch_bounds__(kQThreads) void k_quant(
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float e = v[i] - (g[i] * sb) * s_t;
-        const float q = nv_score_q(e, shift);
-        acc[i] = __builtin_fma((double)q, (double)q, acc[i]);
+        const uint32_t q = nv_score_qi(e, shift);
+        acc[i] += (uint64_t)q * q;
         emax[i] = __builtin_fmaxf(emax[i], __builtin_fabsf(e));
       }
     }
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant(
     if (active) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        if (acc[i] != 0.0) atomicAdd(&lsum[i * tpr + cbl], (unsigned long long)acc[i]);
+        if (acc[i] != 0u) atomicAdd(&lsum[i * tpr + cbl], (unsigned long long)acc[i]);
         if (emax[i] != 0.0f) atomicMax(&lmax[i * tpr + cbl], __float_as_uint(emax[i]));
       }
     }
