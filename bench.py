@@ -54,7 +54,7 @@ def parse():
                     help="MoE workloads: also time the full block (weighted combine), a "
                          "16-token decode call eager vs HIP-graph replay, and the trainer-side "
                          "weight fake-quant; dense workloads: the step eager vs HIP-graph replay")
-    ap.add_argument("--fp8-library-reference", type=int, default=0,
+    ap.add_argument("--fp8-library-reference", type=int, default=1,
                     help="also time the vendor FP8 GEMM (hipBLASLt through torch._scaled_mm, "
                          "row/column scales, bf16 out) on the dense shape of each GEMM: a "
                          "reference point for what an FP8 GEMM reaches on this chip, not a "
@@ -287,7 +287,19 @@ def main():
         res["comparators"] = comparators(w, timed, step, step_fp8, seg, ms_step, rac, NEV,
                                          step_pe if w.kind == "moe" else None)
         if args.fp8_library_reference:
-            res["comparators"]["fp8_dense_library_reference"] = library_fp8_reference(w, dev)
+            lib = library_fp8_reference(w, dev)
+            f8 = res["comparators"]["fp8_w8a8"]
+            ours = ([f8.get("gemm_gate_up_us"), f8.get("gemm_down_us")] if w.kind == "moe"
+                    else [f8.get("gemm_us")])
+            libs = [v.get("us") for v in lib.values()]
+            if None not in ours and None not in libs:
+                # the FP8 step with the library's dense GEMM times in place of
+                # this library's grouped FP8 GEMMs (no grouping, no gather)
+                est = f8["ms_per_step"] + (sum(libs) - sum(ours)) * 1e-3
+                lib["ours_over_library"] = [round(a / b, 3) for a, b in zip(ours, libs)]
+                lib["fp8_step_ms_with_library_gemms"] = round(est, 4)
+                lib["nvfp4_rac_step_over_that"] = round(ms_step / est, 4)
+            res["comparators"]["fp8_dense_library_reference"] = lib
     if args.extras and w.kind == "moe":
         res.update(moe_extras(w, dev, x, lg, wgu, wd, nsx, nsh, timed, step, ms_step, NEV))
     if args.extras and w.kind == "dense":

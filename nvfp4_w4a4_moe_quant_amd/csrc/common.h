@@ -80,6 +80,37 @@ __device__ __forceinline__ float nv_block_recip(float Sb) {
   return (Sb > 0.0f) ? (float)(1.0 / (double)Sb) : 0.0f;
 }
 
+// nv_block_scale from an FP32 product instead of the double-precision
+// quotient.  c6 = RN32(1 / (6 s_t)) (per tensor) makes r = RN32(amax_b c6)
+// agree with y = amax_b / (6 s_t) to within 1.5 * 2^-23 relative (two FP32
+// roundings), and the quotient rounded to FP32 agrees with y to 2^-24: the two
+// lie less than three FP32 ulp apart.  In E4M3's normal range the code only
+// changes at the midpoints between grid values, which sit at 0x80000 in the
+// low 20 mantissa bits of each binade (powers of two are grid values, not
+// boundaries); so when r is at least 16 ulp from a midpoint, r and the
+// quotient round to the same code.  Near a midpoint, below the normal range
+// (2^-6, with a margin) and for zero or non-finite products the exact path
+// decides.
+__device__ __forceinline__ uint32_t nv_block_scale_c6(float amax_b, float s_t, float c6) {
+  if (amax_b == 0.0f) return 0u;
+  const float r = amax_b * c6;
+  const uint32_t u = __float_as_uint(r);
+  const bool near_mid = ((u & 0xFFFFFu) - 0x7FFF0u) < 0x20u;
+  if (r >= 0.0157f && r < 448.0f && !near_mid) {
+    const uint32_t c = ((u + 0x80000u) >> 20) - (120u << 3);  // round half up: no ties here
+    return c > 0x7Eu ? 0x7Eu : c;
+  }
+  if (r >= 448.0f && r <= 3.4e38f) return 0x7Eu;  // the quotient is at least 447.99: saturates
+  return nv_block_scale(amax_b, s_t);
+}
+
+// rb of every E4M3 code for one tensor scale: lut[c] = nv_block_recip(
+// RN32(E4M3(c) s_t)), filled by the first 128 threads (the caller
+// synchronizes before reading it).
+__device__ __forceinline__ void nv_fill_recip_lut(float* lut, float s_t) {
+  if (threadIdx.x < 128) lut[threadIdx.x] = nv_block_recip(nv_e4m3_to_f32(threadIdx.x) * s_t);
+}
+
 // Score shift 8 - Es where s_t = f * 2^Es, f in [0.5, 1).
 __device__ __forceinline__ int nv_score_shift(float s_t) {
   return (s_t == 0.0f) ? 8 : 8 - __builtin_amdgcn_frexp_expf(s_t);

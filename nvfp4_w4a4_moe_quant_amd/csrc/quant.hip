@@ -231,6 +231,12 @@ __global__ __launch_bounds__(kQThreads) void k_quant(
   const float amax = workgroup_amax(partials, nparts, goff ? nullptr : amax_in, red);
   const float s_t = nv_tensor_scale(amax);
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *tscale_out = s_t;
+  // per-tensor constants of the block scales: c6 for the FP32 fast path of
+  // the scale code, and rb of every code (one double division each, here)
+  __shared__ float rb_lut[128];
+  nv_fill_recip_lut(rb_lut, s_t);
+  const float c6 = (float)(1.0 / (6.0 * (double)s_t));
+  __syncthreads();
 
   const int64_t CB = K >> 4;
   const int sub = threadIdx.x / tpr;
@@ -255,9 +261,9 @@ __global__ __launch_bounds__(kQThreads) void k_quant(
     float amax_b = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) amax_b = __builtin_fmaxf(amax_b, __builtin_fabsf(v[i]));
-    const uint32_t sc = nv_block_scale(amax_b, s_t);
+    const uint32_t sc = nv_block_scale_c6(amax_b, s_t, c6);
     const float sb = nv_e4m3_to_f32(sc);
-    const float rb = nv_block_recip(sb * s_t);
+    const float rb = rb_lut[sc];
     const uint32_t lo = nv_encode8(v, rb), hi = nv_encode8(v + 8, rb);
     if constexpr (kStats) {
       float g[16];
@@ -587,6 +593,12 @@ __global__ __launch_bounds__(kThreads) void k_residual(
   const int64_t CB = K >> 4;
   const int64_t nblk = rows * CB;
   const float s_t = *tscale;
+  // rb of every E4M3 code and c6 for the FP32 fast path of the residual's
+  // scale codes (main and residual share the tensor scale)
+  __shared__ float rb_lut[128];
+  nv_fill_recip_lut(rb_lut, s_t);
+  const float c6 = (float)(1.0 / (6.0 * (double)s_t));
+  __syncthreads();
   // Blocks b = row * CB + cb, grid-stride; (row, cb) advance incrementally
   // (one 64-bit division per thread), two blocks in flight per iteration.
   const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -606,8 +618,9 @@ __global__ __launch_bounds__(kThreads) void k_residual(
     uint32_t packed[2] = {0u, 0u};
     uint32_t sc = 0u;
     if (m) {
-      const float sb = nv_e4m3_to_f32(scales[rr * CB + cc]);
-      const float rm = nv_block_recip(sb * s_t);
+      const uint32_t sm = scales[rr * CB + cc];
+      const float sb = nv_e4m3_to_f32(sm);
+      const float rm = rb_lut[sm];
       float g[16], e[16];
       nv_decode8(nv_encode8(v, rm), g);
       nv_decode8(nv_encode8(v + 8, rm), g + 8);
@@ -618,9 +631,8 @@ __global__ __launch_bounds__(kThreads) void k_residual(
         e[i] = ((m >> i) & 1u) ? v[i] - d : 0.0f;
         amax_b = __builtin_fmaxf(amax_b, __builtin_fabsf(e[i]));
       }
-      sc = nv_block_scale(amax_b, s_tr);
-      const float Sb = nv_e4m3_to_f32(sc) * s_tr;
-      const float rb = nv_block_recip(Sb);
+      sc = nv_block_scale_c6(amax_b, s_tr, c6);
+      const float rb = rb_lut[sc];  // nv_block_recip(RN32(E4M3(sc) s_t))
       packed[0] = nv_encode8(e, rb);
       packed[1] = nv_encode8(e + 8, rb);
     }

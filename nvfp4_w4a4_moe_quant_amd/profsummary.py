@@ -16,6 +16,18 @@ The JSON records the kernel, the raw and scaled byte counts, the factors and
 the SHA-256 of the kernel's source file, so that a reader can tell whether the
 counters still describe the current kernel.
 
+Ceiling of the quantizer kernels (k_amax, k_quant, k_rank, k_residual,
+k_zero_stats; one row per kernel and grid size, so the passes over X and H
+stay apart): the larger of the VALU issue time of the counted instructions
+and the time a plain copy kernel needs for the counted HBM bytes, against
+the measured duration.  Inputs: the kernel trace, a counter pass with
+GRBM_GUI_ACTIVE SQ_INSTS_VALU, the FETCH_SIZE and WRITE_SIZE passes and their
+copy calibration (copycal), and a kernel trace of the calibration copy:
+
+    python -m nvfp4_w4a4_moe_quant_amd.profsummary valu \
+        <kernel_trace.csv> <valu_pass.csv> <fetch.csv> <write.csv> \
+        <cal_fetch.csv> <cal_write.csv> <cal_trace.csv> <MiB> <XCDs> <SIMDs> [command]
+
 Clock and matrix-core utilisation of the GEMM kernels from a kernel trace and
 two counter passes (GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES
 SQ_VALU_MFMA_COEXEC_CYCLES SQ_WAVE_CYCLES SQ_ACTIVE_INST_VALU SQ_WAIT_ANY, then
@@ -161,10 +173,83 @@ def mfma(trace_csv, pass1_csv, pass2_csv, n_xcd, n_simd, command=""):
     print("\n".join(lines))
 
 
+def _by_grid(path, kind):
+    """{(kernel, grid size): [per-dispatch values]} for a counter pass
+    (kind = counter name) or a kernel trace (kind = None: durations in us)."""
+    out = collections.defaultdict(list)
+    if kind is None:
+        for r in csv.DictReader(open(path)):
+            g = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            out[(short(r["Kernel_Name"]), g)].append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        return out
+    per = collections.defaultdict(float)
+    meta = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != kind:
+            continue
+        per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+        meta[r["Dispatch_Id"]] = (short(r["Kernel_Name"]), int(r["Grid_Size"]))
+    for d, v in per.items():
+        out[meta[d]].append(v)
+    return out
+
+
+QUANT_KERNELS = ("k_amax", "k_quant", "k_rank", "k_residual", "k_zero_stats")
+
+
+def valu(trace_csv, valu_csv, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv,
+         cal_trace_csv, mib, n_xcd, n_simd, command=""):
+    """Per quantizer kernel and grid size (medians over dispatches):
+    clock f = GRBM_GUI_ACTIVE per XCD / duration; VALU issue time
+    T_v = SQ_INSTS_VALU x 4 cycles / (SIMDs x f) (a wave64 VALU instruction
+    occupies a 16-lane SIMD for 4 cycles; FP64 and transcendental
+    instructions take longer, so T_v is a lower bound); HBM bytes from the
+    scaled FETCH_SIZE + WRITE_SIZE; T_m = bytes / B_copy with B_copy the
+    bytes per second of the calibration copy (2 x MiB per dispatch over its
+    traced duration); ceiling = max(T_v, T_m); frac = ceiling / duration."""
+    mib, n_xcd, n_simd = float(mib), int(n_xcd), int(n_simd)
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    _, _, f_fac = calibration(cal_fetch_csv, "FETCH_SIZE", mib)
+    _, _, w_fac = calibration(cal_write_csv, "WRITE_SIZE", mib)
+    copy_us = max((med(v) for k, v in _by_grid(cal_trace_csv, None).items()
+                   if "elementwise" in k[0] and "add" in k[0].lower()), default=None)
+    if copy_us is None:
+        copy_us = max(med(v) for v in _by_grid(cal_trace_csv, None).values())
+    b_copy = 2.0 * mib * (1 << 20) / (copy_us * 1e-6)  # bytes per second
+    dur = _by_grid(trace_csv, None)
+    gui, insts = _by_grid(valu_csv, "GRBM_GUI_ACTIVE"), _by_grid(valu_csv, "SQ_INSTS_VALU")
+    fetch, write = _by_grid(fetch_csv, "FETCH_SIZE"), _by_grid(write_csv, "WRITE_SIZE")
+    lines = [f"command: {command}"] if command else []
+    lines.append(f"copy calibration: {2 * mib:.0f} MiB moved in {copy_us:.1f} us = "
+                 f"{b_copy / 1e12:.2f} TB/s; FETCH_SIZE x{f_fac:.4f}, WRITE_SIZE x{w_fac:.4f}")
+    lines.append(f"{'kernel':24s} {'grid':>8s} {'n':>3s} {'us':>7s} {'GHz':>5s} {'VALU_Minst':>10s} "
+                 f"{'T_valu':>7s} {'MB':>8s} {'TB/s':>5s} {'T_mem':>7s} {'frac':>5s}")
+    for key in sorted(dur):
+        name, grid = key
+        if not name.startswith(QUANT_KERNELS) or key not in gui or key not in insts:
+            continue
+        t = med(dur[key])
+        f = med(gui[key]) / n_xcd / (t * 1e-6)
+        tv = med(insts[key]) * 4.0 / (n_simd * f) * 1e6
+        nbytes = (med(fetch[key]) * 1024.0 * f_fac if key in fetch else 0.0) + \
+                 (med(write[key]) * 1024.0 * w_fac if key in write else 0.0)
+        tm = nbytes / b_copy * 1e6
+        lines.append(f"{name[:24]:24s} {grid:8d} {len(dur[key]):3d} {t:7.1f} {f / 1e9:5.2f} "
+                     f"{med(insts[key]) / 1e6:10.2f} {tv:7.1f} {nbytes / 1e6:8.1f} "
+                     f"{nbytes / (t * 1e-6) / 1e12:5.2f} {tm:7.1f} {max(tv, tm) / t:5.2f}")
+    lines.append("columns: medians over dispatches; T_valu = VALU issue time of the counted "
+                 "instructions at the measured clock; MB = scaled HBM bytes; T_mem = those "
+                 "bytes at the calibration copy's rate; frac = max(T_valu, T_mem) / us")
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
     if len(sys.argv) > 1 and sys.argv[1] == "traffic":
         traffic(*sys.argv[2:10], command=" ".join(sys.argv[10:]))
     elif len(sys.argv) > 1 and sys.argv[1] == "mfma":
         mfma(*sys.argv[2:7], command=" ".join(sys.argv[7:]))
+    elif len(sys.argv) > 1 and sys.argv[1] == "valu":
+        valu(*sys.argv[2:12], command=" ".join(sys.argv[12:]))
     else:
         main(sys.argv[1], " ".join(sys.argv[2:]))

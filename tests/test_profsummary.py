@@ -89,3 +89,44 @@ def test_kernel_stats_summary(tmp_path, capsys):
     assert out[2].split()[:3] == ["k_gemm<64,", "256,", "true>"]
     assert out[2].split()[-5:] == ["13", "463.14", "436.50", "486.85", "13.60"]
     assert out[3].split() == ["k_amax", "2", "4.50", "4.00", "5.00", "0.10"]
+
+
+def test_valu_ceiling(tmp_path, capsys):
+    """Quantizer ceiling rows: clock, VALU issue time, scaled bytes, copy-rate
+    memory time and the fraction, by hand from the definitions."""
+    q = "void (anonymous namespace)::k_quant<true, true, 0>(void const*)"
+    cp = "void at::native::vectorized_elementwise_kernel<4, add>(int)"
+    TR = ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X", "Grid_Size_Y",
+          "Grid_Size_Z"]
+    PM = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    # two quantize dispatches on different grids (X and H): 50 us and 100 us
+    _write(tmp_path / "t.csv", TR, [[q, 0, 50_000, 1024, 4, 1], [q, 0, 100_000, 1024, 8, 1]])
+    # grid 4096: GRBM_GUI_ACTIVE 2 XCDs x 100000 -> 100000 cycles in 50 us = 2 GHz;
+    # 1e6 VALU instructions x 4 cycles / (4 SIMDs x 2e9) = 500 us ... scaled below
+    _write(tmp_path / "v.csv", PM, [
+        ["1", q, 4096, "GRBM_GUI_ACTIVE", 100_000], ["1", q, 4096, "GRBM_GUI_ACTIVE", 100_000],
+        ["1", q, 4096, "SQ_INSTS_VALU", 40_000],
+        ["2", q, 8192, "GRBM_GUI_ACTIVE", 200_000], ["2", q, 8192, "GRBM_GUI_ACTIVE", 200_000],
+        ["2", q, 8192, "SQ_INSTS_VALU", 20_000]])
+    # bytes: grid 4096 fetch 1000 KiB x2 + write 500 KiB x1 = 2500 KiB
+    _write(tmp_path / "f.csv", PM, [["1", q, 4096, "FETCH_SIZE", 1000.0],
+                                    ["2", q, 8192, "FETCH_SIZE", 0.0]])
+    _write(tmp_path / "w.csv", PM, [["1", q, 4096, "WRITE_SIZE", 500.0],
+                                    ["2", q, 8192, "WRITE_SIZE", 0.0]])
+    _write(tmp_path / "cf.csv", PMC_HDR, [["1", cp, "FETCH_SIZE", 512.0]])
+    _write(tmp_path / "cw.csv", PMC_HDR, [["1", cp, "WRITE_SIZE", 1024.0]])
+    # the 1 MiB copy (2 MiB moved) takes 1 us -> 2 MiB per us
+    _write(tmp_path / "ct.csv", TR, [[cp, 0, 1_000, 256, 1, 1]])
+    S.valu(*(str(tmp_path / n) for n in ("t.csv", "v.csv", "f.csv", "w.csv", "cf.csv",
+                                         "cw.csv", "ct.csv")), "1", "2", "4")
+    out = capsys.readouterr().out.splitlines()
+    rows = [l.split() for l in out if l.startswith("k_quant")]
+    assert len(rows) == 2
+    r = {int(x[-10]): x[-9:] for x in rows}
+    # grid 4096: 50 us, 2.00 GHz, 0.04 Minst, T_v = 40000*4/(4*2e9) = 20 us,
+    # 2.56 MB = 2500 KiB, 51.2 GB/s... = 0.05 TB/s, T_m = 2500 KiB / 2 MiB/us
+    # = 1.2 us, frac = 20 / 50 = 0.40
+    assert r[4096] == ["1", "50.0", "2.00", "0.04", "20.0", "2.6", "0.05", "1.2", "0.40"]
+    # grid 8192: 100 us, 2.00 GHz, T_v = 20000*4/(4*2e9) = 10 us, frac 0.10
+    assert r[8192][:5] == ["1", "100.0", "2.00", "0.02", "10.0"]
+    assert r[8192][-1] == "0.10"
