@@ -196,12 +196,16 @@ def _by_grid(path, kind):
 
 
 QUANT_KERNELS = ("k_amax", "k_quant", "k_rank", "k_residual", "k_zero_stats")
+PEAK_CLOCK_HZ = 2.4e9  # MI355X peak engine clock
 
 
 def valu(trace_csv, valu_csv, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv,
          cal_trace_csv, mib, n_xcd, n_simd, command=""):
     """Per quantizer kernel and grid size (medians over dispatches):
-    clock f = GRBM_GUI_ACTIVE per XCD / duration; VALU issue time
+    clock f = GRBM_GUI_ACTIVE per XCD / duration, at most the chip's 2.4
+    GHz (for kernels of a few tens of microseconds the GUI-active count
+    also covers the counter collection around the dispatch, which would put
+    f above the peak); VALU issue time
     T_v = SQ_INSTS_VALU x 4 cycles / (SIMDs x f) (a wave64 VALU instruction
     occupies a 16-lane SIMD for 4 cycles; FP64 and transcendental
     instructions take longer, so T_v is a lower bound); HBM bytes from the
@@ -230,7 +234,7 @@ def valu(trace_csv, valu_csv, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv
         if not name.startswith(QUANT_KERNELS) or key not in gui or key not in insts:
             continue
         t = med(dur[key])
-        f = med(gui[key]) / n_xcd / (t * 1e-6)
+        f = min(med(gui[key]) / n_xcd / (t * 1e-6), PEAK_CLOCK_HZ)
         tv = med(insts[key]) * 4.0 / (n_simd * f) * 1e6
         nbytes = (med(fetch[key]) * 1024.0 * f_fac if key in fetch else 0.0) + \
                  (med(write[key]) * 1024.0 * w_fac if key in write else 0.0)
@@ -238,9 +242,10 @@ def valu(trace_csv, valu_csv, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv
         lines.append(f"{name[:24]:24s} {grid:8d} {len(dur[key]):3d} {t:7.1f} {f / 1e9:5.2f} "
                      f"{med(insts[key]) / 1e6:10.2f} {tv:7.1f} {nbytes / 1e6:8.1f} "
                      f"{nbytes / (t * 1e-6) / 1e12:5.2f} {tm:7.1f} {max(tv, tm) / t:5.2f}")
-    lines.append("columns: medians over dispatches; T_valu = VALU issue time of the counted "
-                 "instructions at the measured clock; MB = scaled HBM bytes; T_mem = those "
-                 "bytes at the calibration copy's rate; frac = max(T_valu, T_mem) / us")
+    lines.append("columns: medians over dispatches; GHz = measured clock, capped at 2.4; "
+                 "T_valu = VALU issue time of the counted instructions at that clock; MB = "
+                 "scaled HBM bytes; T_mem = those bytes at the calibration copy's rate; "
+                 "frac = max(T_valu, T_mem) / us")
     print("\n".join(lines))
 
 
