@@ -453,12 +453,13 @@ int launch_t(GemmParams& p, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode-shaped GEMM: few rows per group -- one group with at most 64 rows
-// (a 16 x 4096 x 4096 linear layer), or many groups averaging at most four
-// rows (the experts of a decode step) -- with K % 1024 == 0, K <= 16384.  A
-// workgroup owns one 16-column slab of W (with the SiLU*mul epilogue two:
-// gate columns j .. j+15 and the up columns I + j ..) over the whole of K, and
-// the 16-row tiles of one group: N/16 workgroups per group stream W once.
+// Decode-shaped GEMM for one group with at most 64 rows (a 16 x 4096 x 4096
+// linear layer is the model case), K % 1024 == 0, K <= 16384 (12288 with
+// SiLU*mul).  A workgroup owns one 16-column slab of W (with the SiLU*mul
+// epilogue two: gate columns j .. j+15 and the up columns I + j ..) over the
+// whole of K, and one 16-row tile (grid y; the kernel is written for any
+// group count, grid z, but many small groups take k_gemv_wide below): N/16
+// workgroups stream W once.
 //  * Every operand goes through LDS by coalesced DMA: each wave-instruction
 //    fetches 1 KiB of whole 128-byte lines (two rows' 512-byte pieces of a
 //    chunk).  Fetching MFMA fragments straight from global memory would make
