@@ -180,3 +180,49 @@ def test_full_moe_ffn_e128_gate_up_and_down(orc):
     err = rel_frob(host(yd), yd_ref)
     say(f"  down FP32 rel frob {err:.3e} over {yd_ref.size} values")
     assert err <= REL_F
+
+
+@pytest.mark.parametrize("silu", [True, False])
+def test_tail_tiles_every_size(orc, silu):
+    """Experts whose last 128-row m-tile holds 1, 31, 32, 33, 63, 64 or 65
+    rows (and whole tiles) in the 128 x 512 configuration: tails of at most
+    64 rows run with every wave on the same rows (narrow), longer ones with
+    two wave rows.  FP32 outputs (or the FP32 side output of SiLU*mul) at
+    1e-5, H against the oracle's SiLU*mul."""
+    _ORC["o"] = orc
+    sizes = [1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 160, 191, 192, 193, 256, 300, 0, 2]
+    G, H, N = len(sizes), 512, 512
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    total = int(off[-1])
+    say(f"tail tiles silu={silu} rows={total}")
+    rng = np.random.default_rng(5 + silu)
+    src = 150
+    x = D.bf16_to_f32(D.bf16_bits(rng.standard_normal((src, H)).astype(np.float32)))
+    x[:, rng.choice(H, 5, replace=False)] *= 20.0
+    gat = rng.integers(0, src, total).astype(np.int32)
+    d = orc.quantize_rac(x, H // 2)
+    wq = [orc.quantize((rng.standard_normal((N, H)) * 0.02).astype(np.float32)) for _ in range(G)]
+    w = (np.stack([q[0] for q in wq]), np.stack([q[1] for q in wq]),
+         np.array([q[2] for q in wq], np.float32))
+    a = (d["codes"], d["scales"], d["s_t"])
+    r = (d["res_codes"], d["res_scales"], d["s_tr"])
+    y_ref = orc.grouped_gemm(N, H, off, gat, a, r, w)
+    kw = dict(N=N, K=H, total_rows=total, gather_rows=_dev(gat), r=_nv(*r),
+              kblock_active=_dev(d["active"]), validate=True)
+    if not silu:
+        y = host(L.w4a4_grouped_gemm_rac(_nv(*a), _nv(*w), _dev(off), **kw))
+        err = rel_frob(y, y_ref)
+        say(f"  FP32 rel frob {err:.3e}")
+        assert err <= REL_F
+        return
+    out_y = torch.full((total, N), float("nan"), dtype=torch.float32, device=DEV)
+    amax = torch.zeros(1, dtype=torch.float32, device=DEV)
+    h = L.w4a4_grouped_gemm_rac(_nv(*a), _nv(*w), _dev(off), epilogue=L.NVFP4_EPI_SILU_MUL_BF16,
+                                out_amax=amax, out_y=out_y, **kw)
+    y = host(out_y)
+    assert np.isfinite(y).all(), "every output row written"
+    err = rel_frob(y, y_ref)
+    say(f"  gate/up FP32 rel frob {err:.3e}")
+    assert err <= REL_F
+    amax_ref = _check_h(host(h.view(torch.int16)).view(np.uint16), y_ref, y, N // 2, "gate/up")
+    assert abs(host(amax)[0] - amax_ref) <= amax_ref * 2.0 ** -7
