@@ -208,7 +208,14 @@ __device__ __forceinline__ void nv_decode8(uint32_t w, float* g) {
 //    contiguous range of tile indices, so consecutive tiles run on one XCD
 //    and share its L2; workgroups past their XCD's share exit.
 //  * Inside a group the m-tiles vary fastest: the workgroups that read one W
-//    tile (one n-tile of one group) are adjacent.
+//    tile (one n-tile of one group) are adjacent.  With BAND_M > 0 they vary
+//    fastest in bands of at most BAND_M m-tiles, each band running through
+//    every n-tile before the next starts.  A group of at most BAND_M m-tiles
+//    keeps the plain order; in a long group (a dense GEMM) the tiles an XCD
+//    runs at once then cover a few m-tiles by a few n-tiles and share both
+//    their A and their W tiles in its L2, where the plain order has them all
+//    read one W tile and each its own A tile, streaming A from HBM once per
+//    n-tile.
 //  * A second wave scan finds the group of the tile; every wave of the
 //    workgroup computes the same result.
 struct NvTile {
@@ -219,6 +226,7 @@ __device__ __forceinline__ int nv_group_tiles(const int32_t* offsets, int G, int
   return g < G ? (offsets[g + 1] - offsets[g] + bm - 1) / bm : 0;
 }
 
+template <int BAND_M = 0>
 __device__ __forceinline__ NvTile nv_find_tile(const int32_t* offsets, int G, int bm,
                                                int m_slots, int n_tiles) {
   (void)m_slots;
@@ -254,10 +262,18 @@ __device__ __forceinline__ NvTile nv_find_tile(const int32_t* offsets, int G, in
       const int hl = __ffsll((long long)bal) - 1;
       const int first = run + __shfl(excl, hl, 64);
       const int gt = __shfl(tiles, hl, 64);
-      const int i = L - first * n_tiles;
+      const int i = L - first * n_tiles;  // tile inside the group
       t.grp = c + hl;
-      t.local = i % gt;
-      t.nt = i / gt;
+      if constexpr (BAND_M > 0) {
+        const int band = i / (BAND_M * n_tiles);
+        const int gm = min(BAND_M, gt - band * BAND_M);  // m-tiles of the band
+        const int j = i - band * BAND_M * n_tiles;
+        t.local = band * BAND_M + j % gm;
+        t.nt = j / gm;
+      } else {
+        t.local = i % gt;
+        t.nt = i / gt;
+      }
       return t;
     }
     run += __shfl(inc, 63, 64);

@@ -209,7 +209,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void k_fp8_gemm(F8Par
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int lr = lane & 31, lh = lane >> 5;
 
-  const NvTile tile = nv_find_tile(p.offsets, p.G, BM, p.m_slots, p.n_tiles);
+  // long groups in bands of 8 m-tiles (a dense GEMM shares A and W in L2)
+  const NvTile tile = nv_find_tile<8>(p.offsets, p.G, BM, p.m_slots, p.n_tiles);
   if (tile.grp < 0) return;  // wave-uniform and identical in every wave
   const int grp = tile.grp, nt = tile.nt;
   const int row_beg = p.offsets[grp] + tile.local * BM;

@@ -59,6 +59,8 @@ def _weights(orc, rng, G, N, K):
 
 
 def _offsets(rng, G, mean):
+    if mean < 0:                                 # exactly -mean rows per group
+        return np.concatenate([[0], np.cumsum(np.full(G, -mean))]).astype(np.int32)
     sizes = rng.integers(0, 2 * mean + 1, G)
     if G > 2:
         sizes[1] = 0                             # an empty group
@@ -141,6 +143,8 @@ def _run(orc, seed, G, N, K, mean_rows, src_rows, gather, silu):
     (3, 3, 384, 128, 40, 64, True, True),         # SiLU on 128 x 128 tiles, one chunk
     (4, 6, 512, 1024, 100, 500, True, False),     # several chunks and m-tiles per group
     (5, 2, 256, 2048, 1, 4, False, False),        # one-row groups
+    (6, 1, 512, 256, -2300, 2300, False, False),  # one long group: 9 m-tiles, bands of 8, tail
+    (7, 1, 384, 128, -2500, 2600, True, False),   # 20 m-tiles of 128 rows: three bands
 ])
 def test_fp8_gemm_parity(orc, seed, G, N, K, mean_rows, src_rows, gather, silu):
     say(f"fp8 gemm seed={seed} G={G} N={N} K={K} rows~{mean_rows} gather={gather} silu={silu}")
