@@ -145,16 +145,27 @@ def moe_block(x: torch.Tensor, logits: torch.Tensor, wgu: QuantWeights, wd: Quan
 
 class GraphedMoEBlock:
     """moe_block captured once as a HIP graph (torch.cuda.CUDAGraph) for fixed
-    T, H, E.  A call copies the inputs into the graph's static buffers and
-    replays it; the returned tensor is the graph's static output, overwritten
-    by the next call.  Every kernel of the block only reads device memory the
-    graph owns or the caller's weights, and nothing in it is a memset node."""
+    T, H, E.  The graph reads its inputs from two static buffers: its own, or
+    the caller's x [T, H] and logits [T, E] when given (a producer that writes
+    the next step's inputs there lets a call replay with no copy).  A call
+    copies inputs that live elsewhere into those buffers and replays; the
+    returned tensor is the graph's static output, overwritten by the next
+    call.  Every kernel of the block only reads device memory the graph owns,
+    the static inputs or the caller's weights, and nothing in it is a memset
+    node."""
 
     def __init__(self, wgu: QuantWeights, wd: QuantWeights, topk: int, n_sel_x: Optional[int],
                  n_sel_h: Optional[int], T: int, E: int, x_dtype: torch.dtype, device,
-                 out_dtype: torch.dtype = torch.bfloat16, warmup: int = 2):
-        self.x = torch.zeros((T, wgu.K), dtype=x_dtype, device=device)
-        self.logits = torch.zeros((T, E), dtype=torch.float32, device=device)
+                 out_dtype: torch.dtype = torch.bfloat16, warmup: int = 2,
+                 x: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None):
+        if x is not None:
+            assert x.shape == (T, wgu.K) and x.dtype == x_dtype and x.is_contiguous()
+        if logits is not None:
+            assert logits.shape == (T, E) and logits.dtype == torch.float32
+            assert logits.is_contiguous()
+        self.x = x if x is not None else torch.zeros((T, wgu.K), dtype=x_dtype, device=device)
+        self.logits = (logits if logits is not None
+                       else torch.zeros((T, E), dtype=torch.float32, device=device))
         args = (wgu, wd, topk, n_sel_x, n_sel_h, out_dtype)
         side = torch.cuda.Stream(device)
         side.wait_stream(torch.cuda.current_stream(device))
@@ -166,9 +177,12 @@ class GraphedMoEBlock:
         with torch.cuda.graph(self.graph):
             self.out = moe_block(self.x, self.logits, *args)["out"]
 
-    def __call__(self, x: torch.Tensor, logits: torch.Tensor) -> torch.Tensor:
-        self.x.copy_(x)
-        self.logits.copy_(logits)
+    def __call__(self, x: Optional[torch.Tensor] = None,
+                 logits: Optional[torch.Tensor] = None) -> torch.Tensor:
+        if x is not None and x.data_ptr() != self.x.data_ptr():
+            self.x.copy_(x)
+        if logits is not None and logits.data_ptr() != self.logits.data_ptr():
+            self.logits.copy_(logits)
         self.graph.replay()
         return self.out
 

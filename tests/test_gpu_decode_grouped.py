@@ -6,8 +6,9 @@ on oracle-quantized operands.  FP32 outputs within relative Frobenius 1e-5;
 with SiLU*mul, the FP32 gate/up side output within 1e-5, H within the
 propagated one-ulp bound and max|H| within one bf16 ulp of the oracle's.
 The cases cover empty groups, a group longer than one 16-row tile, a row
-gather, RAC off, per-group tensor scales, and K from 512 (one chunk) to
-12288, with odd chunk counts."""
+gather, RAC off, per-group tensor scales, K from 512 (two 256-k chunks) to
+12288 with odd chunk counts, and grids of many groups with more workgroups
+than the chip holds at once."""
 import numpy as np
 import pytest
 import torch
@@ -46,6 +47,10 @@ CASES = [  # (seed, group sizes, K, N, rac, silu, gather source rows, per-group 
     (8, [1, 0, 3, 2, 0, 1, 1, 0, 4, 1], 1536, 384, True, True, 12, False),
     (9, [2, 1, 0, 1], 512, 128, True, False, None, False),
     (10, [1, 1, 0, 2, 1, 0, 0, 3], 2560, 256, False, False, 7, True),
+    # many groups, more workgroups than the chip holds at once (K = 512: two
+    # chunks per workgroup)
+    (11, [1, 2, 0, 3, 1, 2, 1, 1] * 12, 1024, 2048, True, True, 150, False),
+    (12, [2, 1, 1, 3, 0, 1, 2, 1] * 16, 512, 2048, True, False, None, False),
 ]
 
 

@@ -66,6 +66,29 @@ def test_graphed_block_matches_eager(orc):
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
 
 
+def test_graphed_block_on_caller_buffers(orc):
+    """Captured on the caller's own input buffers, a replay reads whatever the
+    caller last wrote there: no copies, same bits as the eager block."""
+    say("graph-captured MoE block on caller-owned inputs")
+    wgu, wd, inputs, c = _small_block(23)
+    args = (wgu, wd, c["k"], c["H"] // 2, c["I"] // 2)
+    xs = torch.zeros((c["T"], c["H"]), dtype=torch.bfloat16, device=DEV)
+    ls = torch.zeros((c["T"], c["E"]), dtype=torch.float32, device=DEV)
+    g = P.GraphedMoEBlock(*args, T=c["T"], E=c["E"], x_dtype=torch.bfloat16, device=DEV,
+                          x=xs, logits=ls)
+    assert g.x.data_ptr() == xs.data_ptr() and g.logits.data_ptr() == ls.data_ptr()
+    for rep, seed in enumerate([4, 5, 4]):
+        x, lg = inputs(seed)
+        xs.copy_(x)
+        ls.copy_(lg)
+        ref = P.moe_block(xs, ls, *args)["out"].clone()
+        _ = P.moe_block(*inputs(200 + rep), *args)
+        torch.cuda.synchronize()
+        out = g()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
+
+
 def test_moe_block_combines_grouped_rows(orc):
     """The block's output is the combine of its own grouped down-projection
     rows (checked against the oracle's combine on those rows read back)."""
