@@ -86,15 +86,18 @@ const char* nvfp4_status_string(int status);
  * amax_in  nullable device float: the tensor amax to use instead of max|x|
  *          (a producer that already knows it, e.g. the SiLU*mul epilogue).
  * codes    out [rows, K/2];  scales out [rows, K/16];  tensor_scale out [1].
- * channel_score, channel_max  nullable pair (both or neither).  When given,
- *          the RAC per-channel error statistics are computed in the same pass
- *          over x:  e = x - deq(q(x)) in FP32;  with Es the exponent of s_t
- *          (s_t = f 2^Es, f in [0.5, 1)) and q = min(floor(|e| 2^(8-Es)),
- *          2^17 - 1):  channel_score[k] = sum over rows of q^2 (int64, exact)
- *          and channel_max[k] = max over rows of |e| (float).  They feed
- *          rac_select_residual.  (Blog, "Two fixes": channels ranked by
- *          quantization error; the metric is this library's reading: the
- *          sum of squared errors, in fixed point so that it is exact.)
+ * channel_score  nullable.  When given, the RAC per-channel error statistics
+ *          are computed in the same pass over x:  e = x - deq(q(x)) in FP32;
+ *          with Es the exponent of s_t (s_t = f 2^Es, f in [0.5, 1)) and
+ *          q = min(floor(|e| 2^(8-Es)), 2^17 - 1):  channel_score[k] = sum
+ *          over rows of q^2 (int64, exact).  It feeds rac_select_residual.
+ *          (Blog, "Two fixes": channels ranked by quantization error; the
+ *          metric is this library's reading: the sum of squared errors, in
+ *          fixed point so that it is exact.)
+ * channel_max  nullable; requires channel_score.  When given, also
+ *          channel_max[k] = max over rows of |e| (float), a diagnostic the
+ *          selection does not read; leaving it NULL saves its arithmetic and
+ *          atomics (about a tenth of the call).
  * rows == 0 is allowed (writes s_t = RN32(amax_in/2688) or 0, and zero stats).
  * ------------------------------------------------------------------------ */
 size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t K);
@@ -144,8 +147,8 @@ int rac_select_residual(const void* x, int dtype, int64_t rows, int64_t K, int64
  * rac_select_residual, in one call that allocates nothing and takes no
  * workspace: for callers that cannot allocate (code under HIP graph capture,
  * tight serving loops, harnesses that forbid allocation).  Arguments and
- * results are those of the two calls (channel_score and channel_max are
- * required).  Scratch (6 KiB: amax partials and block masks) lives in a
+ * results are those of the two calls (channel_score is required,
+ * channel_max may be NULL).  Scratch (6 KiB: amax partials and block masks) lives in a
  * device array of the library, one per GPU, held until the process ends; its
  * address is looked up on the first call on each device (which must be the
  * current device, the stream's device).  Every call on a GPU shares that
@@ -196,8 +199,8 @@ int moe_route(const float* logits, int64_t T, int64_t E, int64_t k,
  * that tensor.  Outputs are in grouped row order: codes / res_codes
  * [total_rows, K/2], scales / res_scales [total_rows, K/16]; per group:
  * tensor_scales / res_tensor_scales [G], channel_score [G, K] (int64),
- * channel_max [G, K], selected [G, n_select] (ascending per group),
- * kblock_active [G, K/16].  The GEMM then runs without a gather, with
+ * channel_max [G, K] (nullable, requires channel_score), selected
+ * [G, n_select] (ascending per group), kblock_active [G, K/16].  The GEMM then runs without a gather, with
  * NVFP4_GEMM_PER_GROUP_SCALES.  Requires 1 <= G <= 65535, K % 16 == 0,
  * total_rows * K / 16 < 2^31, x 16-byte aligned, ldx % 16 == 0; the
  * selection needs K <= 16384.  Empty groups get zero tensor scales and the

@@ -163,8 +163,10 @@ class RouteOut(NamedTuple):
 
 
 def nvfp4_quantize(x: torch.Tensor, *, amax_in: Optional[torch.Tensor] = None,
-                   stats: bool = False) -> QuantOut:
-    """NVFP4-quantize a 2-D bf16/fp32 device tensor (row stride honoured)."""
+                   stats: bool = False, channel_max: bool = True) -> QuantOut:
+    """NVFP4-quantize a 2-D bf16/fp32 device tensor (row stride honoured).
+    stats: the RAC channel scores; channel_max (with stats): also max|e| per
+    channel, which the selection does not need."""
     assert x.dim() == 2 and x.stride(1) == 1
     rows, K = x.shape
     dev = x.device
@@ -172,7 +174,7 @@ def nvfp4_quantize(x: torch.Tensor, *, amax_in: Optional[torch.Tensor] = None,
     scales = torch.empty((rows, K // 16), dtype=torch.uint8, device=dev)
     ts = torch.empty(1, dtype=torch.float32, device=dev)
     score = torch.empty(K, dtype=torch.int64, device=dev) if stats else None
-    chmax = torch.empty(K, dtype=torch.float32, device=dev) if stats else None
+    chmax = torch.empty(K, dtype=torch.float32, device=dev) if stats and channel_max else None
     L = lib()
     ws = _ws(L.nvfp4_quantize_workspace_size(rows, K), dev)
     _check(L.nvfp4_quantize(_ptr(x), _dtype_code(x), rows, K, x.stride(0), _ptr(amax_in),
@@ -202,7 +204,7 @@ def rac_select_residual(x: torch.Tensor, qo: QuantOut, n_select: int) -> RacOut:
 
 
 def nvfp4_quantize_rac_static(x: torch.Tensor, n_select: int, *,
-                              amax_in: Optional[torch.Tensor] = None):
+                              amax_in: Optional[torch.Tensor] = None, channel_max: bool = True):
     """nvfp4_quantize (with statistics) + rac_select_residual in one call that
     takes no workspace (the library's per-device scratch).  Returns
     (QuantOut, RacOut)."""
@@ -213,7 +215,7 @@ def nvfp4_quantize_rac_static(x: torch.Tensor, n_select: int, *,
     scales = torch.empty((rows, K // 16), dtype=torch.uint8, device=dev)
     ts = torch.empty(1, dtype=torch.float32, device=dev)
     score = torch.empty(K, dtype=torch.int64, device=dev)
-    chmax = torch.empty(K, dtype=torch.float32, device=dev)
+    chmax = torch.empty(K, dtype=torch.float32, device=dev) if channel_max else None
     sel = torch.empty(max(n_select, 1), dtype=torch.int32, device=dev)[:n_select]
     kact = torch.empty(K // 16, dtype=torch.uint8, device=dev)
     rc = torch.empty((rows, K // 2), dtype=torch.uint8, device=dev)
@@ -229,7 +231,7 @@ def nvfp4_quantize_rac_static(x: torch.Tensor, n_select: int, *,
 
 def nvfp4_quantize_grouped(x: torch.Tensor, group_offsets: torch.Tensor, total_rows: int, *,
                            gather_rows: Optional[torch.Tensor] = None,
-                           stats: bool = False) -> QuantOut:
+                           stats: bool = False, channel_max: bool = True) -> QuantOut:
     """Per-expert quantization: each group's rows (x[gather[j]] or x[j]) as
     their own tensor.  Returns grouped-order codes/scales, tscale [G] and, with
     stats, score [G, K] and channel max [G, K]."""
@@ -241,7 +243,8 @@ def nvfp4_quantize_grouped(x: torch.Tensor, group_offsets: torch.Tensor, total_r
     scales = torch.empty((total_rows, K // 16), dtype=torch.uint8, device=dev)
     ts = torch.empty(G, dtype=torch.float32, device=dev)
     score = torch.empty((G, K), dtype=torch.int64, device=dev) if stats else None
-    chmax = torch.empty((G, K), dtype=torch.float32, device=dev) if stats else None
+    chmax = (torch.empty((G, K), dtype=torch.float32, device=dev) if stats and channel_max
+             else None)
     L = lib()
     ws = _ws(L.nvfp4_quantize_grouped_workspace_size(G, K), dev)
     _check(L.nvfp4_quantize_grouped(_ptr(x), _dtype_code(x), K, x.stride(0), _ptr(group_offsets),

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void k_amax(const void* __restrict__ x, i
   if (score) {
     for (int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x; k < K; k += stride) {
       score[k] = 0;
-      chmax[k] = 0u;
+      if (chmax) chmax[k] = 0u;
     }
   }
   __shared__ float red[kThreads / 64];
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void k_amax_grouped(
     const int64_t wg = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
     for (int64_t k = wg * kThreads + threadIdx.x; k < (int64_t)G * K; k += nwg * kThreads) {
       score[k] = 0;
-      chmax[k] = 0u;
+      if (chmax) chmax[k] = 0u;
     }
   }
   __shared__ float red[kThreads / 64];
@@ -113,7 +113,7 @@ __global__ void k_zero_stats(int64_t K, int64_t* __restrict__ score, uint32_t* _
   for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < K;
        k += (int64_t)gridDim.x * blockDim.x) {
     score[k] = 0;
-    chmax[k] = 0u;
+    if (chmax) chmax[k] = 0u;
   }
 }
 
@@ -202,7 +202,9 @@ __device__ __forceinline__ void dq_store16(void* out, int64_t o, uint32_t lo, ui
 // kDq 0: codes and block scales.  kDq 1 / 2: the dequantized values instead
 // (FP32 / bf16, row stride K) -- the trainer's weight fake-quantization runs
 // the same quantizer and stores what the rollout's dequantization would give.
-template <bool kStats, bool kBf16, int kDq = 0>
+// kMax: with the statistics, also the per-channel max|e| (the selection does
+// not read it; without it the kernel saves its arithmetic and atomics).
+template <bool kStats, bool kBf16, int kDq = 0, bool kMax = true>
 __global__ __launch_bounds__(kQThreads) void k_quant(
     const void* __restrict__ x, int64_t rows, int64_t K, int64_t ldx,
     const float* __restrict__ partials, int nparts, const float* __restrict__ amax_in,
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant(
     tscale_out += g;
     if (kStats) {
       score += (int64_t)g * K;
-      chmax += (int64_t)g * K;
+      if (kMax) chmax += (int64_t)g * K;
     }
     rows_per_split = (rows + gridDim.y - 1) / gridDim.y;
   }
@@ -274,7 +276,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant(
         const float e = v[i] - (g[i] * sb) * s_t;
         const uint32_t q = nv_score_qi(e, shift);
         acc[i] += (uint64_t)q * q;
-        emax[i] = __builtin_fmaxf(emax[i], __builtin_fabsf(e));
+        if constexpr (kMax) emax[i] = __builtin_fmaxf(emax[i], __builtin_fabsf(e));
       }
     }
     if constexpr (kDq == 0) {
@@ -308,17 +310,19 @@ __global__ __launch_bounds__(kQThreads) void k_quant(
     // major), so the lanes of a wave, which hold consecutive column blocks,
     // hit consecutive words and the atomics are free of bank conflicts.
     unsigned long long* lsum = reinterpret_cast<unsigned long long*>(dyn_lds);
-    uint32_t* lmax = reinterpret_cast<uint32_t*>(lsum + tpr * 16);
+    uint32_t* lmax = reinterpret_cast<uint32_t*>(lsum + tpr * 16);  // kMax only
     for (int i = threadIdx.x; i < tpr * 16; i += kQThreads) {
       lsum[i] = 0ull;
-      lmax[i] = 0u;
+      if constexpr (kMax) lmax[i] = 0u;
     }
     __syncthreads();
     if (active) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if (acc[i] != 0u) atomicAdd(&lsum[i * tpr + cbl], (unsigned long long)acc[i]);
-        if (emax[i] != 0.0f) atomicMax(&lmax[i * tpr + cbl], __float_as_uint(emax[i]));
+        if constexpr (kMax) {
+          if (emax[i] != 0.0f) atomicMax(&lmax[i * tpr + cbl], __float_as_uint(emax[i]));
+        }
       }
     }
     __syncthreads();
@@ -327,7 +331,9 @@ __global__ __launch_bounds__(kQThreads) void k_quant(
       const int64_t k = ((int64_t)blockIdx.x * tpr + j % tpr) * 16 + j / tpr;
       if (k < K) {
         if (lsum[j]) atomicAdd(reinterpret_cast<unsigned long long*>(score) + k, lsum[j]);
-        if (lmax[j]) atomicMax(chmax + k, lmax[j]);
+        if constexpr (kMax) {
+          if (lmax[j]) atomicMax(chmax + k, lmax[j]);
+        }
       }
     }
   }
@@ -701,7 +707,8 @@ static int quantize_launch(const void* x, int dtype, int64_t rows, int64_t K, in
                            float* tensor_scale, int64_t* channel_score, float* channel_max,
                            void* ws, int dq, void* dq_out, hipStream_t s) {
   const bool stats = channel_score != nullptr;
-  uint32_t* chm = reinterpret_cast<uint32_t*>(channel_max);
+  uint32_t* chm = reinterpret_cast<uint32_t*>(channel_max);  // nullable with stats
+  const bool cmax = stats && chm != nullptr;
   float* partials = reinterpret_cast<float*>(ws);
   const int bf16 = dtype == NVFP4_IN_BF16;
   const int64_t CB = K / 16;
@@ -729,14 +736,15 @@ static int quantize_launch(const void* x, int dtype, int64_t rows, int64_t K, in
   const int64_t max_splits = stats ? (wg_target / ntile > 0 ? wg_target / ntile : 1) : 65535;
   if (splits > max_splits) splits = max_splits;
   const int64_t rows_per_split = rows > 0 ? (rows + splits - 1) / splits : 1;
-  const size_t lds = stats ? (size_t)tpr * 16 * (sizeof(uint64_t) + sizeof(uint32_t)) : 0;
+  const size_t lds =
+      stats ? (size_t)tpr * 16 * (sizeof(uint64_t) + (cmax ? sizeof(uint32_t) : 0)) : 0;
   const dim3 grid((unsigned)ntile, (unsigned)splits);
   int64_t* sc = stats ? channel_score : nullptr;
-  uint32_t* cm = stats ? chm : nullptr;
-#define NV_QUANT_LAUNCH(ST, BF)                                                                 \
-  hipLaunchKernelGGL((k_quant<ST, BF>), grid, dim3(kQThreads), ST ? lds : 0, s, x, rows, K, ldx, \
-                     partials, nparts, amax_in, codes, scales, tensor_scale, sc, cm, tpr, rpi,   \
-                     rows_per_split, nullptr, nullptr, nullptr)
+  uint32_t* cm = cmax ? chm : nullptr;
+#define NV_QUANT_LAUNCH(ST, BF, MX)                                                              \
+  hipLaunchKernelGGL((k_quant<ST, BF, 0, MX>), grid, dim3(kQThreads), ST ? lds : 0, s, x, rows, K, \
+                     ldx, partials, nparts, amax_in, codes, scales, tensor_scale, sc, cm, tpr,    \
+                     rpi, rows_per_split, nullptr, nullptr, nullptr)
 #define NV_QUANT_LAUNCH_DQ(DQ, BF)                                                              \
   hipLaunchKernelGGL((k_quant<false, BF, DQ>), grid, dim3(kQThreads), 0, s, x, rows, K, ldx,    \
                      partials, nparts, amax_in, nullptr, nullptr, tensor_scale, nullptr, nullptr, \
@@ -745,10 +753,12 @@ static int quantize_launch(const void* x, int dtype, int64_t rows, int64_t K, in
   else if (dq == 1) NV_QUANT_LAUNCH_DQ(1, false);
   else if (dq == 2 && bf16) NV_QUANT_LAUNCH_DQ(2, true);
   else if (dq == 2) NV_QUANT_LAUNCH_DQ(2, false);
-  else if (stats && bf16) NV_QUANT_LAUNCH(true, true);
-  else if (stats) NV_QUANT_LAUNCH(true, false);
-  else if (bf16) NV_QUANT_LAUNCH(false, true);
-  else NV_QUANT_LAUNCH(false, false);
+  else if (cmax && bf16) NV_QUANT_LAUNCH(true, true, true);
+  else if (cmax) NV_QUANT_LAUNCH(true, false, true);
+  else if (stats && bf16) NV_QUANT_LAUNCH(true, true, false);
+  else if (stats) NV_QUANT_LAUNCH(true, false, false);
+  else if (bf16) NV_QUANT_LAUNCH(false, true, false);
+  else NV_QUANT_LAUNCH(false, false, false);
 #undef NV_QUANT_LAUNCH
 #undef NV_QUANT_LAUNCH_DQ
   return nv_launch_status();
@@ -779,10 +789,10 @@ int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ld
   int st = check_x(x, dtype, rows, K, ldx);
   if (st) return st;
   NV_RETURN_IF(!tensor_scale || (rows > 0 && (!codes || !scales)), NVFP4_ERR_NULL);
-  NV_RETURN_IF((channel_score == nullptr) != (channel_max == nullptr), NVFP4_ERR_NULL);
+  NV_RETURN_IF(channel_max && !channel_score, NVFP4_ERR_NULL);
   NV_RETURN_IF(!nv_aligned16(codes), NVFP4_ERR_ALIGN);
-  NV_RETURN_IF(channel_score && ((reinterpret_cast<uintptr_t>(channel_score) & 7) ||
-                                 (reinterpret_cast<uintptr_t>(channel_max) & 3)),
+  NV_RETURN_IF((reinterpret_cast<uintptr_t>(channel_score) & 7) ||
+                   (reinterpret_cast<uintptr_t>(channel_max) & 3),
                NVFP4_ERR_ALIGN);
   NV_RETURN_IF(!amax_in && (!ws || ws_bytes < nvfp4_quantize_workspace_size(rows, K)),
                NVFP4_ERR_WORKSPACE);
@@ -918,8 +928,8 @@ extern "C" int nvfp4_quantize_rac_static(
   int st = check_x(x, dtype, rows, K, ldx);
   if (st) return st;
   NV_RETURN_IF(K > kMaxSelectK || n_select < 0 || n_select > K, NVFP4_ERR_SHAPE);
-  NV_RETURN_IF(!tensor_scale || !channel_score || !channel_max || !kblock_active ||
-                   !res_tensor_scale || (n_select > 0 && !selected),
+  NV_RETURN_IF(!tensor_scale || !channel_score || !kblock_active || !res_tensor_scale ||
+                   (n_select > 0 && !selected),
                NVFP4_ERR_NULL);
   NV_RETURN_IF(rows > 0 && (!codes || !scales || !res_codes || !res_scales), NVFP4_ERR_NULL);
   NV_RETURN_IF(!nv_aligned16(codes) || !nv_aligned16(res_codes) ||
@@ -964,16 +974,16 @@ int nvfp4_quantize_grouped(const void* x, int dtype, int64_t K, int64_t ldx,
   int st = check_grouped(x, dtype, K, ldx, group_offsets, G, total_rows);
   if (st) return st;
   NV_RETURN_IF(!tensor_scales || (total_rows > 0 && (!codes || !scales)), NVFP4_ERR_NULL);
-  NV_RETURN_IF((channel_score == nullptr) != (channel_max == nullptr), NVFP4_ERR_NULL);
-  NV_RETURN_IF(!nv_aligned16(codes) ||
-                   (channel_score && ((reinterpret_cast<uintptr_t>(channel_score) & 7) ||
-                                      (reinterpret_cast<uintptr_t>(channel_max) & 3))),
+  NV_RETURN_IF(channel_max && !channel_score, NVFP4_ERR_NULL);
+  NV_RETURN_IF(!nv_aligned16(codes) || (reinterpret_cast<uintptr_t>(channel_score) & 7) ||
+                   (reinterpret_cast<uintptr_t>(channel_max) & 3),
                NVFP4_ERR_ALIGN);
   NV_RETURN_IF(!ws || ws_bytes < nvfp4_quantize_grouped_workspace_size(G, K),
                NVFP4_ERR_WORKSPACE);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool stats = channel_score != nullptr;
-  uint32_t* chm = reinterpret_cast<uint32_t*>(channel_max);
+  uint32_t* chm = reinterpret_cast<uint32_t*>(channel_max);  // nullable with stats
+  const bool cmax = stats && chm != nullptr;
   float* partials = reinterpret_cast<float*>(ws);
   const int bf16 = dtype == NVFP4_IN_BF16;
   hipLaunchKernelGGL(k_amax_grouped, dim3(kGroupParts, (unsigned)G), dim3(kThreads), 0, s, x,
@@ -986,18 +996,22 @@ int nvfp4_quantize_grouped(const void* x, int dtype, int64_t K, int64_t ldx,
   const int tpr = (int)((CB + ntile - 1) / ntile);
   const int rpi = kQThreads / tpr;
   int64_t splits = blocks_for((total_rows + G - 1) / G, (int64_t)rpi * 2, 64);
-  const size_t lds = stats ? (size_t)tpr * 16 * (sizeof(uint64_t) + sizeof(uint32_t)) : 0;
+  const size_t lds =
+      stats ? (size_t)tpr * 16 * (sizeof(uint64_t) + (cmax ? sizeof(uint32_t) : 0)) : 0;
   const dim3 grid((unsigned)ntile, (unsigned)splits, (unsigned)G);
   int64_t* sc = stats ? channel_score : nullptr;
-  uint32_t* cm = stats ? chm : nullptr;
-#define NV_QUANT_LAUNCH_G(ST, BF)                                                                \
-  hipLaunchKernelGGL((k_quant<ST, BF>), grid, dim3(kQThreads), ST ? lds : 0, s, x, total_rows, K, \
-                     ldx, partials, kGroupParts, nullptr, codes, scales, tensor_scales, sc, cm,  \
-                     tpr, rpi, (int64_t)0, nullptr, group_offsets, gather_rows)
-  if (stats && bf16) NV_QUANT_LAUNCH_G(true, true);
-  else if (stats) NV_QUANT_LAUNCH_G(true, false);
-  else if (bf16) NV_QUANT_LAUNCH_G(false, true);
-  else NV_QUANT_LAUNCH_G(false, false);
+  uint32_t* cm = cmax ? chm : nullptr;
+#define NV_QUANT_LAUNCH_G(ST, BF, MX)                                                            \
+  hipLaunchKernelGGL((k_quant<ST, BF, 0, MX>), grid, dim3(kQThreads), ST ? lds : 0, s, x,        \
+                     total_rows, K, ldx, partials, kGroupParts, nullptr, codes, scales,          \
+                     tensor_scales, sc, cm, tpr, rpi, (int64_t)0, nullptr, group_offsets,        \
+                     gather_rows)
+  if (cmax && bf16) NV_QUANT_LAUNCH_G(true, true, true);
+  else if (cmax) NV_QUANT_LAUNCH_G(true, false, true);
+  else if (stats && bf16) NV_QUANT_LAUNCH_G(true, true, false);
+  else if (stats) NV_QUANT_LAUNCH_G(true, false, false);
+  else if (bf16) NV_QUANT_LAUNCH_G(false, true, false);
+  else NV_QUANT_LAUNCH_G(false, false, false);
 #undef NV_QUANT_LAUNCH_G
   return nv_launch_status();
 }

@@ -65,7 +65,7 @@ SKIP_BELOW_FRACTION = 1.0 / 8
 def quantize_input(x: torch.Tensor, n_select: Optional[int],
                    amax_in: Optional[torch.Tensor] = None) -> GemmInput:
     """Online quantization of a GEMM input; n_select None turns RAC off."""
-    qo = L.nvfp4_quantize(x, amax_in=amax_in, stats=n_select is not None)
+    qo = L.nvfp4_quantize(x, amax_in=amax_in, stats=n_select is not None, channel_max=False)
     rac = L.rac_select_residual(x, qo, n_select) if n_select is not None else None
     skip = n_select is not None and n_select <= SKIP_BELOW_FRACTION * x.shape[1]
     return GemmInput(qo, rac, skip)
@@ -78,7 +78,7 @@ def quantize_input_grouped(x: torch.Tensor, offsets: torch.Tensor, total_rows: i
     given) are quantized and compensated as their own tensor; the GEMM then
     runs on grouped rows without a gather."""
     qo = L.nvfp4_quantize_grouped(x, offsets, total_rows, gather_rows=gather,
-                                  stats=n_select is not None)
+                                  stats=n_select is not None, channel_max=False)
     rac = (L.rac_select_residual_grouped(x, qo, offsets, total_rows, n_select, gather_rows=gather)
            if n_select is not None else None)
     skip = n_select is not None and n_select <= SKIP_BELOW_FRACTION * x.shape[1]

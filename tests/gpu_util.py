@@ -74,4 +74,14 @@ def check_quant_rac(orc, x, dtype, n_select, amax=None, ldx_pad=0):
     eq(host(rac.r.tscale)[0], np.float32(d["s_tr"]), "residual tensor scale")
     eq(host(rac.r.scales), d["res_scales"], "residual scales")
     eq(host(rac.r.codes), d["res_codes"], "residual codes")
+    # the statistics without the channel maximum (the kernel variant the
+    # pipeline runs): the same scores, codes, selection and residual
+    qn = L.nvfp4_quantize(xd, amax_in=am, stats=True, channel_max=False)
+    assert qn.channel_max is None
+    rn = L.rac_select_residual(xd, qn, n_select)
+    eq(host(qn.q.codes), d["codes"], "codes (no channel max)")
+    eq(host(qn.q.scales), d["scales"], "block scales (no channel max)")
+    eq(host(qn.channel_score), d["score"], "channel score (no channel max)")
+    eq(host(rn.selected), d["selected"], "selected (no channel max)")
+    eq(host(rn.r.codes), d["res_codes"], "residual codes (no channel max)")
     return qo, rac, d

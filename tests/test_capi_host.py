@@ -44,6 +44,7 @@ def test_status_strings(lib):
 
 FAKE = ctypes.c_void_p(0x100000)      # 16-byte aligned, never dereferenced
 FAKE_MIS = ctypes.c_void_p(0x100004)  # misaligned
+FAKE_MIS2 = ctypes.c_void_p(0x100002)  # misaligned even for 4-byte elements
 
 
 def _q(lib, x=FAKE, dtype=1, rows=4, K=32, ldx=32, codes=FAKE, scales=FAKE, ts=FAKE,
@@ -55,7 +56,9 @@ def _q(lib, x=FAKE, dtype=1, rows=4, K=32, ldx=32, codes=FAKE, scales=FAKE, ts=F
 def test_quantize_validation(lib):
     assert _q(lib, x=None) == ENULL
     assert _q(lib, codes=None) == ENULL
-    assert _q(lib, score=FAKE) == ENULL            # score without chmax
+    assert _q(lib, chmax=FAKE) == ENULL            # chmax without score
+    assert _q(lib, score=FAKE, chmax=FAKE_MIS2) == EALIGN
+    assert _q(lib, score=FAKE_MIS) == EALIGN       # int64 scores: 8-byte aligned
     assert _q(lib, dtype=7) == EDTYPE
     assert _q(lib, K=24, ldx=32) == ESHAPE          # K % 16
     assert _q(lib, rows=-1) == ESHAPE
@@ -101,8 +104,9 @@ def test_static_quant_rac_validation(lib):
             a["rts"], None)
     assert call(K=16384 + 16, ldx=16384 + 16) == ESHAPE   # beyond the scratch's limit
     assert call(nsel=33) == ESHAPE
-    assert call(chmax=None) == ENULL
+    assert call(chmax=FAKE_MIS2) == EALIGN  # channel_max may be NULL, not misaligned
     assert call(score=None) == ENULL
+    assert call(score=None, chmax=None) == ENULL
     assert call(sel=None) == ENULL
     assert call(rc=None) == ENULL
     assert call(x=None) == ENULL
@@ -247,9 +251,9 @@ def test_combine_validation(lib):
 
 def test_grouped_rac_validation(lib):
     def q(x=FAKE, dt=1, K=32, ldx=32, off=FAKE, G=2, rows=8, codes=FAKE, ts=FAKE, ws=FAKE,
-          wsb=1 << 20):
+          wsb=1 << 20, score=None, chmax=None):
         return lib.nvfp4_quantize_grouped(x, dt, K, ldx, off, G, rows, None, codes, FAKE, ts,
-                                          None, None, ws, wsb, None)
+                                          score, chmax, ws, wsb, None)
     assert q(off=None) == ENULL
     assert q(ts=None) == ENULL
     assert q(G=0) == ESHAPE
@@ -258,6 +262,8 @@ def test_grouped_rac_validation(lib):
     assert q(dt=5) == EDTYPE
     assert q(x=FAKE_MIS) == EALIGN
     assert q(ws=None) == EWS
+    assert q(chmax=FAKE) == ENULL                   # channel_max needs channel_score
+    assert q(score=FAKE, chmax=FAKE_MIS2) == EALIGN
 
     def r(nsel=16, K=32, sel=FAKE, ws=FAKE, wsb=1 << 20, kact=FAKE):
         return lib.rac_select_residual_grouped(FAKE, 1, K, K, FAKE, 2, 8, None, FAKE, FAKE, FAKE,

@@ -66,6 +66,13 @@ def test_grouped_quant_rac_parity(orc, seed, sizes, K, src, n_sel, dtype):
     eq(host(rac.r.tscale), d["s_tr"], "residual tensor scales")
     eq(host(rac.r.scales), d["res_scales"], "residual scales")
     eq(host(rac.r.codes), d["res_codes"], "residual codes")
+    qn = L.nvfp4_quantize_grouped(xd, od, total, gather_rows=gd, stats=True, channel_max=False)
+    assert qn.channel_max is None
+    rn = L.rac_select_residual_grouped(xd, qn, od, total, n_sel, gather_rows=gd)
+    eq(host(qn.channel_score), d["score"], "channel scores (no channel max)")
+    eq(host(qn.q.codes), d["codes"], "codes (no channel max)")
+    eq(host(rn.selected), d["selected"], "selected (no channel max)")
+    eq(host(rn.r.codes), d["res_codes"], "residual codes (no channel max)")
 
 
 @pytest.mark.parametrize("silu,skip", [(False, False), (True, False), (False, True)])

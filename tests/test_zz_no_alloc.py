@@ -39,6 +39,16 @@ def _compare(x, n_sel, amax=None):
                        ("residual scales", rs.r.scales, ro.r.scales),
                        ("residual tensor scale", rs.r.tscale, ro.r.tscale)]:
         eq(host(a), host(b), name)
+    # channel_max NULL: the same results without the diagnostic maximum
+    qn, rn = L.nvfp4_quantize_rac_static(xd, n_sel, amax_in=am, channel_max=False)
+    torch.cuda.synchronize()
+    assert qn.channel_max is None
+    for name, a, b in [("codes", qn.q.codes, qo.q.codes),
+                       ("channel score", qn.channel_score, qo.channel_score),
+                       ("selected", rn.selected, ro.selected),
+                       ("residual codes", rn.r.codes, ro.r.codes),
+                       ("residual scales", rn.r.scales, ro.r.scales)]:
+        eq(host(a), host(b), name + " (no channel max)")
 
 
 def test_static_quant_rac_two_calls():
