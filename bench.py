@@ -584,8 +584,11 @@ def dense_graph(w, dev, x, wq, nsx, flops):
 def library_fp8_reference(w, dev):
     """hipBLASLt's FP8 GEMM (torch._scaled_mm with per-row and per-column
     scales, bf16 output) on the dense shape rows x N x K of each GEMM of the
-    workload: no grouping, no gather, one weight matrix."""
+    workload: no grouping, no gather, one weight matrix.  Beside it, this
+    library's FP8 GEMM on the same operands with the same output type (one
+    group, bf16 epilogue): the like-for-like kernel ratio."""
     import torch
+    from nvfp4_w4a4_moe_quant_amd import _lib as L
     shapes = ([("gate_up", w.T * w.topk, 2 * w.I, w.H), ("down", w.T * w.topk, w.H, w.I)]
               if w.kind == "moe" else [("gemm", w.rows, w.N, w.K)])
     out = {}
@@ -610,6 +613,24 @@ def library_fp8_reference(w, dev):
                              tflops=round(2.0 * M * N * K / us / 1e6, 1))
         except Exception as ex:  # the library may lack a kernel for the shape
             out[name] = dict(shape=[M, N, K], error=repr(ex)[:200])
+            continue
+        A = L.FP8(a.view(torch.uint8), sa.reshape(M))
+        Wt = L.FP8(b.view(torch.uint8).reshape(1, N, K), sb.reshape(1, N))
+        off = torch.tensor([0, M], dtype=torch.int32, device=dev)
+        yb = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ours = lambda: L.fp8_grouped_gemm(A, Wt, off, N=N, K=K, total_rows=M,
+                                          epilogue=L.NVFP4_EPI_BF16, out=yb)
+        for _ in range(3):
+            ours()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(20):
+            ours()
+        e1.record()
+        torch.cuda.synchronize()
+        ous = e0.elapsed_time(e1) / 20 * 1e3
+        out[name].update(this_library_dense_bf16_us=round(ous, 1),
+                         this_library_dense_over_library=round(ous / us, 3))
     return out
 
 

@@ -69,8 +69,10 @@ typedef enum {
 typedef enum { NVFP4_IN_F32 = 0, NVFP4_IN_BF16 = 1 } nvfp4_in_dtype_t;
 
 typedef enum {
-  NVFP4_EPI_F32 = 0,          /* out: float [total_rows, N] */
-  NVFP4_EPI_SILU_MUL_BF16 = 1 /* out: bf16 [total_rows, N/2], h = silu(gate) * up */
+  NVFP4_EPI_F32 = 0,           /* out: float [total_rows, N] */
+  NVFP4_EPI_SILU_MUL_BF16 = 1, /* out: bf16 [total_rows, N/2], h = silu(gate) * up */
+  NVFP4_EPI_BF16 = 2           /* out: bf16 [total_rows, N], y rounded to nearest even
+                                  (fp8_grouped_gemm only) */
 } nvfp4_epilogue_t;
 
 /* Text for a status code (static storage). */
@@ -364,7 +366,9 @@ int fp8_quantize_rows(const void* x, int in_dtype, int64_t rows, int64_t K, uint
  *   y[j, n] = a_scales[src] * w_scales[g*N + n] * sum_k A[src,k] W_g[n,k]
  * with A, W the E4M3 values (products exact, FP32 accumulation).  Epilogue
  * SILU_MUL_BF16 writes h[j, i] = bf16(silu(y[j, i]) * y[j, I + i]) to out
- * [total_rows, I] (no amax: the FP8 quantizer scales per row).  Requires
+ * [total_rows, I] (no amax: the FP8 quantizer scales per row); epilogue
+ * BF16 writes bf16(y) to out [total_rows, N] (the output type of the vendor
+ * FP8 GEMM it is compared with).  Requires
  * K % 128 == 0, N % 128 == 0, codes 16-byte aligned, scales 4-byte aligned.
  * No workspace. */
 typedef struct {
@@ -379,7 +383,7 @@ typedef struct {
   const uint8_t* w_codes;       /* [G, N, K] E4M3 */
   const float* w_scales;        /* [G, N] */
   int64_t epilogue;             /* nvfp4_epilogue_t */
-  void* out;                    /* float [total_rows, N] or bf16 [total_rows, N/2] */
+  void* out;                    /* float or bf16 [total_rows, N], or bf16 [total_rows, N/2] */
 } fp8_gemm_args_t;
 
 int fp8_grouped_gemm(const fp8_gemm_args_t* args, void* stream);

@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnvfp4rac.so")
 
 NVFP4_IN_F32, NVFP4_IN_BF16 = 0, 1
-NVFP4_EPI_F32, NVFP4_EPI_SILU_MUL_BF16 = 0, 1
+NVFP4_EPI_F32, NVFP4_EPI_SILU_MUL_BF16, NVFP4_EPI_BF16 = 0, 1, 2
 NVFP4_GEMM_SKIP_INACTIVE_BLOCKS = 1
 NVFP4_GEMM_PER_GROUP_SCALES = 2
 
@@ -414,12 +414,14 @@ def fp8_grouped_gemm(a: FP8, w: FP8, group_offsets: torch.Tensor, *, N: int, K: 
                      total_rows: int, gather_rows: Optional[torch.Tensor] = None,
                      epilogue: int = NVFP4_EPI_F32,
                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """w: codes [G, N, K], scales [G, N]."""
+    """w: codes [G, N, K], scales [G, N].  epilogue F32, SILU_MUL_BF16 or BF16."""
     dev = a.codes.device
     G = group_offsets.numel() - 1
     if out is None:
         if epilogue == NVFP4_EPI_F32:
             out = torch.empty((total_rows, N), dtype=torch.float32, device=dev)
+        elif epilogue == NVFP4_EPI_BF16:
+            out = torch.empty((total_rows, N), dtype=torch.bfloat16, device=dev)
         else:
             out = torch.empty((total_rows, N // 2), dtype=torch.bfloat16, device=dev)
     args = Fp8GemmArgs(

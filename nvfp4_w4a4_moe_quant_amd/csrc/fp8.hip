@@ -29,6 +29,8 @@
 //    global->LDS copies (about 1.8 GB per call), not by the matrix cores;
 //    256 x 256 tiles of eight waves halve the copies per MFMA.
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace {
@@ -185,7 +187,7 @@ __device__ __forceinline__ float f8_silu_mul(float g, float u) {
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int MINW, bool SILU, bool GATHER,
-          int KC = KB>
+          int KC = KB, bool OUT_BF16 = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void k_fp8_gemm(F8Params p) {
   static_assert(KC == 64 || KC == 128, "64- or 128-byte chunks");
   constexpr int PPR = KC / 16;  // 16-byte pieces per row per chunk
@@ -332,7 +334,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void k_fp8_gemm(F8Par
   const float* sa = sc_lds + wm * WTM + lh * 4;
   const float* sw = sc_lds + BM + wn * WTN + lr;
   if constexpr (!SILU) {
-    float* ob = reinterpret_cast<float*>(p.out) + (int64_t)m0 * p.N + nt * BN + wn * WTN + lr;
+    using OutT = std::conditional_t<OUT_BF16, uint16_t, float>;
+    OutT* ob = reinterpret_cast<OutT*>(p.out) + (int64_t)m0 * p.N + nt * BN + wn * WTN + lr;
 #pragma unroll
     for (int a = 0; a < FM; ++a)
 #pragma unroll
@@ -341,7 +344,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void k_fp8_gemm(F8Par
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int dm = a * 32 + (e >> 2) * 8 + (e & 3);
-          if (full || m0 + dm < row_end) ob[(int64_t)dm * p.N + b * 32] = (sa[dm] * swb) * acc[a][b][e];
+          if (full || m0 + dm < row_end) {
+            const float y = (sa[dm] * swb) * acc[a][b][e];
+            if constexpr (OUT_BF16)
+              ob[(int64_t)dm * p.N + b * 32] = (uint16_t)nv_f32_to_bf16(y);
+            else
+              ob[(int64_t)dm * p.N + b * 32] = y;
+          }
         }
       }
   } else {
@@ -365,14 +374,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINW) void k_fp8_gemm(F8Par
   }
 }
 
-template <int BM, int BN, int WM, int WN, int NS, int MINW, bool SILU, bool GATHER, int KC = KB>
+template <int BM, int BN, int WM, int WN, int NS, int MINW, bool SILU, bool GATHER, int KC = KB,
+          bool OUT_BF16 = false>
 int launch_f8(F8Params& p, hipStream_t s) {
   if (p.N % BN) return NVFP4_ERR_SHAPE;
   p.m_slots = (p.total_rows + BM - 1) / BM + p.G;
   p.n_tiles = p.N / BN;
   const int64_t nb = (int64_t)p.m_slots * p.n_tiles;
   if (nb > 0x7fffffff) return NVFP4_ERR_SHAPE;
-  hipLaunchKernelGGL((k_fp8_gemm<BM, BN, WM, WN, NS, MINW, SILU, GATHER, KC>), dim3((unsigned)nb),
+  hipLaunchKernelGGL((k_fp8_gemm<BM, BN, WM, WN, NS, MINW, SILU, GATHER, KC, OUT_BF16>), dim3((unsigned)nb),
                      dim3(64 * WM * WN), 0, s, p);
   return nv_launch_status();
 }
@@ -381,10 +391,10 @@ int launch_f8(F8Params& p, hipStream_t s) {
 // workgroup per CU (twice the MFMAs per staged byte and per LDS fragment read
 // of 128 x 128 tiles with 64 x 64 waves, which were bound by the copies into
 // LDS).  Other N: 128 x 128 tiles (waves of 64 x 64), two workgroups per CU.
-template <bool SILU, bool GATHER>
+template <bool SILU, bool GATHER, bool OUT_BF16 = false>
 int launch_f8_cfg(F8Params& p, hipStream_t s) {
-  if (p.N % 256 == 0) return launch_f8<256, 256, 4, 2, 2, 1, SILU, GATHER>(p, s);
-  return launch_f8<128, 128, 2, 2, 2, 2, SILU, GATHER>(p, s);
+  if (p.N % 256 == 0) return launch_f8<256, 256, 4, 2, 2, 1, SILU, GATHER, KB, OUT_BF16>(p, s);
+  return launch_f8<128, 128, 2, 2, 2, 2, SILU, GATHER, KB, OUT_BF16>(p, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -490,7 +500,8 @@ int fp8_quantize_rows(const void* x, int in_dtype, int64_t rows, int64_t K, uint
 
 int fp8_grouped_gemm(const fp8_gemm_args_t* a, void* stream) {
   NV_RETURN_IF(!a, NVFP4_ERR_NULL);
-  NV_RETURN_IF(a->epilogue != NVFP4_EPI_F32 && a->epilogue != NVFP4_EPI_SILU_MUL_BF16,
+  NV_RETURN_IF(a->epilogue != NVFP4_EPI_F32 && a->epilogue != NVFP4_EPI_SILU_MUL_BF16 &&
+                   a->epilogue != NVFP4_EPI_BF16,
                NVFP4_ERR_DTYPE);
   NV_RETURN_IF(a->num_groups < 1 || a->total_rows < 0 || a->N <= 0 || a->K <= 0 ||
                    a->K % KB || a->N % 128 || a->N > (1 << 24) || a->K > (1 << 24) ||
@@ -517,9 +528,12 @@ int fp8_grouped_gemm(const fp8_gemm_args_t* a, void* stream) {
   p.out = a->out;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool silu = a->epilogue == NVFP4_EPI_SILU_MUL_BF16, gather = a->gather_rows != nullptr;
-  if (p.G == 1 && p.total_rows <= kF8GvMaxRows && p.K % 512 == 0 && !silu)
+  const bool bf16 = a->epilogue == NVFP4_EPI_BF16;
+  if (p.G == 1 && p.total_rows <= kF8GvMaxRows && p.K % 512 == 0 && !silu && !bf16)
     return gather ? launch_f8_gemv<true>(p, s) : launch_f8_gemv<false>(p, s);
   if (silu) return gather ? launch_f8_cfg<true, true>(p, s) : launch_f8_cfg<true, false>(p, s);
+  if (bf16)
+    return gather ? launch_f8_cfg<false, true, true>(p, s) : launch_f8_cfg<false, false, true>(p, s);
   return gather ? launch_f8_cfg<false, true>(p, s) : launch_f8_cfg<false, false>(p, s);
 }
 

@@ -144,6 +144,7 @@ def test_gemm_validation(lib):
     assert call(out=None, total_rows=0) == OK       # empty problem: nothing enqueued
     assert call(r_codes=FAKE) == ENULL              # residual codes without scales
     assert call(epilogue=5) == EDTYPE
+    assert call(epilogue=2) == EDTYPE               # plain bf16: the FP8 GEMM's only
     assert call(K=200) == ESHAPE                    # K % 128
     assert call(N=96) == ESHAPE                     # N % 128
     assert call(num_groups=0) == ESHAPE
@@ -207,6 +208,8 @@ def test_fp8_validation(lib):
     assert g(w_scales=None) == ENULL
     assert g(out=None, total_rows=0) == OK
     assert g(epilogue=5) == EDTYPE
+    assert g(epilogue=3) == EDTYPE
+    assert g(epilogue=2, out=None, total_rows=0) == OK   # plain bf16 output: accepted
     assert g(K=192) == ESHAPE                       # K % 128
     assert g(N=96) == ESHAPE                        # N % 128
     assert g(num_groups=0) == ESHAPE

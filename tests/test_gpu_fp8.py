@@ -100,7 +100,7 @@ def _fp8_bound(orc, ac, as_, wc, wsc, off, gat):
     return bound
 
 
-def _run(orc, seed, G, N, K, mean_rows, src_rows, gather, silu):
+def _run(orc, seed, G, N, K, mean_rows, src_rows, gather, silu, bf16out=False):
     rng = np.random.default_rng(seed)
     x = D.bf16_to_f32(D.bf16_bits(_edge_rows(rng, src_rows, K, "f32")))
     ac, as_ = orc.fp8_quantize_rows(x)
@@ -115,7 +115,8 @@ def _run(orc, seed, G, N, K, mean_rows, src_rows, gather, silu):
     gd = None if gat is None else torch.from_numpy(gat).to(DEV)
     out = L.fp8_grouped_gemm(a, w, torch.from_numpy(off).to(DEV), N=N, K=K, total_rows=total,
                              gather_rows=gd,
-                             epilogue=L.NVFP4_EPI_SILU_MUL_BF16 if silu else L.NVFP4_EPI_F32)
+                             epilogue=(L.NVFP4_EPI_SILU_MUL_BF16 if silu else
+                                       L.NVFP4_EPI_BF16 if bf16out else L.NVFP4_EPI_F32))
     if silu:
         I = N // 2
         h_ref, _ = orc.silu_mul(y, I)
@@ -128,6 +129,13 @@ def _run(orc, seed, G, N, K, mean_rows, src_rows, gather, silu):
                + np.abs(silu_g) * bound[:, I:])
         bad = np.abs(h - hr) > tol * 1.0001
         assert not bad.any(), f"{bad.sum()} SiLU outputs beyond the bound"
+    elif bf16out:
+        # the FP32 value within the bound, then one rounding to bf16 (nearest
+        # even, 7 fraction bits: at most half an ulp, 2^-8 of the value)
+        yb = D.bf16_to_f32(host(out.view(torch.int16)).view(np.uint16)).astype(np.float64)
+        tol = bound + 2.0 ** -8 * (np.abs(y) + bound) * 1.0001
+        bad = np.abs(yb - y) > tol
+        assert not bad.any(), f"{bad.sum()} bf16 outputs beyond the bound"
     else:
         yg = host(out).astype(np.float64)
         bad = np.abs(yg - y) > bound
@@ -149,6 +157,16 @@ def _run(orc, seed, G, N, K, mean_rows, src_rows, gather, silu):
 def test_fp8_gemm_parity(orc, seed, G, N, K, mean_rows, src_rows, gather, silu):
     say(f"fp8 gemm seed={seed} G={G} N={N} K={K} rows~{mean_rows} gather={gather} silu={silu}")
     _run(orc, seed, G, N, K, mean_rows, src_rows, gather, silu)
+
+
+@pytest.mark.parametrize("seed,G,N,K,mean_rows,src_rows,gather", [
+    (20, 1, 512, 256, -2300, 2300, False),      # dense, 256 x 256 tiles in bands, ragged tail
+    (21, 5, 384, 384, 70, 90, True),            # grouped, gather, 128 x 128 tiles
+    (22, 1, 256, 1024, -40, 40, False),         # one short group (not the decode kernel)
+])
+def test_fp8_gemm_bf16_out(orc, seed, G, N, K, mean_rows, src_rows, gather):
+    say(f"fp8 gemm bf16 out seed={seed} G={G} N={N} K={K} rows~{mean_rows} gather={gather}")
+    _run(orc, seed, G, N, K, mean_rows, src_rows, gather, False, bf16out=True)
 
 
 @pytest.mark.parametrize("rows,N,K,gather", [(16, 4096, 4096, False), (1, 256, 512, False),
