@@ -694,17 +694,18 @@ __global__ __launch_bounds__(64 * kGvWaves) void k_gemv(GemmParams p) {
 // and one group.  A wave dequantizes its A and R fragments once for four
 // slabs, which keeps the VALU work per streamed W byte low.  K goes in
 // 256-k chunks (codes, then the chunk's block scales, of 160 LDS rows) through
-// a three-deep ring of 23 KiB buffers: two chunks stay in flight while the
-// third is computed, and two workgroups fit on a CU, so one streams while
-// the other starts or finishes.  Wave w takes k-slice w % 2 (128 k) of every
-// chunk for slabs 4 (w / 2) .. 4 (w / 2) + 3; the two slices of a slab are
-// added in slice order.
+// two 23 KiB buffers: one chunk is in flight while the other is computed,
+// and three workgroups fit on a CU.  (A three-deep ring with two workgroups
+// per CU keeps more bytes in flight but streams 3-10% slower: more
+// independent workgroups hide each one's start and finish better.)  Wave w
+// takes k-slice w % 2 (128 k) of every chunk for slabs 4 (w / 2) .. 4 (w / 2)
+// + 3; the two slices of a slab are added in slice order.
 constexpr int kGwWaves = 4;
 constexpr int kGwSlices = 2;               // 128-k slices per chunk
 constexpr int kGwKC = 128 * kGwSlices;     // k per chunk
 constexpr int kGwSlabs = 8;                // 16-column W slabs per workgroup
 constexpr int kGwWaveSlabs = kGwSlabs * kGwSlices / kGwWaves;  // slabs per wave
-constexpr int kGwBufs = 3;
+constexpr int kGwBufs = 2;
 
 template <bool RAC, bool SILU, bool GATHER>
 __global__ __launch_bounds__(64 * kGwWaves) void k_gemv_wide(GemmParams p) {
