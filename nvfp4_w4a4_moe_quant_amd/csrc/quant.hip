@@ -287,18 +287,26 @@ __global__ __launch_bounds__(kQThreads) void k_quant(
     }
   };
 
-  // bf16: two rows per iteration, both loads issued before either is used
-  // (fp32 blocks are twice as large, so one row there).
-  constexpr int kIn = kBf16 ? 2 : 1;
+  // kIn rows per iteration, all their loads issued before any is used.  The
+  // statistics pass takes four bf16 rows (128 bytes a lane); two otherwise:
+  // fp32 blocks are twice as large, the per-channel maxima leave no registers
+  // for more, and without statistics a thread has only two rows (the row
+  // splits are many).  The loads are unconditional -- a row past the end
+  // reads row r again, a cache hit -- so the compiler can wait for each row's
+  // own load only.
+  constexpr int kIn = kBf16 && kStats && !kMax ? 4 : 2;
   if (active) {
     for (int64_t r = r0 + sub; r < r1; r += kIn * (int64_t)rpi) {
+      int64_t src[kIn];
+#pragma unroll
+      for (int u = 0; u < kIn; ++u) src[u] = r + u * rpi < r1 ? r + u * rpi : r;
+      if (gather) {
+#pragma unroll
+        for (int u = 0; u < kIn; ++u) src[u] = gather[src[u]];
+      }
       RawBlock<kBf16> b[kIn];
 #pragma unroll
-      for (int u = 0; u < kIn; ++u)
-        if (r + u * rpi < r1) {
-          const int64_t rr = r + u * rpi;
-          b[u].load(x, (gather ? (int64_t)gather[rr] : rr) * ldx + cb * 16);
-        }
+      for (int u = 0; u < kIn; ++u) b[u].load(x, src[u] * ldx + cb * 16);
 #pragma unroll
       for (int u = 0; u < kIn; ++u)
         if (r + u * rpi < r1) block(b[u], r + u * rpi);
