@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant(
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ tscale_out,
     int64_t* __restrict__ score, uint32_t* __restrict__ chmax, int tpr, int rpi,
     int64_t rows_per_split, void* __restrict__ dq_out, const int32_t* __restrict__ goff,
-    const int32_t* __restrict__ gather) {
+    const int32_t* __restrict__ gather, int store_sums) {
   extern __shared__ unsigned char dyn_lds[];
   __shared__ float red[kQThreads / 64];
   // With goff (per-expert RAC) workgroup z quantizes group z's rows, grouped
@@ -334,13 +334,20 @@ __global__ __launch_bounds__(kQThreads) void k_quant(
       }
     }
     __syncthreads();
-    // slot j holds channel (tile start) + 16 * (j % tpr) + j / tpr
+    // slot j holds channel (tile start) + 16 * (j % tpr) + j / tpr.  With
+    // one row split (store_sums) this workgroup holds the channels' whole
+    // sums and stores them; otherwise it adds them to the zeroed totals.
     for (int j = threadIdx.x; j < tpr * 16; j += kQThreads) {
       const int64_t k = ((int64_t)blockIdx.x * tpr + j % tpr) * 16 + j / tpr;
       if (k < K) {
-        if (lsum[j]) atomicAdd(reinterpret_cast<unsigned long long*>(score) + k, lsum[j]);
-        if constexpr (kMax) {
-          if (lmax[j]) atomicMax(chmax + k, lmax[j]);
+        if (store_sums) {
+          score[k] = (int64_t)lsum[j];
+          if constexpr (kMax) chmax[k] = lmax[j];
+        } else {
+          if (lsum[j]) atomicAdd(reinterpret_cast<unsigned long long*>(score) + k, lsum[j]);
+          if constexpr (kMax) {
+            if (lmax[j]) atomicMax(chmax + k, lmax[j]);
+          }
         }
       }
     }
@@ -760,15 +767,6 @@ static int quantize_launch(const void* x, int dtype, int64_t rows, int64_t K, in
   float* partials = reinterpret_cast<float*>(ws);
   const int bf16 = dtype == NVFP4_IN_BF16;
   const int64_t CB = K / 16;
-  int nparts = 0;
-  if (!amax_in) {
-    nparts = (int)blocks_for(rows * CB, kThreads * 4, kMaxParts);
-    hipLaunchKernelGGL(k_amax, dim3(nparts), dim3(kThreads), 0, s, x, bf16, rows, K, ldx,
-                       partials, stats ? channel_score : nullptr, chm);
-  } else if (stats) {
-    hipLaunchKernelGGL(k_zero_stats, dim3((unsigned)blocks_for(K, 256, 1024)), dim3(256), 0, s,
-                       K, channel_score, chm);
-  }
   // Column tiles of at most tile_max column blocks (16: 256 channels, 512 B
   // of bf16 per row), rpi rows in flight per pass.  Narrow tiles keep the
   // global atomics per workgroup few.
@@ -778,12 +776,25 @@ static int quantize_launch(const void* x, int dtype, int64_t rows, int64_t K, in
   const int rpi = kQThreads / tpr;
   // Row splits: with statistics every workgroup adds one atomic per channel
   // to the global sums, so the splits stay few (about one workgroup per CU
-  // over all column tiles) and each thread takes at least two rows.
+  // over all column tiles) and each thread takes at least two rows.  With a
+  // single split (few rows) the workgroups store the sums instead, and
+  // nothing needs zeroing first.
   constexpr int wg_target = 256, min_rows = 2;
   int64_t splits = blocks_for(rows, (int64_t)rpi * min_rows, 65535);
   const int64_t max_splits = stats ? (wg_target / ntile > 0 ? wg_target / ntile : 1) : 65535;
   if (splits > max_splits) splits = max_splits;
   const int64_t rows_per_split = rows > 0 ? (rows + splits - 1) / splits : 1;
+  const int store = stats && splits == 1 ? 1 : 0;
+  int nparts = 0;
+  if (!amax_in) {
+    nparts = (int)blocks_for(rows * CB, kThreads * 4, kMaxParts);
+    hipLaunchKernelGGL(k_amax, dim3(nparts), dim3(kThreads), 0, s, x, bf16, rows, K, ldx,
+                       partials, stats && !store ? channel_score : nullptr,
+                       store ? nullptr : chm);
+  } else if (stats && !store) {
+    hipLaunchKernelGGL(k_zero_stats, dim3((unsigned)blocks_for(K, 256, 1024)), dim3(256), 0, s,
+                       K, channel_score, chm);
+  }
   const size_t lds =
       stats ? (size_t)tpr * 16 * (sizeof(uint64_t) + (cmax ? sizeof(uint32_t) : 0)) : 0;
   const dim3 grid((unsigned)ntile, (unsigned)splits);
@@ -792,11 +803,11 @@ static int quantize_launch(const void* x, int dtype, int64_t rows, int64_t K, in
 #define NV_QUANT_LAUNCH(ST, BF, MX)                                                              \
   hipLaunchKernelGGL((k_quant<ST, BF, 0, MX>), grid, dim3(kQThreads), ST ? lds : 0, s, x, rows, K, \
                      ldx, partials, nparts, amax_in, codes, scales, tensor_scale, sc, cm, tpr,    \
-                     rpi, rows_per_split, nullptr, nullptr, nullptr)
+                     rpi, rows_per_split, nullptr, nullptr, nullptr, store)
 #define NV_QUANT_LAUNCH_DQ(DQ, BF)                                                              \
   hipLaunchKernelGGL((k_quant<false, BF, DQ>), grid, dim3(kQThreads), 0, s, x, rows, K, ldx,    \
                      partials, nparts, amax_in, nullptr, nullptr, tensor_scale, nullptr, nullptr, \
-                     tpr, rpi, rows_per_split, dq_out, nullptr, nullptr)
+                     tpr, rpi, rows_per_split, dq_out, nullptr, nullptr, 0)
   if (dq == 1 && bf16) NV_QUANT_LAUNCH_DQ(1, true);
   else if (dq == 1) NV_QUANT_LAUNCH_DQ(1, false);
   else if (dq == 2 && bf16) NV_QUANT_LAUNCH_DQ(2, true);
@@ -1053,7 +1064,7 @@ int nvfp4_quantize_grouped(const void* x, int dtype, int64_t K, int64_t ldx,
   hipLaunchKernelGGL((k_quant<ST, BF, 0, MX>), grid, dim3(kQThreads), ST ? lds : 0, s, x,        \
                      total_rows, K, ldx, partials, kGroupParts, nullptr, codes, scales,          \
                      tensor_scales, sc, cm, tpr, rpi, (int64_t)0, nullptr, group_offsets,        \
-                     gather_rows)
+                     gather_rows, 0)
   if (cmax && bf16) NV_QUANT_LAUNCH_G(true, true, true);
   else if (cmax) NV_QUANT_LAUNCH_G(true, false, true);
   else if (stats && bf16) NV_QUANT_LAUNCH_G(true, true, false);

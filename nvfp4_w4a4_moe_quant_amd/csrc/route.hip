@@ -16,6 +16,9 @@
 //              is small, each block sums the counts itself (the earlier
 //              blocks' for its base, all blocks' for the offsets) and k_scan
 //              is not launched.
+//   k_route1   at most 64 tokens (a decode step): all of the above in one
+//              workgroup, the ids, counts and ranks kept in LDS -- one launch
+//              instead of three.
 #include "common.h"
 
 namespace {
@@ -29,15 +32,15 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-// PER logits per lane (E <= 64 * PER), so the per-lane scan is unrolled to
-// exactly the lanes' share and has no branches.
+// Top-k of token t by one wave: k rounds of a wave arg-max.  PER logits per
+// lane (E <= 64 * PER), so the per-lane scan is unrolled to exactly the
+// lanes' share and has no branches.  Lane 0 writes the ids (and, with sid, a
+// copy to LDS); wts, when given, gets the softmax weights of the k chosen.
 template <int PER>
-__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int64_t T, int E,
-                                              int k, int32_t* __restrict__ ids,
-                                              float* __restrict__ wts) {
+__device__ __forceinline__ void topk_token(const float* __restrict__ logits, int64_t t, int E,
+                                           int k, int32_t* __restrict__ ids,
+                                           float* __restrict__ wts, int32_t* sid) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
   float l[PER];
   bool live[PER];  // a real logit not taken yet
 #pragma unroll
@@ -69,7 +72,10 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
     for (int j = 0; j < PER; ++j)
       if (bi == lane + 64 * j) live[j] = false;
     chosen[s] = bv;  // wave-uniform after the reduction
-    if (lane == 0) ids[t * k + s] = bi;
+    if (lane == 0) {
+      ids[t * k + s] = bi;
+      if (sid) sid[t * k + s] = bi;
+    }
   }
   if (wts) {
     const float mx = chosen[0];
@@ -84,6 +90,16 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
     for (int s = 0; s < k; ++s)
       if (lane == s) wts[t * k + s] = __expf(chosen[s] - mx) / den;
   }
+}
+
+// One wave per token.
+template <int PER>
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int64_t T, int E,
+                                              int k, int32_t* __restrict__ ids,
+                                              float* __restrict__ wts) {
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  topk_token<PER>(logits, t, E, k, ids, wts, nullptr);
 }
 
 __global__ __launch_bounds__(kTok) void k_counts(const int32_t* __restrict__ ids, int64_t T, int E,
@@ -222,6 +238,74 @@ __global__ __launch_bounds__(kTok) void k_scatter(const int32_t* __restrict__ id
   }
 }
 
+// ------------------------------------------------- one-workgroup routing
+// T <= kR1MaxT: wave w takes tokens w, w + 16, ... (at most four: beyond
+// that the separate top-k launch, a wave per token over many CUs, is
+// faster); then, from LDS, the expert counts, their exclusive scan (the
+// offsets; thread e holds expert e) and the rank of each token inside its
+// expert by bit masks, as k_counts, k_scan and k_scatter do for one block.
+constexpr int kR1Threads = 1024;
+constexpr int kR1MaxT = 4 * (kR1Threads / 64);
+constexpr int kR1Words = kR1MaxT / 32;  // token bit-mask words per expert
+
+template <int PER>
+__global__ __launch_bounds__(kR1Threads) void k_route1(const float* __restrict__ logits, int T,
+                                                       int E, int k, int32_t* __restrict__ ids,
+                                                       float* __restrict__ wts,
+                                                       int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ gather,
+                                                       int32_t* __restrict__ row_of) {
+  __shared__ int32_t sid[kR1MaxT * kMaxK];
+  __shared__ int32_t sbase[kMaxE];  // counts, then each expert's first row
+  __shared__ uint32_t bits[kMaxE * kR1Words];
+  __shared__ int32_t wtot[kR1Threads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < E; i += kR1Threads) sbase[i] = 0;
+  for (int i = tid; i < E * kR1Words; i += kR1Threads) bits[i] = 0u;
+  for (int t = w; t < T; t += kR1Threads / 64) topk_token<PER>(logits, t, E, k, ids, wts, sid);
+  __syncthreads();
+  if (tid < T)
+    for (int s = 0; s < k; ++s) {
+      const int e = sid[tid * k + s];
+      atomicAdd(&sbase[e], 1);
+      atomicOr(&bits[e * kR1Words + (tid >> 5)], 1u << (tid & 31));
+    }
+  __syncthreads();
+  // exclusive scan of the counts over the experts
+  const int32_t c = tid < E ? sbase[tid] : 0;
+  int32_t inc = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t n = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += n;
+  }
+  if (lane == 63) wtot[w] = inc;
+  __syncthreads();
+  int32_t before = 0, total = 0;
+  for (int i = 0; i < kR1Threads / 64; ++i) {
+    before += i < w ? wtot[i] : 0;
+    total += wtot[i];
+  }
+  const int32_t off = before + inc - c;
+  if (tid < E) {
+    offsets[tid] = off;
+    sbase[tid] = off;
+  }
+  if (tid == 0) offsets[E] = total;
+  __syncthreads();
+  if (tid < T) {
+    for (int s = 0; s < k; ++s) {
+      const int e = sid[tid * k + s];
+      const uint32_t* m = bits + e * kR1Words;
+      int rank = __builtin_popcount(m[tid >> 5] & ((1u << (tid & 31)) - 1u));
+      for (int i = 0; i < (tid >> 5); ++i) rank += __builtin_popcount(m[i]);
+      const int32_t pos = sbase[e] + rank;
+      gather[pos] = tid;
+      row_of[tid * k + s] = pos;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- combine
 // out[t, :] = sum over the token's k slots, in slot order, of
 // w[t, s] * y[row_of[t, s], :]: one FP32 product and one FP32 addition per
@@ -309,6 +393,18 @@ int moe_route(const float* logits, int64_t T, int64_t E, int64_t k, int32_t* top
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int32_t* cnt = reinterpret_cast<int32_t*>(ws);
   const int64_t nblk = (T + kTok - 1) / kTok;
+  if (T > 0 && T <= kR1MaxT) {
+#define NV_ROUTE1(PER)                                                                       \
+  hipLaunchKernelGGL(k_route1<PER>, dim3(1), dim3(kR1Threads), 0, s, logits, (int)T, (int)E, \
+                     (int)k, topk_ids, topk_weights, expert_offsets, gather_rows, row_of)
+    if (E <= 64) NV_ROUTE1(1);
+    else if (E <= 128) NV_ROUTE1(2);
+    else if (E <= 256) NV_ROUTE1(4);
+    else if (E <= 512) NV_ROUTE1(8);
+    else NV_ROUTE1(16);
+#undef NV_ROUTE1
+    return nv_launch_status();
+  }
   if (T > 0) {
     const dim3 grid((unsigned)((T + 3) / 4));
 #define NV_TOPK(PER)                                                                        \

@@ -119,9 +119,15 @@ def test_quant_empty_rows(orc):
 
 
 # ------------------------------------------------------------- routing
-# the last two cases are past the fused scan's bound (blocks^2 x E > 2^20): the
-# separate one-workgroup scan of the expert counts runs there
-@pytest.mark.parametrize("T,E,k,routing", [(1, 4, 1, "normal"), (300, 8, 2, "zipf"),
+# Up to 64 tokens one workgroup does all of the routing (the first five
+# cases: a decode step, the largest E and k, every expert taken); 65 tokens is
+# the first case of the three-launch path.  The last two cases are past the
+# fused scan's bound (blocks^2 x E > 2^20): the separate one-workgroup scan of
+# the expert counts runs there.
+@pytest.mark.parametrize("T,E,k,routing", [(1, 4, 1, "normal"), (16, 256, 8, "normal"),
+                                           (33, 100, 5, "zipf"), (64, 1024, 16, "normal"),
+                                           (64, 16, 16, "normal"), (65, 512, 8, "zipf"),
+                                           (300, 8, 2, "zipf"),
                                            (1000, 128, 8, "normal"), (777, 256, 8, "normal"),
                                            (513, 64, 6, "zipf"), (200, 384, 8, "normal"),
                                            (20000, 256, 8, "zipf"), (9000, 1024, 4, "normal")])
