@@ -108,6 +108,42 @@ def test_quant_amax_in_and_stride(orc):
     check_quant_rac(orc, x, "bf16", 128, ldx_pad=32)
 
 
+# Statistics buffers that start with garbage: with one row split (at most 128
+# rows at this K) the workgroups store each channel's sums and nothing zeroes
+# them first; with more rows k_amax, or k_zero_stats when amax_in is given,
+# zeroes them before the atomic sums.  Called through the C ABI directly, so
+# that the outputs can be pre-filled.
+@pytest.mark.parametrize("rows,amax_in", [(16, False), (16, True), (128, True), (129, True),
+                                          (1000, False), (1000, True)])
+def test_quant_stats_overwrite_garbage(orc, rows, amax_in):
+    say(f"quant stats over garbage rows={rows} amax_in={amax_in}")
+    K = 2048
+    rng = np.random.default_rng(800 + rows)
+    x = D.bf16_to_f32(D.bf16_bits(rng.standard_normal((rows, K)).astype(np.float32)))
+    amax = float(np.abs(x).max()) if amax_in else None
+    d = orc.quantize_rac(x, K // 2, amax=amax)
+    xd = to_dev(x, "bf16")
+    am = None if amax is None else torch.tensor([amax], dtype=torch.float32, device=DEV)
+    codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((rows, K // 16), dtype=torch.uint8, device=DEV)
+    ts = torch.empty(1, dtype=torch.float32, device=DEV)
+    score = torch.full((K,), 0x5A5A5A5A5A5A5A5A, dtype=torch.int64, device=DEV)
+    chmax = torch.full((K,), 3.0e38, dtype=torch.float32, device=DEV)
+    lib = L.lib()
+    ws = torch.empty(max(int(lib.nvfp4_quantize_workspace_size(rows, K)), 256), dtype=torch.uint8,
+                     device=DEV)
+    for cm in (chmax, None):  # with the channel maximum, then without
+        score.fill_(0x5A5A5A5A5A5A5A5A)
+        st = lib.nvfp4_quantize(L._ptr(xd), L.NVFP4_IN_BF16, rows, K, xd.stride(0), L._ptr(am),
+                                L._ptr(codes), L._ptr(scales), L._ptr(ts), L._ptr(score),
+                                L._ptr(cm), L._ptr(ws), ws.numel(), L._stream(xd.device))
+        assert st == 0, st
+        eq(host(codes), d["codes"], "codes")
+        eq(host(score), d["score"], "channel score")
+        if cm is not None:
+            eq(host(cm), d["chmax"], "channel max")
+
+
 def test_quant_empty_rows(orc):
     say("quant rows=0")
     xd = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
