@@ -139,13 +139,15 @@ __device__ float workgroup_amax(const float* __restrict__ partials, int nparts,
 // (one v_mad_u64_u32 per element), combined in LDS, then added to the global
 // int64 sums.  That costs one
 // global atomic pair per channel and workgroup, and atomics on one address
-// are serialized, so the host keeps the row splits few and the workgroups
-// large (16 waves).
-constexpr int kQThreads = 1024;
+// are serialized, so the host keeps the row splits few (about two
+// workgroups per CU).  Workgroups of 8 waves, two per CU, run out of step,
+// so one's loads overlap the other's arithmetic better than one 16-wave
+// workgroup per CU.
+constexpr int kQThreads = 512;
 
 // Raw 16-element block as loaded (bf16: 8 dwords, fp32: 16 dwords); it is
-// widened to FP32 only when used, which keeps two rows in flight within the
-// register budget of a 1024-thread workgroup.
+// widened to FP32 only when used, which keeps several rows in flight within
+// the 128 registers that four waves per SIMD leave.
 template <bool kBf16>
 struct RawBlock {
   uint32_t w[kBf16 ? 8 : 16];
@@ -775,14 +777,17 @@ static int quantize_launch(const void* x, int dtype, int64_t rows, int64_t K, in
   const int tpr = (int)((CB + ntile - 1) / ntile);
   const int rpi = kQThreads / tpr;
   // Row splits: with statistics every workgroup adds one atomic per channel
-  // to the global sums, so the splits stay few (about one workgroup per CU
+  // to the global sums, so the splits stay few (about two workgroups per CU
   // over all column tiles) and each thread takes at least two rows.  With a
   // single split (few rows) the workgroups store the sums instead, and
   // nothing needs zeroing first.
-  constexpr int wg_target = 256, min_rows = 2;
+  constexpr int wg_target = 512, min_rows = 2;
   int64_t splits = blocks_for(rows, (int64_t)rpi * min_rows, 65535);
   const int64_t max_splits = stats ? (wg_target / ntile > 0 ? wg_target / ntile : 1) : 65535;
   if (splits > max_splits) splits = max_splits;
+  // with amax_in, one split also saves the launch that zeroes the sums: worth
+  // it while a thread has at most eight rows
+  if (amax_in && stats && rows <= (int64_t)rpi * 8) splits = 1;
   const int64_t rows_per_split = rows > 0 ? (rows + splits - 1) / splits : 1;
   const int store = stats && splits == 1 ? 1 : 0;
   int nparts = 0;
