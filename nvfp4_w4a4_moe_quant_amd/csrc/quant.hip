@@ -8,7 +8,8 @@
 // residual for a second FP4 pass.
 //
 // Passes over x (row-major [rows, K], 16-element blocks along K):
-//   k_amax      partial max|x| per workgroup (tensor amax), zeroes RAC stats
+//   k_amax      partial max|x| per workgroup (tensor amax); zeroes the RAC
+//               statistics when k_quant adds them atomically
 //   k_quant     tensor scale, block scales, E2M1 codes; optionally the exact
 //               per-channel error statistics (score = sum q^2, max |e|)
 //   k_rank      rank of every channel by (score desc, index asc); the

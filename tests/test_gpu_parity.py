@@ -187,14 +187,17 @@ def test_route_empty():
     assert rt.gather_rows.numel() == 0 and rt.row_of.numel() == 0
 
 
-def test_route_ties(orc):
-    say("route with tied logits")
-    lg = np.zeros((70, 16), np.float32)
+@pytest.mark.parametrize("T", [70, 40])  # three launches / one workgroup
+def test_route_ties(orc, T):
+    say(f"route with tied logits T={T}")
+    lg = np.zeros((T, 16), np.float32)
     lg[::3, 5] = 1.0
     rt = L.moe_route(torch.from_numpy(lg).to(DEV), 4)
     d = orc.route(lg, 4)
     eq(host(rt.topk_ids), d["topk_ids"], "topk ids")
+    eq(host(rt.expert_offsets), d["offsets"], "offsets")
     eq(host(rt.gather_rows), d["gather"], "gather")
+    eq(host(rt.row_of), d["row_of"], "row_of")
 
 
 # --------------------------------------------------------------- GEMM
