@@ -481,7 +481,7 @@ int launch_t(GemmParams& p, hipStream_t s) {
 // workgroup dequantizes its A and R rows again) and DMA latency, not MFMA.
 typedef float float4v __attribute__((ext_vector_type(4)));
 constexpr int kGvMaxRows = 64;      // one group: rows up to which this kernel is used
-constexpr int kGvAvgRows = 4;       // many groups: average rows per group
+constexpr int kGvAvgRows = 16;      // many groups: average rows per group
 constexpr int kGvWaves = 8;
 constexpr int kGvKC = 128 * kGvWaves;  // k per chunk
 constexpr int kGvCRow = kGvKC / 2;     // code bytes per row per chunk
@@ -917,10 +917,16 @@ __global__ __launch_bounds__(64 * kGwWaves) void k_gemv_wide(GemmParams p) {
   }
 }
 
+// Up to 16 rows per group on average a group's 16-row tiles are few, and one
+// workgroup per column block walks them.  Above 8, a second workgroup per
+// column block takes every other tile, so that groups of more than 16 rows
+// do not stream their weights twice in a row; it exits at once where a
+// group has one tile.
 template <bool RAC, bool SILU, bool GATHER>
 int launch_gemv_wide(GemmParams& p, hipStream_t s) {
   const int cols = 16 * kGwSlabs;  // output columns (SiLU: gate + up columns) per workgroup
-  const dim3 grid((unsigned)(p.N / cols), 1u, (unsigned)p.G);
+  const unsigned ytiles = p.total_rows > 8 * (int64_t)p.G ? 2u : 1u;
+  const dim3 grid((unsigned)(p.N / cols), ytiles, (unsigned)p.G);
   hipLaunchKernelGGL((k_gemv_wide<RAC, SILU, GATHER>), grid, dim3(64 * kGwWaves), 0, s, p);
   return nv_launch_status();
 }
