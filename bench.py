@@ -440,6 +440,27 @@ def moe_extras(w, dev, x, lg, wgu, wd, nsx, nsh, timed, step, ms_step, nev):
                                speedup=round(eager_us / graph_us, 3),
                                graph_with_input_copies_us=round(graph_cp_us, 1))
     out["decode_gemms"] = decode_moe_gemms(w, P, L, xd, lgd, args)
+    # a larger decode batch: 256 tokens, 8 routed rows per expert on average
+    Tb = 256
+    xb, lgb = x[:Tb].contiguous(), lg[:Tb].contiguous()
+    gb = P.GraphedMoEBlock(*args, T=Tb, E=w.E, x_dtype=x.dtype, device=dev, x=xb, logits=lgb)
+    modes_b = dict(eager=lambda: P.moe_block(xb, lgb, *args), graph=lambda: gb())
+    for fn in modes_b.values():
+        for _ in range(2):
+            fn()
+    torch.cuda.synchronize()
+    per_b = {k: [] for k in modes_b}
+    for _ in range(3):
+        for k, fn in modes_b.items():
+            t0 = time.perf_counter()
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            per_b[k].append((time.perf_counter() - t0) / 5 * 1e6)
+    out["decode_graph_256"] = dict(tokens=Tb,
+                                   eager_us_per_call=round(float(np.median(per_b["eager"])), 1),
+                                   graph_us_per_call=round(float(np.median(per_b["graph"])), 1))
+    del gb
     # trainer-side fake-quant of the gate/up weight bank (bf16 -> bf16)
     wb = (torch.randn((w.E * 2 * w.I, w.H), device=dev) * 0.02).to(torch.bfloat16)
     for _ in range(2):
