@@ -623,15 +623,6 @@ def library_fp8_reference(w, dev):
             for _ in range(3):
                 fn()
             torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(20):
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) / 20 * 1e3
-            out[name] = dict(shape=[M, N, K], us=round(us, 1),
-                             tflops=round(2.0 * M * N * K / us / 1e6, 1))
         except Exception as ex:  # the library may lack a kernel for the shape
             out[name] = dict(shape=[M, N, K], error=repr(ex)[:200])
             continue
@@ -644,13 +635,22 @@ def library_fp8_reference(w, dev):
         for _ in range(3):
             ours()
         torch.cuda.synchronize()
-        e0.record()
-        for _ in range(20):
-            ours()
-        e1.record()
-        torch.cuda.synchronize()
-        ous = e0.elapsed_time(e1) / 20 * 1e3
-        out[name].update(this_library_dense_bf16_us=round(ous, 1),
+        # the two alternate in blocks of 10 calls, so that a drift of the
+        # clock over the run falls on both; medians of the blocks
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        per = {"lib": [], "ours": []}
+        for _ in range(4):
+            for k, f in (("lib", fn), ("ours", ours)):
+                e0.record()
+                for _ in range(10):
+                    f()
+                e1.record()
+                torch.cuda.synchronize()
+                per[k].append(e0.elapsed_time(e1) / 10 * 1e3)
+        us, ous = float(np.median(per["lib"])), float(np.median(per["ours"]))
+        out[name] = dict(shape=[M, N, K], us=round(us, 1),
+                         tflops=round(2.0 * M * N * K / us / 1e6, 1),
+                         this_library_dense_bf16_us=round(ous, 1),
                          this_library_dense_over_library=round(ous / us, 3))
     return out
 
