@@ -481,7 +481,7 @@ int launch_t(GemmParams& p, hipStream_t s) {
 // workgroup dequantizes its A and R rows again) and DMA latency, not MFMA.
 typedef float float4v __attribute__((ext_vector_type(4)));
 constexpr int kGvMaxRows = 64;      // one group: rows up to which this kernel is used
-constexpr int kGvAvgRows = 16;      // many groups: average rows per group
+constexpr int kGvAvgRows = 32;      // many groups: average rows per group
 constexpr int kGvWaves = 8;
 constexpr int kGvKC = 128 * kGvWaves;  // k per chunk
 constexpr int kGvCRow = kGvKC / 2;     // code bytes per row per chunk
@@ -691,11 +691,13 @@ __global__ __launch_bounds__(64 * kGvWaves) void k_gemv(GemmParams p) {
 // Many groups with few rows each (the experts of a decode step): there is
 // parallelism to spare across groups, so a workgroup owns 128 columns (eight
 // 16-column slabs; with SiLU*mul four gate and the four matching up slabs)
-// and one group.  A wave dequantizes its A and R fragments once for four
+// and one group, and takes MT 16-row fragments of the group per pass over W
+// (MT = 1 or 2).  A wave dequantizes its A and R fragments once for four
 // slabs, which keeps the VALU work per streamed W byte low.  K goes in
-// 256-k chunks (codes, then the chunk's block scales, of 160 LDS rows) through
-// two 23 KiB buffers: one chunk is in flight while the other is computed,
-// and three workgroups fit on a CU.  (A three-deep ring with two workgroups
+// 256-k chunks (codes, then the chunk's block scales, of 128 + 32 MT LDS
+// rows) through two buffers (23 KiB with MT = 1, 27 KiB with MT = 2): one
+// chunk is in flight while the other is computed, and three workgroups (MT
+// = 1) or two (MT = 2, registers) fit on a CU.  (A three-deep ring with two workgroups
 // per CU keeps more bytes in flight but streams 3-10% slower: more
 // independent workgroups hide each one's start and finish better.)  Wave w
 // takes k-slice w % 2 (128 k) of every chunk for slabs 4 (w / 2) .. 4 (w / 2)
@@ -707,9 +709,10 @@ constexpr int kGwSlabs = 8;                // 16-column W slabs per workgroup
 constexpr int kGwWaveSlabs = kGwSlabs * kGwSlices / kGwWaves;  // slabs per wave
 constexpr int kGwBufs = 2;
 
-template <bool RAC, bool SILU, bool GATHER>
+template <bool RAC, bool SILU, bool GATHER, int MT>
 __global__ __launch_bounds__(64 * kGwWaves) void k_gemv_wide(GemmParams p) {
-  constexpr int ROWS = 32 + 16 * kGwSlabs;   // A 16 | R 16 (zero rows without RAC) | W
+  constexpr int TR = 16 * MT;                 // rows of a group per pass over W
+  constexpr int ROWS = 2 * TR + 16 * kGwSlabs;  // A TR | R TR (zero rows without RAC) | W
   constexpr int CROW = kGwKC / 2;            // code bytes per row per chunk (8 pieces)
   constexpr int SROW = kGwKC / 16;           // scale bytes per row per chunk
   constexpr int CODES = ROWS * CROW;
@@ -721,14 +724,14 @@ __global__ __launch_bounds__(64 * kGwWaves) void k_gemv_wide(GemmParams p) {
   constexpr int CHUNK = CODES + NSI * kGwWaves * 256;
   constexpr int PER = NCI + NSI;             // DMA instructions per wave per chunk
   static_assert(CODES % (1024 * kGwWaves) == 0 && (kGwBufs - 1) * PER <= 63, "DMA, vmcnt");
-  static_assert(kGwWaves * kGwWaveSlabs * 64 * 16 <= CHUNK, "reduction fits in a chunk buffer");
+  static_assert(kGwWaves * kGwWaveSlabs * MT * 64 * 16 <= kGwBufs * CHUNK, "reduction fits");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kGwBufs * CHUNK];
   float4v* red = reinterpret_cast<float4v*>(lds);  // [wave][wave slab][lane], after the last chunk
 
   const int grp = blockIdx.z;
   const int row_beg = p.offsets[grp], row_end = p.offsets[grp + 1];
   const int nrows = row_end - row_beg;
-  if ((int)blockIdx.y * 16 >= nrows) return;  // workgroup-uniform
+  if ((int)blockIdx.y * TR >= nrows) return;  // workgroup-uniform
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ks = wave % kGwSlices, sh = wave / kGwSlices;  // k-slice, slab group
@@ -751,22 +754,22 @@ __global__ __launch_bounds__(64 * kGwWaves) void k_gemv_wide(GemmParams p) {
   const int c = lane & 15, q = lane >> 4;
   float hmax = 0.0f;
 
-  for (int tile = blockIdx.y; tile * 16 < nrows; tile += gridDim.y) {
-    const int m0 = row_beg + tile * 16;
+  for (int tile = blockIdx.y; tile * TR < nrows; tile += gridDim.y) {
+    const int m0 = row_beg + tile * TR;
     auto act = [&](const uint8_t* base, int i, int per_row) -> const uint8_t* {
       const int m = m0 + i;
       if (m >= row_end) return nv_zero_row;
       return base + (GATHER ? (int64_t)p.gather[m] : (int64_t)m) * per_row;
     };
     auto code_row = [&](int r) -> const uint8_t* {
-      if (r < 16) return act(p.a_codes, r, K2);
-      if (r < 32) return RAC ? act(p.r_codes, r - 16, K2) : nv_zero_row;
-      return p.w_codes + w_row(r - 32) * K2;
+      if (r < TR) return act(p.a_codes, r, K2);
+      if (r < 2 * TR) return RAC ? act(p.r_codes, r - TR, K2) : nv_zero_row;
+      return p.w_codes + w_row(r - 2 * TR) * K2;
     };
     auto scale_row = [&](int r) -> const uint8_t* {
-      if (r < 16) return act(p.a_scales, r, K16);
-      if (r < 32) return RAC ? act(p.r_scales, r - 16, K16) : nv_zero_row;
-      return p.w_scales + w_row(r - 32) * K16;
+      if (r < TR) return act(p.a_scales, r, K16);
+      if (r < 2 * TR) return RAC ? act(p.r_scales, r - TR, K16) : nv_zero_row;
+      return p.w_scales + w_row(r - 2 * TR) * K16;
     };
     // per-lane sources: code pieces (8 per row per chunk, XOR-swizzled by
     // row) and scale words (4 per row per chunk); chunk ch adds ch * CROW
@@ -811,13 +814,15 @@ __global__ __launch_bounds__(64 * kGwWaves) void k_gemv_wide(GemmParams p) {
       const uint32_t v = *reinterpret_cast<const uint16_t*>(buf + CODES + r * SROW + (kl >> 4));
       return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, false);
     };
-    float4v acc[kGwWaveSlabs];  // main and residual passes (one tensor scale)
+    float4v acc[MT][kGwWaveSlabs];  // main and residual passes (one tensor scale)
 #pragma unroll
-    for (int t = 0; t < kGwWaveSlabs; ++t) acc[t] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int f = 0; f < MT; ++f)
+#pragma unroll
+      for (int t = 0; t < kGwWaveSlabs; ++t) acc[f][t] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
     for (int ch = 0; ch < nch; ++ch) {
-      // issue chunk ch + 2 into the buffer computed two iterations ago (the
-      // barrier at the end of the previous iteration ended its reads), then
-      // wait for chunk ch: the chunks issued after it may stay in flight
+      // issue chunk ch + 1 into the buffer computed in the previous iteration
+      // (the barrier at its end ended its reads), then wait for chunk ch:
+      // the chunk issued after it may stay in flight
       if (ch + kGwBufs - 1 < nch) issue(ch + kGwBufs - 1);
       const int pend = nch - 1 - ch < kGwBufs - 1 ? nch - 1 - ch : kGwBufs - 1;
       if (pend >= 2)
@@ -829,40 +834,53 @@ __global__ __launch_bounds__(64 * kGwWaves) void k_gemv_wide(GemmParams p) {
       __syncthreads();
       const uint8_t* buf = lds + (ch % kGwBufs) * CHUNK;
       const int kl = ks * 128 + q * 32;  // this lane's 32 k within the chunk
-      const uint4 av = code16(buf, c, kl);
-      const half2v sa = scale2(buf, c, kl);
-      uint4 rv = av;
-      half2v sr = sa;
-      if constexpr (RAC) {
-        rv = code16(buf, 16 + c, kl);
-        sr = scale2(buf, 16 + c, kl);
+      uint32_t aw[MT][4], rw[MT][4];
+      half2v sa[MT], sr[MT];
+#pragma unroll
+      for (int f = 0; f < MT; ++f) {
+        const uint4 av = code16(buf, 16 * f + c, kl);
+        sa[f] = scale2(buf, 16 * f + c, kl);
+        uint4 rv = av;
+        sr[f] = sa[f];
+        if constexpr (RAC) {
+          rv = code16(buf, TR + 16 * f + c, kl);
+          sr[f] = scale2(buf, TR + 16 * f + c, kl);
+        }
+        aw[f][0] = av.x; aw[f][1] = av.y; aw[f][2] = av.z; aw[f][3] = av.w;
+        rw[f][0] = rv.x; rw[f][1] = rv.y; rw[f][2] = rv.z; rw[f][3] = rv.w;
       }
-      const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, rw[4] = {rv.x, rv.y, rv.z, rv.w};
 #pragma unroll
       for (int hi = 0; hi < 2; ++hi) {  // the two 16-k blocks of the lane's 32 k
-        const half2v s_a = hi ? __builtin_shufflevector(sa, sa, 1, 1)
-                              : __builtin_shufflevector(sa, sa, 0, 0);
-        const half2v s_r = hi ? __builtin_shufflevector(sr, sr, 1, 1)
-                              : __builtin_shufflevector(sr, sr, 0, 0);
-        const half8 ba0 = dequant8(aw[2 * hi], s_a), ba1 = dequant8(aw[2 * hi + 1], s_a);
-        half8 br0, br1;
-        if constexpr (RAC) {
-          br0 = dequant8(rw[2 * hi], s_r);
-          br1 = dequant8(rw[2 * hi + 1], s_r);
+        half8 ba0[MT], ba1[MT], br0[MT], br1[MT];
+#pragma unroll
+        for (int f = 0; f < MT; ++f) {
+          const half2v s_a = hi ? __builtin_shufflevector(sa[f], sa[f], 1, 1)
+                                : __builtin_shufflevector(sa[f], sa[f], 0, 0);
+          ba0[f] = dequant8(aw[f][2 * hi], s_a);
+          ba1[f] = dequant8(aw[f][2 * hi + 1], s_a);
+          if constexpr (RAC) {
+            const half2v s_r = hi ? __builtin_shufflevector(sr[f], sr[f], 1, 1)
+                                  : __builtin_shufflevector(sr[f], sr[f], 0, 0);
+            br0[f] = dequant8(rw[f][2 * hi], s_r);
+            br1[f] = dequant8(rw[f][2 * hi + 1], s_r);
+          }
         }
 #pragma unroll
         for (int t = 0; t < kGwWaveSlabs; ++t) {
-          const int r = 32 + 16 * (sh * kGwWaveSlabs + t) + c;
+          const int r = 2 * TR + 16 * (sh * kGwWaveSlabs + t) + c;
           const uint4 wv = code16(buf, r, kl);
           const half2v sw = scale2(buf, r, kl);
           const half2v s_w = hi ? __builtin_shufflevector(sw, sw, 1, 1)
                                 : __builtin_shufflevector(sw, sw, 0, 0);
           const half8 bw0 = dequant8(hi ? wv.z : wv.x, s_w), bw1 = dequant8(hi ? wv.w : wv.y, s_w);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ba0, bw0, acc[t], 0, 0, 0);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ba1, bw1, acc[t], 0, 0, 0);
-          if constexpr (RAC) {
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(br0, bw0, acc[t], 0, 0, 0);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(br1, bw1, acc[t], 0, 0, 0);
+#pragma unroll
+          for (int f = 0; f < MT; ++f) {
+            acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ba0[f], bw0, acc[f][t], 0, 0, 0);
+            acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ba1[f], bw1, acc[f][t], 0, 0, 0);
+            if constexpr (RAC) {
+              acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(br0[f], bw0, acc[f][t], 0, 0, 0);
+              acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(br1[f], bw1, acc[f][t], 0, 0, 0);
+            }
           }
         }
       }
@@ -870,41 +888,49 @@ __global__ __launch_bounds__(64 * kGwWaves) void k_gemv_wide(GemmParams p) {
     }
 
 #pragma unroll
-    for (int t = 0; t < kGwWaveSlabs; ++t) red[(wave * kGwWaveSlabs + t) * 64 + lane] = acc[t];
+    for (int f = 0; f < MT; ++f)
+#pragma unroll
+      for (int t = 0; t < kGwWaveSlabs; ++t)
+        red[((f * kGwWaves + wave) * kGwWaveSlabs + t) * 64 + lane] = acc[f][t];
     __syncthreads();
-    // wave w finishes slabs w and w + 4 (with SiLU: gate slab w, up slab w + 4);
-    // slab sl's two k-slices sit with the waves of slab group sl / 4
+    // wave w finishes slabs w and w + 4 (with SiLU: gate slab w, up slab w + 4)
+    // of every 16-row fragment; slab sl's two k-slices sit with the waves of
+    // slab group sl / 4
     constexpr int PERW = kGwSlabs / kGwWaves;
-    float4v sm[PERW];
 #pragma unroll
-    for (int t = 0; t < PERW; ++t) {
-      const int sl = wave + t * kGwWaves;
-      const int g = sl / kGwWaveSlabs, u = sl % kGwWaveSlabs;
-      sm[t] = red[((g * kGwSlices + 0) * kGwWaveSlabs + u) * 64 + lane];
+    for (int f = 0; f < MT; ++f) {
+      const float4v* rf = red + f * kGwWaves * kGwWaveSlabs * 64;
+      float4v sm[PERW];
 #pragma unroll
-      for (int i = 1; i < kGwSlices; ++i)
-        sm[t] += red[((g * kGwSlices + i) * kGwWaveSlabs + u) * 64 + lane];
-    }
+      for (int t = 0; t < PERW; ++t) {
+        const int sl = wave + t * kGwWaves;
+        const int g = sl / kGwWaveSlabs, u = sl % kGwWaveSlabs;
+        sm[t] = rf[((g * kGwSlices + 0) * kGwWaveSlabs + u) * 64 + lane];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = m0 + 4 * q + i;  // D row of element i
-      if (row >= row_end) continue;
-      if constexpr (!SILU) {
-        float* out = reinterpret_cast<float*>(p.out);
+        for (int i = 1; i < kGwSlices; ++i)
+          sm[t] += rf[((g * kGwSlices + i) * kGwWaveSlabs + u) * 64 + lane];
+      }
 #pragma unroll
-        for (int t = 0; t < PERW; ++t)
-          out[(int64_t)row * p.N + j0 + (wave + t * kGwWaves) * 16 + c] = scale * sm[t][i];
-      } else {
-        static_assert(!SILU || (PERW == 2 && HS == kGwWaves), "gate slab w, up slab w + HS");
-        const int j = j0 + wave * 16 + c;
-        const float g = scale * sm[0][i], u = scale * sm[1][i];
-        if (p.out_y) {
-          p.out_y[(int64_t)row * p.N + j] = g;
-          p.out_y[(int64_t)row * p.N + I + j] = u;
+      for (int i = 0; i < 4; ++i) {
+        const int row = m0 + 16 * f + 4 * q + i;  // D row of element i
+        if (row >= row_end) continue;
+        if constexpr (!SILU) {
+          float* out = reinterpret_cast<float*>(p.out);
+#pragma unroll
+          for (int t = 0; t < PERW; ++t)
+            out[(int64_t)row * p.N + j0 + (wave + t * kGwWaves) * 16 + c] = scale * sm[t][i];
+        } else {
+          static_assert(!SILU || (PERW == 2 && HS == kGwWaves), "gate slab w, up slab w + HS");
+          const int j = j0 + wave * 16 + c;
+          const float g = scale * sm[0][i], u = scale * sm[1][i];
+          if (p.out_y) {
+            p.out_y[(int64_t)row * p.N + j] = g;
+            p.out_y[(int64_t)row * p.N + I + j] = u;
+          }
+          const uint32_t h = nv_f32_to_bf16(silu_mul(g, u));
+          reinterpret_cast<uint16_t*>(p.out)[(int64_t)row * I + j] = (uint16_t)h;
+          hmax = __builtin_fmaxf(hmax, __builtin_fabsf(nv_bf16_to_f32(h)));
         }
-        const uint32_t h = nv_f32_to_bf16(silu_mul(g, u));
-        reinterpret_cast<uint16_t*>(p.out)[(int64_t)row * I + j] = (uint16_t)h;
-        hmax = __builtin_fmaxf(hmax, __builtin_fabsf(nv_bf16_to_f32(h)));
       }
     }
   }
@@ -921,13 +947,22 @@ __global__ __launch_bounds__(64 * kGwWaves) void k_gemv_wide(GemmParams p) {
 // workgroup per column block walks them.  Above 8, a second workgroup per
 // column block takes every other tile, so that groups of more than 16 rows
 // do not stream their weights twice in a row; it exits at once where a
-// group has one tile.
+// group has one tile.  From 16 to 32 rows per group the workgroups take
+// 32-row tiles (two 16-row fragments per pass over W; two workgroups per CU
+// instead of three), and above 24 a second workgroup per column block again
+// takes every other tile.
 template <bool RAC, bool SILU, bool GATHER>
 int launch_gemv_wide(GemmParams& p, hipStream_t s) {
   const int cols = 16 * kGwSlabs;  // output columns (SiLU: gate + up columns) per workgroup
+  if (p.total_rows > 16 * (int64_t)p.G) {
+    const unsigned yt = p.total_rows > 24 * (int64_t)p.G ? 2u : 1u;
+    const dim3 grid((unsigned)(p.N / cols), yt, (unsigned)p.G);
+    hipLaunchKernelGGL((k_gemv_wide<RAC, SILU, GATHER, 2>), grid, dim3(64 * kGwWaves), 0, s, p);
+    return nv_launch_status();
+  }
   const unsigned ytiles = p.total_rows > 8 * (int64_t)p.G ? 2u : 1u;
   const dim3 grid((unsigned)(p.N / cols), ytiles, (unsigned)p.G);
-  hipLaunchKernelGGL((k_gemv_wide<RAC, SILU, GATHER>), grid, dim3(64 * kGwWaves), 0, s, p);
+  hipLaunchKernelGGL((k_gemv_wide<RAC, SILU, GATHER, 1>), grid, dim3(64 * kGwWaves), 0, s, p);
   return nv_launch_status();
 }
 
