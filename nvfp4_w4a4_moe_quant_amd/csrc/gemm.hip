@@ -695,9 +695,10 @@ __global__ __launch_bounds__(64 * kGvWaves) void k_gemv(GemmParams p) {
 // (MT = 1 or 2).  A wave dequantizes its A and R fragments once for four
 // slabs, which keeps the VALU work per streamed W byte low.  K goes in
 // 256-k chunks (codes, then the chunk's block scales, of 128 + 32 MT LDS
-// rows) through two buffers (23 KiB with MT = 1, 27 KiB with MT = 2): one
-// chunk is in flight while the other is computed, and three workgroups (MT
-// = 1) or two (MT = 2, registers) fit on a CU.  (A three-deep ring with two workgroups
+// rows) through NB buffers (23 KiB with MT = 1, 27 KiB with MT = 2): with
+// two, one chunk is in flight while the other is computed, and three
+// workgroups (MT = 1) or two (MT = 2, registers) fit on a CU; a handful of
+// rows over many groups takes three.  (A three-deep ring with two workgroups
 // per CU keeps more bytes in flight but streams 3-10% slower: more
 // independent workgroups hide each one's start and finish better.)  Wave w
 // takes k-slice w % 2 (128 k) of every chunk for slabs 4 (w / 2) .. 4 (w / 2)
@@ -709,7 +710,7 @@ constexpr int kGwSlabs = 8;                // 16-column W slabs per workgroup
 constexpr int kGwWaveSlabs = kGwSlabs * kGwSlices / kGwWaves;  // slabs per wave
 constexpr int kGwBufs = 2;
 
-template <bool RAC, bool SILU, bool GATHER, int MT>
+template <bool RAC, bool SILU, bool GATHER, int MT, int NB = kGwBufs>
 __global__ __launch_bounds__(64 * kGwWaves) void k_gemv_wide(GemmParams p) {
   constexpr int TR = 16 * MT;                 // rows of a group per pass over W
   constexpr int ROWS = 2 * TR + 16 * kGwSlabs;  // A TR | R TR (zero rows without RAC) | W
@@ -723,9 +724,9 @@ __global__ __launch_bounds__(64 * kGwWaves) void k_gemv_wide(GemmParams p) {
   constexpr int SCALE_WORDS = ROWS * SROW / 4;
   constexpr int CHUNK = CODES + NSI * kGwWaves * 256;
   constexpr int PER = NCI + NSI;             // DMA instructions per wave per chunk
-  static_assert(CODES % (1024 * kGwWaves) == 0 && (kGwBufs - 1) * PER <= 63, "DMA, vmcnt");
-  static_assert(kGwWaves * kGwWaveSlabs * MT * 64 * 16 <= kGwBufs * CHUNK, "reduction fits");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kGwBufs * CHUNK];
+  static_assert(CODES % (1024 * kGwWaves) == 0 && (NB - 1) * PER <= 63, "DMA, vmcnt");
+  static_assert(kGwWaves * kGwWaveSlabs * MT * 64 * 16 <= NB * CHUNK, "reduction fits");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NB * CHUNK];
   float4v* red = reinterpret_cast<float4v*>(lds);  // [wave][wave slab][lane], after the last chunk
 
   const int grp = blockIdx.z;
@@ -787,7 +788,7 @@ __global__ __launch_bounds__(64 * kGwWaves) void k_gemv_wide(GemmParams p) {
       gscale[j] = slot < SCALE_WORDS ? scale_row(slot >> 2) + (slot & 3) * 4 : nv_zero_row;
     }
     auto issue = [&](int ch) {
-      const uint32_t st = lbase + (ch % kGwBufs) * CHUNK;
+      const uint32_t st = lbase + (ch % NB) * CHUNK;
 #pragma unroll
       for (int j = 0; j < NCI; ++j) {
         const uint32_t m0r = __builtin_amdgcn_readfirstlane(st + (j * kGwWaves + wave) * 1024);
@@ -805,7 +806,7 @@ __global__ __launch_bounds__(64 * kGwWaves) void k_gemv_wide(GemmParams p) {
       }
     };
     __syncthreads();  // the previous tile's reduction has been read
-    for (int ch = 0; ch < kGwBufs - 1 && ch < nch; ++ch) issue(ch);
+    for (int ch = 0; ch < NB - 1 && ch < nch; ++ch) issue(ch);
 
     auto code16 = [&](const uint8_t* buf, int r, int kl) -> uint4 {
       return *reinterpret_cast<const uint4*>(buf + r * CROW + (((kl >> 5) ^ (r & 7)) << 4));
@@ -823,8 +824,8 @@ __global__ __launch_bounds__(64 * kGwWaves) void k_gemv_wide(GemmParams p) {
       // issue chunk ch + 1 into the buffer computed in the previous iteration
       // (the barrier at its end ended its reads), then wait for chunk ch:
       // the chunk issued after it may stay in flight
-      if (ch + kGwBufs - 1 < nch) issue(ch + kGwBufs - 1);
-      const int pend = nch - 1 - ch < kGwBufs - 1 ? nch - 1 - ch : kGwBufs - 1;
+      if (ch + NB - 1 < nch) issue(ch + NB - 1);
+      const int pend = nch - 1 - ch < NB - 1 ? nch - 1 - ch : NB - 1;
       if (pend >= 2)
         asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * PER) : "memory");
       else if (pend == 1)
@@ -832,7 +833,7 @@ __global__ __launch_bounds__(64 * kGwWaves) void k_gemv_wide(GemmParams p) {
       else
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      const uint8_t* buf = lds + (ch % kGwBufs) * CHUNK;
+      const uint8_t* buf = lds + (ch % NB) * CHUNK;
       const int kl = ks * 128 + q * 32;  // this lane's 32 k within the chunk
       uint32_t aw[MT][4], rw[MT][4];
       half2v sa[MT], sr[MT];
@@ -962,6 +963,13 @@ int launch_gemv_wide(GemmParams& p, hipStream_t s) {
   }
   const unsigned ytiles = p.total_rows > 8 * (int64_t)p.G ? 2u : 1u;
   const dim3 grid((unsigned)(p.N / cols), ytiles, (unsigned)p.G);
+  // a handful of rows over many groups (one or two tokens through a large
+  // MoE layer): few workgroups have work, one per CU, so each keeps two
+  // chunks in flight through a three-deep ring
+  if (p.total_rows * 16 <= (int64_t)p.G) {
+    hipLaunchKernelGGL((k_gemv_wide<RAC, SILU, GATHER, 1, 3>), grid, dim3(64 * kGwWaves), 0, s, p);
+    return nv_launch_status();
+  }
   hipLaunchKernelGGL((k_gemv_wide<RAC, SILU, GATHER, 1>), grid, dim3(64 * kGwWaves), 0, s, p);
   return nv_launch_status();
 }

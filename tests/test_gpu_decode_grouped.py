@@ -2,7 +2,8 @@
 a decode step, on average at most 32 rows per group, K % 512 == 0 (the wide
 kernel: 128 columns per workgroup; 16-row tiles up to 16 rows per group on
 average, 32-row tiles above, and above 8 and above 24 a second workgroup per
-column block takes every other tile) -- and on one group with the
+column block takes every other tile; a three-deep chunk ring for at most one
+row per sixteen groups) -- and on one group with the
 SiLU*mul epilogue (16-column slabs), against the oracle's exact grouped GEMM
 on oracle-quantized operands.  FP32 outputs within relative Frobenius 1e-5;
 with SiLU*mul, the FP32 gate/up side output within 1e-5, H within the
@@ -68,6 +69,10 @@ CASES = [  # (seed, group sizes, K, N, rac, silu, gather source rows, per-group 
     (17, [30, 70, 2, 0, 25, 40, 33, 31], 1024, 384, True, False, None, True),
     (18, [18, 23, 19, 21] * 4, 1536, 128, False, True, 40, False),
     (19, [29, 31, 27, 30, 26, 32, 28, 28] * 2, 512, 2048, True, False, None, False),
+    # at most one row per sixteen groups (a one-token decode step): a
+    # three-deep chunk ring
+    (20, [0] * 60 + [1, 0, 2, 1], 1024, 256, True, True, 3, False),
+    (21, [0, 1] + [0] * 30, 3072, 128, True, False, None, True),
 ]
 
 
